@@ -1,0 +1,240 @@
+"""Benchmark of the XPress Jacobi refinement step on one MI355X.
+
+A step is one xpress_jacobi_step over the synthetic 32-block, full-vocabulary workload (N=32
+blocks of B=16 slots, r=256, H=4096, M=512, V=151936): hidden cache, starting block from the base
+argmax, then K=15 Jacobi passes (latent + readout GEMM + fused add/argmax), inputs resident in HBM.
+
+Prints one JSON line. `value` is Jacobi passes per second of whole steps (per-step setup
+included). Also reported:
+  * `roofline`: the readout GEMM kernel (the dominant kernel), algorithmic bytes per launch
+    (w2 + base + lat) over its average duration measured with HIP events on the launch stream,
+    against the 8 TB/s HBM peak; its MFMA fraction of the 2.5 PFLOP/s bf16 peak is in `extra`;
+  * `cpu_baseline`: the CPU oracle timed on this host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "Jacobi passes/s at N=32,B=16,V=151936; HBM TB/s & MFMA % of peak"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, help="synthetic workload id (2..5)")
+    ap.add_argument("--kernel-reps", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def traffic_record(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on the
+    current kernel source (else None)."""
+    f = ROOT / "profiles" / "traffic.json"
+    if not f.exists():
+        return None
+    import hashlib
+
+    rec = json.loads(f.read_text()).get(f"{kernel}@{workload}")
+    if not rec:
+        return None
+    src = ROOT / "jacobi_block_refiner_amd" / "csrc" / rec["source"]
+    digest = hashlib.sha256(src.read_bytes()).hexdigest()[:16]
+    if digest != rec.get("source_sha256_16"):
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the pass library has no multi-GPU path here "
+              "(blocks shard with zero communication; see the design notes).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from jacobi_block_refiner_amd import synth, upload, xpress
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda"
+    wl = synth.WORKLOADS[args.workload]
+    K = wl.K
+    log(f"workload {wl.name}: drawing inputs")
+    inp = synth.make_inputs(wl)
+    log("uploading")
+    w = upload.weights(inp, dev)
+    h = upload.bf16_tensor(inp.h, dev)
+    base = upload.base_logits(inp.base, dev)
+    anchor = upload.tokens(inp.anchor, dev)
+    am1 = upload.tokens(inp.am1, dev)
+    blk = torch.zeros(wl.N, wl.B, dtype=torch.int64, device=dev)
+    ws = xpress.alloc_workspace(wl.N, wl.B, wl.r, wl.V, wl.C, K, dev)
+    torch.cuda.synchronize()
+
+    def step():
+        xpress.jacobi_step(w, h, base, anchor, am1, blk, K=K, C=wl.C,
+                           flags=xpress.INIT_FROM_BASE, ws=ws)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps of {K} passes")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
+    passes_per_s = K / (ms_per_step / 1e3)
+    draft = blk.cpu().numpy()
+
+    # Per-kernel timing with HIP events on the launch stream (the current torch stream), same
+    # inputs and launch configuration as inside the step.
+    rows = wl.rows
+    xh = torch.empty(wl.N, wl.B, wl.r, dtype=torch.float32, device=dev)
+    xpress.hidden_cache(w, h, xh, ws)
+    lat = torch.empty(wl.N, wl.B - 1, wl.r, dtype=torch.bfloat16, device=dev)
+    blk2 = blk.clone()
+    xpress.latent_pass(w, blk2, am1, xh, lat)
+    ntiles = xpress.readout_tiles(wl.V)
+    part = torch.empty(rows, ntiles, 2, dtype=torch.int32, device=dev)
+
+    def timed(fn, reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3  # us
+
+    reps = args.kernel_reps
+    fn_readout = lambda: xpress.readout_partials(w, lat, base, part)
+    fn_reduce = lambda: xpress.argmax_reduce(part, blk2)
+    fn_latent = lambda: xpress.latent_pass(w, blk2, am1, xh, lat)
+    for f in (fn_readout, fn_reduce, fn_latent):
+        f()
+    torch.cuda.synchronize()
+    readout_us = timed(fn_readout, reps)
+    reduce_us = timed(fn_reduce, reps)
+    latent_us = timed(fn_latent, reps)
+
+    # The K-pass loop alone (per-step setup excluded), through the per-pass entry points.
+    xpress.initial_block(base, anchor, blk2)
+
+    def loop():
+        for _ in range(K):
+            xpress.latent_pass(w, blk2, am1, xh, lat)
+            xpress.readout_argmax(w, lat, base, blk2, ws)
+
+    loop()
+    torch.cuda.synchronize()
+    loop_us = timed(loop, max(3, args.steps // 2))
+
+    alg_bytes = wl.V * wl.r * 2 + rows * wl.V * 2 + rows * wl.r * 2
+    flops = 2.0 * rows * wl.V * wl.r
+    achieved_gbs = alg_bytes / (readout_us * 1e-6) / 1e9
+    mfma_tflops = flops / (readout_us * 1e-6) / 1e12
+    traffic = traffic_record("readout_partial_kernel", wl.name)
+
+    out = {
+        "metric": METRIC,
+        "value": round(passes_per_s, 2),
+        "unit": "passes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded NumPy PCG64 draws; random-init head weights)",
+        "config": {"workload": wl.name, "N": wl.N, "B": wl.B, "r": wl.r, "H": wl.H, "M": wl.M,
+                   "V": wl.V, "topc": wl.C, "passes_per_step": K},
+        "roofline": {
+            "kernel": "readout_partial_kernel (bf16 MFMA readout + add + tile argmax)",
+            "bound": "hbm",
+            "achieved": round(achieved_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "avg_launch_us": round(readout_us, 2),
+        },
+        "extra": {
+            "rows_x_V_scored_per_s": round(rows * wl.V * passes_per_s, 1),
+            "loop_only_passes_per_s": round(K / (loop_us * 1e-6), 1),
+            "readout_mfma_tflops": round(mfma_tflops, 1),
+            "readout_mfma_frac_of_bf16_peak": round(mfma_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "argmax_reduce_us": round(reduce_us, 2),
+            "latent_us": round(latent_us, 2),
+            "pass_loop_us_per_pass": round(loop_us / K, 2),
+            "draft_checksum": int(np.sum(draft * (np.arange(draft.size).reshape(draft.shape) + 1)) % (1 << 61)),
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, K, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(inp, K, budget_s):
+    """The oracle (plain C, double, OpenMP over rows/blocks) on this host: hidden cache, starting
+    block, then whole passes over all rows until about budget_s seconds have been spent."""
+    import numpy as np
+
+    from jacobi_block_refiner_amd import synth
+    from oracle import oracle as O
+
+    wl = inp.wl
+    log(f"cpu baseline: oracle on {O.max_threads()} threads, budget {budget_s:.0f} s")
+    t0 = time.perf_counter()
+    L = synth.bf16_round(O.fold_mixer(inp.raw_L).astype(np.float32))
+    xh = O.hidden_cache(inp.h, inp.down_h, inp.down_g, inp.in_proj)
+    blk = O.initial_block(inp.base, inp.anchor, wl.N, wl.B)
+    passes = 0
+    while passes < K:
+        blk, _, _, _ = O.jacobi(inp, L, xh, blk, K=1, stop_at_fixed_point=False)
+        passes += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(passes / dt, 4), "unit": "passes/s", "cores": O.max_threads(),
+            "kind": "oracle",
+            "sample": f"{wl.name}: hidden cache + starting block + {passes} of {K} passes over all "
+                      f"{wl.rows} rows ({dt:.1f} s)"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

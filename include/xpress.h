@@ -1,0 +1,184 @@
+/*
+ * xpress.h -- C ABI of the MI355X (gfx950) XPress Jacobi block-refiner pass library.
+ *
+ * The XPress refiner drafts a block of B tokens per request: slot 0 holds the verified anchor and
+ * slots 1..B-1 hold draft tokens. One Jacobi pass re-derives every draft slot from the block as it
+ * stood at the start of the pass (definitions: vLLM API pages "vllm.model_executor.models.
+ * qwen3_xpress", class XPressRefinerHead, and "vllm.v1.worker.gpu.spec_decode.xpress.kernels",
+ * module docstring):
+ *   latent  x[b] = xh[b] + P_e . w1[prev[b]],  prev[0] = am1, prev[b] = blk[b-1]
+ *           u[b] = sum_{j<=b} L[:, b, j] * x[j]               (per-channel causal mixer)
+ *           lat[b] = u[b] + w_down . (silu(w_gate . u[b]) * (w_up . u[b]))     (b >= 1)
+ *   readout logit[b, v] = base[b, v] + lat[b] . w2[v]
+ *   argmax  blk[b] = argmax_v logit[b, v]   (ties: lowest vocabulary id)
+ * with xh the pass-invariant hidden cache (in_proj's hidden half applied to
+ * [down_h(h) ++ down_g(mean_b h)]). With top-C the readout only scores the C candidates taken
+ * once per step from the base logits.
+ *
+ * Conventions shared by every call:
+ *   - Every pointer is a DEVICE pointer owned by the caller, except the xpress_weights struct
+ *     itself (host memory, read during the call only) and out-parameters named *_bytes (host).
+ *   - bf16 tensors are passed as their 16-bit patterns (xpress_bf16). Token ids are int64.
+ *   - Layouts are dense row-major with the shapes given, except base logits, which take a row
+ *     stride (elements) base_ld >= V.
+ *   - Rows of the readout: row p = n*(B-1) + (b-1) is slot b (1..B-1) of block n.
+ *   - Every call only enqueues work on `stream` (NULL = the null stream) and returns; none
+ *     allocates, frees or synchronises, so a sequence of calls can be captured into a HIP graph.
+ *   - Argument errors are detected on the host before anything is enqueued; the call then returns
+ *     a non-zero status and xpress_last_error() describes it. XPRESS_ERR_HIP reports a launch
+ *     failure from the HIP runtime.
+ *   - N == 0 is a no-op that returns XPRESS_OK.
+ *   - Supported shapes on the GPU path: r in {64, 128, 256}; 2 <= B <= 16; M a multiple of 64
+ *     (64..1024); H a multiple of 64; V >= 1 and V*r < 2^31; all pointers 16-byte aligned and
+ *     base_ld a multiple of 8 elements. Inputs must be finite; results for NaN/Inf inputs are
+ *     unspecified.
+ */
+#ifndef XPRESS_H
+#define XPRESS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t xpress_bf16;             /* bfloat16 bit pattern */
+typedef struct ihipStream_t* xpress_stream; /* hipStream_t */
+
+typedef enum {
+  XPRESS_OK = 0,
+  XPRESS_ERR_ARG = 1,       /* null/misaligned pointer, unsupported shape, C > V, K < 0, ... */
+  XPRESS_ERR_WORKSPACE = 2, /* the workspace is smaller than the call needs for this N */
+  XPRESS_ERR_HIP = 3        /* the HIP runtime reported an error at launch */
+} xpress_status;
+
+/* Parameters of one refiner head (qwen3_xpress page, XPressRefinerHead constructor), in the
+ * nn.Linear layout [out_features, in_features]. Device pointers, bf16. */
+typedef struct {
+  int32_t B; /* slots per block, anchor included */
+  int32_t r; /* latent rank */
+  int32_t H; /* model hidden size */
+  int32_t M; /* SwiGLU hidden size (mlp_hidden) */
+  int64_t V; /* vocabulary size */
+  const xpress_bf16* w1;      /* [V, r]   token embedding                                      */
+  const xpress_bf16* down_h;  /* [r, H]   per-slot hidden projection                           */
+  const xpress_bf16* down_g;  /* [r, H]   projection of the block-mean hidden state            */
+  const xpress_bf16* in_proj; /* [r, 3r]  columns [0,r) act on down_h, [r,2r) on down_g,
+                                          [2r,3r) on the token embedding                       */
+  const xpress_bf16* mix_L;   /* [r, B, B] FOLDED mixer, L[c,b,j] = raw[c,b,j]*[j<=b] + [j==b]
+                                           (qwen3_xpress page, fold_from_raw_); only j <= b is
+                                           read                                                */
+  const xpress_bf16* w_gate;  /* [M, r]                                                        */
+  const xpress_bf16* w_up;    /* [M, r]                                                        */
+  const xpress_bf16* w_down;  /* [r, M]                                                        */
+  const xpress_bf16* w2;      /* [V, r]   readout                                              */
+} xpress_weights;
+
+/* Flags of xpress_jacobi_step. */
+#define XPRESS_INIT_FROM_BASE 1u      /* blk[:,0] = anchor, blk[:,1:] = argmax(base) first    */
+#define XPRESS_STOP_AT_FIXED_POINT 2u /* passes after the first pass that changes no slot
+                                          return at once on the device (K stays the launch
+                                          count, so the step remains graph-capturable)        */
+
+/* Bytes of device workspace the calls below need for up to n_max blocks, C candidates (0 = full
+ * vocabulary) and up to k_max passes per step. Allocate once; any call with N <= n_max, the same
+ * B, r, V, C and K <= k_max fits. Returns XPRESS_ERR_ARG for an unsupported shape. */
+xpress_status xpress_workspace_size(int32_t n_max, int32_t B, int32_t r, int64_t V, int32_t C,
+                                    int32_t k_max, size_t* bytes);
+
+/* Fold of a raw (training-form) mixer into its serving form (qwen3_xpress page,
+ * XPressRefinerHead.fold_from_raw_): mix_L[c,b,j] = raw[c,b,j] * [j <= b] + [j == b], computed in
+ * fp32 and rounded to bf16 (round to nearest even), as copying into a bf16 parameter does.
+ * raw, mix_L: [r, B, B] bf16 (mix_L written; must not alias raw). */
+xpress_status xpress_fold_mixer(const xpress_bf16* raw, int32_t r, int32_t B, xpress_bf16* mix_L,
+                                xpress_stream stream);
+
+/* Hidden cache (qwen3_xpress page, hidden_cache, and the hidden half of in_proj that
+ * jacobi_refine_greedy applies once per step):
+ *   xh[n,b,:] = in_proj[:, 0:r] . (down_h . h[n,b]) + in_proj[:, r:2r] . (down_g . mean_b h[n,b])
+ * h: [N, B, H] bf16. xh: [N, B, r] fp32 (written). ws: workspace of ws_bytes bytes. */
+xpress_status xpress_hidden_cache(const xpress_weights* w, const xpress_bf16* h, int32_t N,
+                                  float* xh, void* ws, size_t ws_bytes, xpress_stream stream);
+
+/* Starting block of a step (qwen3_xpress page, jacobi_refine_greedy): blk[n,0] = anchor[n] and
+ * blk[n,b] = argmax_v base[n*(B-1)+b-1, v] for b >= 1 (lowest id on ties).
+ * base: [N*(B-1), V] bf16, row stride base_ld. anchor: [N]. blk: [N, B] (written). */
+xpress_status xpress_initial_block(const xpress_bf16* base, int64_t base_ld,
+                                   const int64_t* anchor, int32_t N, int32_t B, int64_t V,
+                                   int64_t* blk, xpress_stream stream);
+
+/* Latent stage of one pass (kernels page, _xpress_latent_kernel; qwen3_xpress page,
+ * _refine_latent): reads blk, never writes it.
+ * blk: [N, B]; am1: [N] (token before each anchor); xh: [N, B, r] fp32 from xpress_hidden_cache;
+ * lat: [N, B-1, r] bf16 (written; row n*(B-1)+b-1 is slot b). */
+xpress_status xpress_latent_pass(const xpress_weights* w, const int64_t* blk, const int64_t* am1,
+                                 const float* xh, int32_t N, xpress_bf16* lat,
+                                 xpress_stream stream);
+
+/* Full-vocabulary readout and argmax (kernels page, fused_add_argmax_to_blk; qwen3_xpress page,
+ * refine_bias): blk[n, b] = argmax_v (base[p, v] + lat[p] . w2[v]) for p = n*(B-1)+b-1, written in
+ * place for slots 1..B-1. The [N*(B-1), V] logits are never stored.
+ * lat: [N*(B-1), r] bf16; base: [N*(B-1), V] bf16 stride base_ld; blk: [N, B] in/out.
+ * changed (nullable): set to 1 if any slot took a new value (never cleared by this call). */
+xpress_status xpress_readout_argmax(const xpress_weights* w, const xpress_bf16* lat,
+                                    const xpress_bf16* base, int64_t base_ld, int32_t N,
+                                    int64_t* blk, int32_t* changed, void* ws, size_t ws_bytes,
+                                    xpress_stream stream);
+
+/* The two stages of xpress_readout_argmax, for callers that reduce the per-tile winners
+ * themselves (for example across GPUs that each hold a slice of the vocabulary) and for timing
+ * the readout GEMM on its own (kernels page, _xpress_add_argmax_partial_kernel and
+ * _xpress_add_argmax_reduce_to_blk_kernel).
+ * xpress_readout_tiles: number of vocabulary tiles a readout row is split into (depends on V).
+ * xpress_readout_partials: part[p * ntiles + t] = {bits of the fp32 maximum of base + lat . w2
+ *   over tile t of row p, the lowest vocabulary id attaining it}. part: [N*(B-1), ntiles] pairs of
+ *   uint32 (caller-owned, 8 bytes each).
+ * xpress_argmax_reduce: blk[n, b] = the id of the largest pair of row p = n*(B-1)+b-1 (ties:
+ *   lowest id), written in place; `changed` as in xpress_readout_argmax. */
+xpress_status xpress_readout_tiles(int64_t V, int32_t* ntiles);
+xpress_status xpress_readout_partials(const xpress_weights* w, const xpress_bf16* lat,
+                                      const xpress_bf16* base, int64_t base_ld, int32_t N,
+                                      uint32_t* part, xpress_stream stream);
+xpress_status xpress_argmax_reduce(const uint32_t* part, int32_t ntiles, int32_t N, int32_t B,
+                                   int64_t* blk, int32_t* changed, xpress_stream stream);
+
+/* Top-C preparation, once per step (qwen3_xpress page, top-C branch of jacobi_refine_greedy):
+ * cand[p] = the c = min(C, V) ids with the largest base[p, :] under the order (value descending,
+ * id ascending), stored in ascending id order; base_c[p, k] = base[p, cand[p, k]];
+ * w2c[p, k, :] = w2[cand[p, k], :].
+ * cand: [N*(B-1), c] int64; base_c: [N*(B-1), c] bf16; w2c: [N*(B-1), c, r] bf16 (written). */
+xpress_status xpress_topc_prepare(const xpress_weights* w, const xpress_bf16* base,
+                                  int64_t base_ld, int32_t N, int32_t C, int64_t* cand,
+                                  xpress_bf16* base_c, xpress_bf16* w2c, void* ws,
+                                  size_t ws_bytes, xpress_stream stream);
+
+/* Top-C readout and argmax (kernels page, _xpress_topc_argmax_to_blk_kernel): for every row p,
+ * k* = argmax_k (base_c[p, k] + lat[p] . w2c[p, k]) and blk[n, b] = cand[p, k*]; ties go to the
+ * lowest vocabulary id. Shapes as in xpress_topc_prepare with c candidates per row. */
+xpress_status xpress_readout_argmax_topc(const xpress_bf16* lat, const xpress_bf16* w2c,
+                                         const xpress_bf16* base_c, const int64_t* cand,
+                                         int32_t N, int32_t B, int32_t r, int32_t c,
+                                         int64_t* blk, int32_t* changed, xpress_stream stream);
+
+/* One draft step (qwen3_xpress page, jacobi_refine_greedy): hidden cache, starting block (with
+ * XPRESS_INIT_FROM_BASE; otherwise blk[:, 1:] is taken as given and blk[:, 0] is set to anchor),
+ * top-C preparation when C > 0, then K passes of latent + readout + argmax. On return blk[:, 1:]
+ * is the draft.
+ * h: [N, B, H]; base: [N*(B-1), V] stride base_ld; anchor, am1: [N]; blk: [N, B] in/out.
+ * passes_run (nullable, device int32): number of passes that ran (with
+ * XPRESS_STOP_AT_FIXED_POINT, the pass that changed nothing is counted). */
+xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
+                                 const xpress_bf16* base, int64_t base_ld, const int64_t* anchor,
+                                 const int64_t* am1, int32_t N, int32_t K, int32_t C,
+                                 uint32_t flags, int64_t* blk, int32_t* passes_run, void* ws,
+                                 size_t ws_bytes, xpress_stream stream);
+
+/* Message of the last non-OK status returned on the calling thread ("" if none). */
+const char* xpress_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XPRESS_H */

@@ -1,0 +1,298 @@
+// Top-C path of an XPress step (gfx950).
+//
+// Once per step (vLLM API page "vllm.model_executor.models.qwen3_xpress", top-C branch of
+// jacobi_refine_greedy): each draft row's candidate set is the c = min(C, V) ids with the largest
+// base logits, under the total order (value descending, id ascending), kept in ascending id
+// order; base_c and the readout rows w2c = w2[cand] are gathered once and reused by every pass.
+// Per pass (vLLM API page "vllm.v1.worker.gpu.spec_decode.xpress.kernels",
+// _xpress_topc_argmax_to_blk_kernel): a gathered GEMV base_c + w2c . lat, its argmax (lowest
+// vocabulary id on ties) and the candidate -> vocabulary id -> blk write, in one kernel.
+//
+// Selection is a per-row radix select on the 16-bit order-preserving key of the bf16 value
+// (high byte histogram, then low byte histogram inside the boundary bin), followed by one ordered
+// compaction pass that keeps every id above the threshold key and the lowest-id ties at it.
+#include "launch.hpp"
+#include "xpress_common.hpp"
+
+#include <limits.h>
+
+namespace xpress {
+
+namespace {
+
+// Larger key <=> larger value; -0.0 and +0.0 share a key.
+__device__ __forceinline__ uint32_t order_key(uint32_t b) {
+  b &= 0xffffu;
+  if (b == 0x8000u) b = 0;
+  return (b & 0x8000u) ? (~b & 0xffffu) : (b | 0x8000u);
+}
+
+__device__ __forceinline__ int block_exclusive_scan(int x, int* s_tmp, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  if (lane == 63) s_tmp[wave] = inc;
+  __syncthreads();
+  int pre = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int t = s_tmp[w];
+    if (w < wave) pre += t;
+    total += t;
+  }
+  __syncthreads();
+  return pre + inc - x;
+}
+
+__device__ __forceinline__ void load8_keys(const uint16_t* row, int64_t id0, int64_t V,
+                                           uint32_t key[8], uint16_t bits[8]) {
+  if (id0 + 8 <= V) {
+    const uint4 u = *reinterpret_cast<const uint4*>(row + id0);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bits[2 * e] = (uint16_t)(w[e] & 0xffffu);
+      bits[2 * e + 1] = (uint16_t)(w[e] >> 16);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) key[e] = order_key(bits[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool in = id0 + e < V;
+      bits[e] = in ? row[id0 + e] : 0;
+      key[e] = in ? order_key(bits[e]) : 0xffffffffu;  // never counted, never selected
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void topc_select_kernel(const uint16_t* __restrict__ base,
+                                                          int64_t ld, int64_t V, int c,
+                                                          int64_t* __restrict__ cand,
+                                                          uint16_t* __restrict__ base_c) {
+  __shared__ uint32_t s_hist[256];
+  __shared__ int s_tmp[4];
+  __shared__ uint32_t s_par[4];
+  const int p = blockIdx.x, tid = threadIdx.x;
+  const uint16_t* row = base + (int64_t)p * ld;
+  const int64_t nchunk = (V + 7) / 8;
+
+  // pass 1: high byte histogram
+  s_hist[tid] = 0;
+  __syncthreads();
+  for (int64_t q = tid; q < nchunk; q += 256) {
+    uint32_t key[8];
+    uint16_t bits[8];
+    load8_keys(row, q * 8, V, key, bits);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (key[e] <= 0xffffu) atomicAdd(&s_hist[key[e] >> 8], 1u);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t acc = 0;
+    int hb = 0;
+    for (int b = 255; b >= 0; --b) {
+      if (acc + s_hist[b] >= (uint32_t)c) { hb = b; break; }
+      acc += s_hist[b];
+    }
+    s_par[0] = (uint32_t)hb;
+    s_par[1] = acc;  // ids with a larger high byte
+  }
+  __syncthreads();
+  const uint32_t h1 = s_par[0], above1 = s_par[1];
+  s_hist[tid] = 0;
+  __syncthreads();
+  // pass 2: low byte histogram inside the boundary bin
+  for (int64_t q = tid; q < nchunk; q += 256) {
+    uint32_t key[8];
+    uint16_t bits[8];
+    load8_keys(row, q * 8, V, key, bits);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (key[e] <= 0xffffu && (key[e] >> 8) == h1) atomicAdd(&s_hist[key[e] & 0xffu], 1u);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t rem = (uint32_t)c - above1;
+    uint32_t acc = 0;
+    int lb = 0;
+    for (int b = 255; b >= 0; --b) {
+      if (acc + s_hist[b] >= rem) { lb = b; break; }
+      acc += s_hist[b];
+    }
+    s_par[2] = (h1 << 8) | (uint32_t)lb;   // threshold key T
+    s_par[3] = (uint32_t)c - (above1 + acc);  // ids equal to T that are taken (lowest ids)
+  }
+  __syncthreads();
+  const uint32_t T = s_par[2];
+  const int need_eq = (int)s_par[3];
+
+  // pass 3: ordered compaction, 2048 ids per round, ascending id order
+  int eq_carry = 0, sel_carry = 0;
+  int64_t* out_id = cand + (int64_t)p * c;
+  uint16_t* out_b = base_c + (int64_t)p * c;
+  for (int64_t id_base = 0; id_base < V && sel_carry < c; id_base += 2048) {
+    const int64_t id0 = id_base + (int64_t)tid * 8;
+    uint32_t key[8];
+    uint16_t bits[8];
+    if (id0 < V) {
+      load8_keys(row, id0, V, key, bits);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { key[e] = 0xffffffffu; bits[e] = 0; }
+    }
+    int n_eq = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) n_eq += (key[e] == T);
+    int eq_total;
+    const int eq_before = eq_carry + block_exclusive_scan(n_eq, s_tmp, eq_total);
+    bool sel[8];
+    int n_sel = 0, eq_seen = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool gt = key[e] <= 0xffffu && key[e] > T;
+      const bool eq = key[e] == T;
+      sel[e] = gt || (eq && eq_before + eq_seen < need_eq);
+      eq_seen += eq;
+      n_sel += sel[e];
+    }
+    int sel_total;
+    const int pos0 = sel_carry + block_exclusive_scan(n_sel, s_tmp, sel_total);
+    int k = pos0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (sel[e]) {
+        out_id[k] = id0 + e;
+        out_b[k] = bits[e];
+        ++k;
+      }
+    eq_carry += eq_total;
+    sel_carry += sel_total;
+  }
+}
+
+__global__ __launch_bounds__(256) void topc_gather_kernel(const int64_t* __restrict__ cand,
+                                                          const uint16_t* __restrict__ w2,
+                                                          int64_t total, int rq,
+                                                          uint16_t* __restrict__ w2c) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int64_t pk = i / rq;
+  const int q = (int)(i % rq);
+  const int64_t id = cand[pk];
+  reinterpret_cast<uint4*>(w2c)[i] = reinterpret_cast<const uint4*>(w2)[id * rq + q];
+}
+
+// One workgroup per draft row. Lanes form groups of G = R/8 that each hold one candidate's w2c
+// row (16 bytes per lane); the group's partial dot products are summed with xor shuffles.
+template <int R>
+__global__ __launch_bounds__(256) void topc_readout_kernel(
+    const uint16_t* __restrict__ lat, const uint16_t* __restrict__ w2c,
+    const uint16_t* __restrict__ base_c, const int64_t* __restrict__ cand, int B, int c,
+    int64_t* __restrict__ blk, int32_t* changed, int32_t* flags, int pass) {
+  if (pass_skipped(flags, pass)) return;
+  constexpr int G = R / 8;
+  constexpr int CPW = 64 / G;
+  __shared__ float s_v[4];
+  __shared__ int s_i[4];
+  const int p = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane % G, sub = lane / G;
+  float lv[8];
+  {
+    const uint4 u = reinterpret_cast<const uint4*>(lat + (int64_t)p * R)[q];
+    lv[0] = bf16_lo(u.x); lv[1] = bf16_hi(u.x); lv[2] = bf16_lo(u.y); lv[3] = bf16_hi(u.y);
+    lv[4] = bf16_lo(u.z); lv[5] = bf16_hi(u.z); lv[6] = bf16_lo(u.w); lv[7] = bf16_hi(u.w);
+  }
+  const uint4* wrow = reinterpret_cast<const uint4*>(w2c + (int64_t)p * c * R);
+  const uint16_t* bc = base_c + (int64_t)p * c;
+  const int64_t* cd = cand + (int64_t)p * c;
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+  const int step = 4 * CPW;
+  for (int k0 = 0; k0 < c; k0 += step) {
+    const int k = k0 + wave * CPW + sub;
+    float d = 0.f;
+    if (k < c) {
+      const uint4 u = ld_nt16(wrow + (int64_t)k * G + q);
+      d = lv[0] * bf16_lo(u.x);
+      d = fmaf(lv[1], bf16_hi(u.x), d);
+      d = fmaf(lv[2], bf16_lo(u.y), d);
+      d = fmaf(lv[3], bf16_hi(u.y), d);
+      d = fmaf(lv[4], bf16_lo(u.z), d);
+      d = fmaf(lv[5], bf16_hi(u.z), d);
+      d = fmaf(lv[6], bf16_lo(u.w), d);
+      d = fmaf(lv[7], bf16_hi(u.w), d);
+    }
+#pragma unroll
+    for (int off = G / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+    if (q == 0 && k < c) argmax_merge(bv, bi, bf16_to_f32(bc[k]) + d, (int)cd[k]);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    argmax_merge(bv, bi, ov, oi);
+  }
+  if (lane == 0) {
+    s_v[wave] = bv;
+    s_i[wave] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 4; ++w) argmax_merge(bv, bi, s_v[w], s_i[w]);
+    const int n = p / (B - 1), b = 1 + p % (B - 1);
+    int64_t* slot = blk + (int64_t)n * B + b;
+    if (*slot != (int64_t)bi) {
+      *slot = bi;
+      if (changed) __hip_atomic_store(changed, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (flags) __hip_atomic_store(flags + pass, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_topc_select(const uint16_t* base, int64_t ld, int rows, int64_t V, int c,
+                              int64_t* cand, uint16_t* base_c, hipStream_t s) {
+  hipLaunchKernelGGL(topc_select_kernel, dim3(rows), dim3(256), 0, s, base, ld, V, c, cand, base_c);
+  return hipGetLastError();
+}
+
+hipError_t launch_topc_gather(const int64_t* cand, const uint16_t* w2, int rows, int c, int r,
+                              uint16_t* w2c, hipStream_t s) {
+  const int rq = r / 8;
+  const int64_t total = (int64_t)rows * c * rq;
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(topc_gather_kernel, dim3((unsigned)blocks), dim3(256), 0, s, cand, w2, total,
+                     rq, w2c);
+  return hipGetLastError();
+}
+
+hipError_t launch_topc_readout(const uint16_t* lat, const uint16_t* w2c, const uint16_t* base_c,
+                               const int64_t* cand, int rows, int B, int r, int c, int64_t* blk,
+                               int32_t* changed, int32_t* flags, int pass, hipStream_t s) {
+  switch (r) {
+    case 64:
+      hipLaunchKernelGGL(topc_readout_kernel<64>, dim3(rows), dim3(256), 0, s, lat, w2c, base_c,
+                         cand, B, c, blk, changed, flags, pass);
+      break;
+    case 128:
+      hipLaunchKernelGGL(topc_readout_kernel<128>, dim3(rows), dim3(256), 0, s, lat, w2c, base_c,
+                         cand, B, c, blk, changed, flags, pass);
+      break;
+    case 256:
+      hipLaunchKernelGGL(topc_readout_kernel<256>, dim3(rows), dim3(256), 0, s, lat, w2c, base_c,
+                         cand, B, c, blk, changed, flags, pass);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace xpress

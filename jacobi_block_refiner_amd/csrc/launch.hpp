@@ -1,0 +1,56 @@
+// Host-side launchers of the XPress pass kernels. Shapes are validated by the C-ABI layer
+// (xpress_api.hip) before any of these is called; each launcher only enqueues work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace xpress {
+
+// Readout tiling: a workgroup scores TV = 32 * readout_waves() vocabulary ids against a group of
+// 32-row tiles.
+int readout_waves();
+int readout_tiles(int64_t V);
+int readout_row_groups(int rows, int64_t V);
+
+// K1a: hdg[m, j] = sum_k h[m, k] * Wcat[j, k], Wcat = [down_h; down_g], m < NB, j < 2r (fp32 out).
+hipError_t launch_hidden_gemm(const uint16_t* h, const uint16_t* down_h, const uint16_t* down_g,
+                              int NB, int H, int r, float* hdg, hipStream_t s);
+// K1b: xh[n, b] = in_proj[:, :r] . hdg[n, b, :r] + in_proj[:, r:2r] . mean_b hdg[n, b, r:].
+hipError_t launch_hidden_project(const float* hdg, const uint16_t* in_proj, int N, int B, int r,
+                                 float* xh, hipStream_t s);
+// K2: blk[n, 0] = anchor[n]; blk[n, b] = argmax_v base[n*(B-1)+b-1, v].
+hipError_t launch_initial_block(const uint16_t* base, int64_t ld, const int64_t* anchor, int N,
+                                int B, int64_t V, int64_t* blk, hipStream_t s);
+// K4: fused latent stage of one pass.
+hipError_t launch_latent(const int64_t* blk, const int64_t* am1, const float* xh,
+                         const uint16_t* w1, const uint16_t* in_proj, const uint16_t* mix_L,
+                         const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                         int N, int B, int r, int M, int64_t V, uint16_t* lat,
+                         const int32_t* flags, int pass, hipStream_t s);
+// K5: per (vocab tile, row) partial argmax of base + lat . w2^T; part: [rows, ntiles].
+hipError_t launch_readout_partial(const uint16_t* lat, const uint16_t* w2, const uint16_t* base,
+                                  int64_t ld, int rows, int64_t V, int r, uint2* part,
+                                  const int32_t* flags, int pass, hipStream_t s);
+// K6: per-row reduce of the partials into blk[n, 1 + p % (B-1)].
+hipError_t launch_argmax_reduce(const uint2* part, int ntiles, int rows, int B, int64_t* blk,
+                                int32_t* changed, int32_t* pass_flags, int pass, hipStream_t s);
+// K3: top-C candidate selection (+ base_c) and the w2 gather.
+hipError_t launch_topc_select(const uint16_t* base, int64_t ld, int rows, int64_t V, int c,
+                              int64_t* cand, uint16_t* base_c, hipStream_t s);
+hipError_t launch_topc_gather(const int64_t* cand, const uint16_t* w2, int rows, int c, int r,
+                              uint16_t* w2c, hipStream_t s);
+// K7: top-C gathered GEMV + argmax + candidate -> vocabulary id -> blk.
+hipError_t launch_topc_readout(const uint16_t* lat, const uint16_t* w2c, const uint16_t* base_c,
+                               const int64_t* cand, int rows, int B, int r, int c, int64_t* blk,
+                               int32_t* changed, int32_t* pass_flags, int pass, hipStream_t s);
+// mix_L = bf16(raw * tril + I), per channel.
+hipError_t launch_fold_mixer(const uint16_t* raw, int r, int B, uint16_t* mix_L, hipStream_t s);
+// blk[n, 0] = anchor[n] (the step without the argmax start).
+hipError_t launch_set_anchor(const int64_t* anchor, int N, int B, int64_t* blk, hipStream_t s);
+// Step bookkeeping: zero the per-pass change flags; count the passes that ran.
+hipError_t launch_flags_reset(int32_t* flags, int n, hipStream_t s);
+hipError_t launch_count_passes(const int32_t* flags, int K, int stop, int32_t* passes_run,
+                               hipStream_t s);
+
+}  // namespace xpress

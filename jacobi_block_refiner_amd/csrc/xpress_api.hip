@@ -1,0 +1,381 @@
+// C ABI of the XPress pass library: argument checks, workspace carving and kernel sequencing.
+// Every entry point validates on the host, then only enqueues kernels on the caller's stream.
+#include "xpress.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+xpress_status fail(xpress_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+xpress_status hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(XPRESS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return XPRESS_OK;
+}
+
+#define XP_TRY(expr, what)                                   \
+  do {                                                       \
+    xpress_status st_ = hip_check((expr), (what));           \
+    if (st_ != XPRESS_OK) return st_;                        \
+  } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+xpress_status check_ptr(const void* p, const char* name) {
+  if (p == nullptr) return fail(XPRESS_ERR_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(XPRESS_ERR_ARG, "%s is not 16-byte aligned", name);
+  return XPRESS_OK;
+}
+
+#define XP_PTR(p)                                        \
+  do {                                                   \
+    xpress_status st_ = check_ptr((p), #p);              \
+    if (st_ != XPRESS_OK) return st_;                    \
+  } while (0)
+
+xpress_status check_dims(int B, int r, int64_t V) {
+  if (B < 2 || B > 16) return fail(XPRESS_ERR_ARG, "B=%d outside [2, 16]", B);
+  if (r != 64 && r != 128 && r != 256) return fail(XPRESS_ERR_ARG, "r=%d not in {64,128,256}", r);
+  if (V < 1 || V * (int64_t)r >= ((int64_t)1 << 31))
+    return fail(XPRESS_ERR_ARG, "V=%lld outside [1, 2^31/r)", (long long)V);
+  return XPRESS_OK;
+}
+
+xpress_status check_weights(const xpress_weights* w, bool need_hidden, bool need_latent,
+                            bool need_w2) {
+  if (w == nullptr) return fail(XPRESS_ERR_ARG, "weights struct is NULL");
+  xpress_status st = check_dims(w->B, w->r, w->V);
+  if (st != XPRESS_OK) return st;
+  if (need_hidden) {
+    if (w->H < 64 || w->H % 64) return fail(XPRESS_ERR_ARG, "H=%d not a positive multiple of 64", w->H);
+    XP_PTR(w->down_h);
+    XP_PTR(w->down_g);
+    XP_PTR(w->in_proj);
+  }
+  if (need_latent) {
+    const int M = w->M;
+    if (M != 64 && M != 128 && M != 256 && M != 512 && M != 1024)
+      return fail(XPRESS_ERR_ARG, "M=%d not in {64,128,256,512,1024}", M);
+    XP_PTR(w->w1);
+    XP_PTR(w->in_proj);
+    if (w->mix_L == nullptr) return fail(XPRESS_ERR_ARG, "w->mix_L is NULL");
+    XP_PTR(w->w_gate);
+    XP_PTR(w->w_up);
+    XP_PTR(w->w_down);
+  }
+  if (need_w2) XP_PTR(w->w2);
+  return XPRESS_OK;
+}
+
+xpress_status check_base(const xpress_bf16* base, int64_t ld, int64_t V) {
+  XP_PTR(base);
+  if (ld < V || ld % 8) return fail(XPRESS_ERR_ARG, "base_ld=%lld must be >= V=%lld and a multiple of 8",
+                                    (long long)ld, (long long)V);
+  return XPRESS_OK;
+}
+
+// Workspace regions of a call with N blocks.
+struct Layout {
+  size_t hdg = 0, xh = 0, lat = 0, part = 0, flags = 0, cand = 0, base_c = 0, w2c = 0, total = 0;
+};
+
+Layout step_layout(int N, int B, int r, int64_t V, int C, int K) {
+  Layout L;
+  const size_t rows = (size_t)N * (B - 1);
+  const size_t c = C > 0 ? (size_t)(C < V ? C : V) : 0;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += up256(bytes);
+    return at;
+  };
+  L.hdg = take((size_t)N * B * 2 * r * sizeof(float));
+  L.xh = take((size_t)N * B * r * sizeof(float));
+  L.lat = take(rows * r * 2);
+  L.part = take(C > 0 ? 0 : rows * (size_t)xpress::readout_tiles(V) * sizeof(uint2));
+  L.flags = take((size_t)(K + 1) * sizeof(int32_t));
+  L.cand = take(rows * c * sizeof(int64_t));
+  L.base_c = take(rows * c * 2);
+  L.w2c = take(rows * c * r * 2);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* xpress_last_error(void) { return g_err.c_str(); }
+
+xpress_status xpress_workspace_size(int32_t n_max, int32_t B, int32_t r, int64_t V, int32_t C,
+                                    int32_t k_max, size_t* bytes) {
+  if (bytes == nullptr) return fail(XPRESS_ERR_ARG, "bytes is NULL");
+  if (n_max < 0 || C < 0 || k_max < 0) return fail(XPRESS_ERR_ARG, "negative n_max, C or k_max");
+  xpress_status st = check_dims(B, r, V);
+  if (st != XPRESS_OK) return st;
+  *bytes = step_layout(n_max, B, r, V, C, k_max).total;
+  return XPRESS_OK;
+}
+
+xpress_status xpress_fold_mixer(const xpress_bf16* raw, int32_t r, int32_t B, xpress_bf16* mix_L,
+                                xpress_stream stream) {
+  xpress_status st = check_dims(B, r, 1);
+  if (st != XPRESS_OK) return st;
+  if (raw == nullptr || mix_L == nullptr) return fail(XPRESS_ERR_ARG, "raw or mix_L is NULL");
+  if (raw == mix_L) return fail(XPRESS_ERR_ARG, "mix_L must not alias raw");
+  XP_TRY(xpress::launch_fold_mixer(raw, r, B, mix_L, reinterpret_cast<hipStream_t>(stream)),
+         "fold mixer");
+  return XPRESS_OK;
+}
+
+xpress_status xpress_hidden_cache(const xpress_weights* w, const xpress_bf16* h, int32_t N,
+                                  float* xh, void* ws, size_t ws_bytes, xpress_stream stream) {
+  xpress_status st = check_weights(w, true, false, false);
+  if (st != XPRESS_OK) return st;
+  if (N < 0) return fail(XPRESS_ERR_ARG, "N=%d < 0", N);
+  if (N == 0) return XPRESS_OK;
+  XP_PTR(h);
+  XP_PTR(xh);
+  XP_PTR(ws);
+  const size_t need = (size_t)N * w->B * 2 * w->r * sizeof(float);
+  if (ws_bytes < need)
+    return fail(XPRESS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed for N=%d", ws_bytes, need, N);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float* hdg = static_cast<float*>(ws);
+  XP_TRY(xpress::launch_hidden_gemm(h, w->down_h, w->down_g, N * w->B, w->H, w->r, hdg, s), "hidden gemm");
+  XP_TRY(xpress::launch_hidden_project(hdg, w->in_proj, N, w->B, w->r, xh, s), "hidden project");
+  return XPRESS_OK;
+}
+
+xpress_status xpress_initial_block(const xpress_bf16* base, int64_t base_ld, const int64_t* anchor,
+                                   int32_t N, int32_t B, int64_t V, int64_t* blk,
+                                   xpress_stream stream) {
+  xpress_status st = check_dims(B, 64, V);
+  if (st != XPRESS_OK) return st;
+  if (N < 0) return fail(XPRESS_ERR_ARG, "N=%d < 0", N);
+  if (N == 0) return XPRESS_OK;
+  st = check_base(base, base_ld, V);
+  if (st != XPRESS_OK) return st;
+  XP_PTR(anchor);
+  XP_PTR(blk);
+  XP_TRY(xpress::launch_initial_block(base, base_ld, anchor, N, B, V, blk,
+                                      reinterpret_cast<hipStream_t>(stream)),
+         "initial block");
+  return XPRESS_OK;
+}
+
+xpress_status xpress_latent_pass(const xpress_weights* w, const int64_t* blk, const int64_t* am1,
+                                 const float* xh, int32_t N, xpress_bf16* lat,
+                                 xpress_stream stream) {
+  xpress_status st = check_weights(w, false, true, false);
+  if (st != XPRESS_OK) return st;
+  if (N < 0) return fail(XPRESS_ERR_ARG, "N=%d < 0", N);
+  if (N == 0) return XPRESS_OK;
+  XP_PTR(blk);
+  XP_PTR(am1);
+  XP_PTR(xh);
+  XP_PTR(lat);
+  XP_TRY(xpress::launch_latent(blk, am1, xh, w->w1, w->in_proj, w->mix_L, w->w_gate, w->w_up,
+                               w->w_down, N, w->B, w->r, w->M, w->V, lat, nullptr, 0,
+                               reinterpret_cast<hipStream_t>(stream)),
+         "latent");
+  return XPRESS_OK;
+}
+
+xpress_status xpress_readout_argmax(const xpress_weights* w, const xpress_bf16* lat,
+                                    const xpress_bf16* base, int64_t base_ld, int32_t N,
+                                    int64_t* blk, int32_t* changed, void* ws, size_t ws_bytes,
+                                    xpress_stream stream) {
+  xpress_status st = check_weights(w, false, false, true);
+  if (st != XPRESS_OK) return st;
+  if (N < 0) return fail(XPRESS_ERR_ARG, "N=%d < 0", N);
+  if (N == 0) return XPRESS_OK;
+  st = check_base(base, base_ld, w->V);
+  if (st != XPRESS_OK) return st;
+  XP_PTR(lat);
+  XP_PTR(blk);
+  XP_PTR(ws);
+  const int rows = N * (w->B - 1);
+  const int ntiles = xpress::readout_tiles(w->V);
+  const size_t need = (size_t)rows * ntiles * sizeof(uint2);
+  if (ws_bytes < need)
+    return fail(XPRESS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed for N=%d", ws_bytes, need, N);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint2* part = static_cast<uint2*>(ws);
+  XP_TRY(xpress::launch_readout_partial(lat, w->w2, base, base_ld, rows, w->V, w->r, part, nullptr, 0, s),
+         "readout");
+  XP_TRY(xpress::launch_argmax_reduce(part, ntiles, rows, w->B, blk, changed, nullptr, 0, s),
+         "argmax reduce");
+  return XPRESS_OK;
+}
+
+xpress_status xpress_readout_tiles(int64_t V, int32_t* ntiles) {
+  if (ntiles == nullptr) return fail(XPRESS_ERR_ARG, "ntiles is NULL");
+  xpress_status st = check_dims(2, 64, V);
+  if (st != XPRESS_OK) return st;
+  *ntiles = xpress::readout_tiles(V);
+  return XPRESS_OK;
+}
+
+xpress_status xpress_readout_partials(const xpress_weights* w, const xpress_bf16* lat,
+                                      const xpress_bf16* base, int64_t base_ld, int32_t N,
+                                      uint32_t* part, xpress_stream stream) {
+  xpress_status st = check_weights(w, false, false, true);
+  if (st != XPRESS_OK) return st;
+  if (N < 0) return fail(XPRESS_ERR_ARG, "N=%d < 0", N);
+  if (N == 0) return XPRESS_OK;
+  st = check_base(base, base_ld, w->V);
+  if (st != XPRESS_OK) return st;
+  XP_PTR(lat);
+  XP_PTR(part);
+  XP_TRY(xpress::launch_readout_partial(lat, w->w2, base, base_ld, N * (w->B - 1), w->V, w->r,
+                                        reinterpret_cast<uint2*>(part), nullptr, 0,
+                                        reinterpret_cast<hipStream_t>(stream)),
+         "readout");
+  return XPRESS_OK;
+}
+
+xpress_status xpress_argmax_reduce(const uint32_t* part, int32_t ntiles, int32_t N, int32_t B,
+                                   int64_t* blk, int32_t* changed, xpress_stream stream) {
+  if (B < 2 || B > 16) return fail(XPRESS_ERR_ARG, "B=%d outside [2, 16]", B);
+  if (N < 0 || ntiles < 1) return fail(XPRESS_ERR_ARG, "N=%d < 0 or ntiles=%d < 1", N, ntiles);
+  if (N == 0) return XPRESS_OK;
+  XP_PTR(part);
+  XP_PTR(blk);
+  XP_TRY(xpress::launch_argmax_reduce(reinterpret_cast<const uint2*>(part), ntiles, N * (B - 1), B,
+                                      blk, changed, nullptr, 0,
+                                      reinterpret_cast<hipStream_t>(stream)),
+         "argmax reduce");
+  return XPRESS_OK;
+}
+
+xpress_status xpress_topc_prepare(const xpress_weights* w, const xpress_bf16* base,
+                                  int64_t base_ld, int32_t N, int32_t C, int64_t* cand,
+                                  xpress_bf16* base_c, xpress_bf16* w2c, void* ws,
+                                  size_t ws_bytes, xpress_stream stream) {
+  (void)ws;
+  (void)ws_bytes;
+  xpress_status st = check_weights(w, false, false, true);
+  if (st != XPRESS_OK) return st;
+  if (N < 0) return fail(XPRESS_ERR_ARG, "N=%d < 0", N);
+  if (C < 1) return fail(XPRESS_ERR_ARG, "C=%d < 1", C);
+  if (N == 0) return XPRESS_OK;
+  st = check_base(base, base_ld, w->V);
+  if (st != XPRESS_OK) return st;
+  XP_PTR(cand);
+  XP_PTR(base_c);
+  XP_PTR(w2c);
+  const int c = (int)(C < w->V ? C : w->V);
+  const int rows = N * (w->B - 1);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  XP_TRY(xpress::launch_topc_select(base, base_ld, rows, w->V, c, cand, base_c, s), "top-C select");
+  XP_TRY(xpress::launch_topc_gather(cand, w->w2, rows, c, w->r, w2c, s), "top-C gather");
+  return XPRESS_OK;
+}
+
+xpress_status xpress_readout_argmax_topc(const xpress_bf16* lat, const xpress_bf16* w2c,
+                                         const xpress_bf16* base_c, const int64_t* cand,
+                                         int32_t N, int32_t B, int32_t r, int32_t c,
+                                         int64_t* blk, int32_t* changed, xpress_stream stream) {
+  xpress_status st = check_dims(B, r, 1);
+  if (st != XPRESS_OK) return st;
+  if (N < 0 || c < 1) return fail(XPRESS_ERR_ARG, "N=%d < 0 or c=%d < 1", N, c);
+  if (N == 0) return XPRESS_OK;
+  XP_PTR(lat);
+  XP_PTR(w2c);
+  if (base_c == nullptr || cand == nullptr || blk == nullptr)
+    return fail(XPRESS_ERR_ARG, "base_c, cand or blk is NULL");
+  XP_TRY(xpress::launch_topc_readout(lat, w2c, base_c, cand, N * (B - 1), B, r, c, blk, changed,
+                                     nullptr, 0, reinterpret_cast<hipStream_t>(stream)),
+         "top-C readout");
+  return XPRESS_OK;
+}
+
+xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
+                                 const xpress_bf16* base, int64_t base_ld, const int64_t* anchor,
+                                 const int64_t* am1, int32_t N, int32_t K, int32_t C,
+                                 uint32_t flags, int64_t* blk, int32_t* passes_run, void* ws,
+                                 size_t ws_bytes, xpress_stream stream) {
+  xpress_status st = check_weights(w, true, true, true);
+  if (st != XPRESS_OK) return st;
+  if (N < 0 || K < 0 || C < 0) return fail(XPRESS_ERR_ARG, "negative N, K or C");
+  if (flags & ~(uint32_t)(XPRESS_INIT_FROM_BASE | XPRESS_STOP_AT_FIXED_POINT))
+    return fail(XPRESS_ERR_ARG, "unknown flag bits 0x%x", flags);
+  if (N == 0) return XPRESS_OK;
+  st = check_base(base, base_ld, w->V);
+  if (st != XPRESS_OK) return st;
+  XP_PTR(h);
+  XP_PTR(anchor);
+  XP_PTR(am1);
+  XP_PTR(blk);
+  XP_PTR(ws);
+  const Layout L = step_layout(N, w->B, w->r, w->V, C, K);
+  if (ws_bytes < L.total)
+    return fail(XPRESS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed for N=%d, C=%d, K=%d",
+                ws_bytes, L.total, N, C, K);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int B = w->B, r = w->r, rows = N * (B - 1);
+  const int64_t V = w->V;
+  float* hdg = at<float>(ws, L.hdg);
+  float* xh = at<float>(ws, L.xh);
+  xpress_bf16* lat = at<xpress_bf16>(ws, L.lat);
+  XP_TRY(xpress::launch_hidden_gemm(h, w->down_h, w->down_g, N * B, w->H, r, hdg, s), "hidden gemm");
+  XP_TRY(xpress::launch_hidden_project(hdg, w->in_proj, N, B, r, xh, s), "hidden project");
+  if (flags & XPRESS_INIT_FROM_BASE)
+    XP_TRY(xpress::launch_initial_block(base, base_ld, anchor, N, B, V, blk, s), "initial block");
+  else
+    XP_TRY(xpress::launch_set_anchor(anchor, N, B, blk, s), "set anchor");
+  const int c = C > 0 ? (int)(C < V ? C : V) : 0;
+  int64_t* cand = at<int64_t>(ws, L.cand);
+  xpress_bf16* base_c = at<xpress_bf16>(ws, L.base_c);
+  xpress_bf16* w2c = at<xpress_bf16>(ws, L.w2c);
+  if (c > 0) {
+    XP_TRY(xpress::launch_topc_select(base, base_ld, rows, V, c, cand, base_c, s), "top-C select");
+    XP_TRY(xpress::launch_topc_gather(cand, w->w2, rows, c, r, w2c, s), "top-C gather");
+  }
+  const bool stop = (flags & XPRESS_STOP_AT_FIXED_POINT) != 0;
+  int32_t* pf = stop ? at<int32_t>(ws, L.flags) : nullptr;
+  if (stop) XP_TRY(xpress::launch_flags_reset(pf, K + 1, s), "flags reset");
+  uint2* part = at<uint2>(ws, L.part);
+  const int ntiles = xpress::readout_tiles(V);
+  for (int p = 0; p < K; ++p) {
+    XP_TRY(xpress::launch_latent(blk, am1, xh, w->w1, w->in_proj, w->mix_L, w->w_gate, w->w_up,
+                                 w->w_down, N, B, r, w->M, V, lat, pf, p, s),
+           "latent");
+    if (c > 0) {
+      XP_TRY(xpress::launch_topc_readout(lat, w2c, base_c, cand, rows, B, r, c, blk, nullptr, pf, p, s),
+             "top-C readout");
+    } else {
+      XP_TRY(xpress::launch_readout_partial(lat, w->w2, base, base_ld, rows, V, r, part, pf, p, s),
+             "readout");
+      XP_TRY(xpress::launch_argmax_reduce(part, ntiles, rows, B, blk, nullptr, pf, p, s),
+             "argmax reduce");
+    }
+  }
+  if (passes_run) XP_TRY(xpress::launch_count_passes(pf, K, stop ? 1 : 0, passes_run, s), "count passes");
+  return XPRESS_OK;
+}
+
+}  // extern "C"

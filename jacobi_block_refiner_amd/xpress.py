@@ -1,0 +1,250 @@
+"""Thin ctypes binding of ``libxpress.so`` (the C ABI in ``include/xpress.h``).
+
+Argument marshalling only: tensors are passed as device pointers together with the current HIP
+stream of PyTorch, and every step of the method runs in the library's HIP kernels. There is no
+fallback: if the library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import re
+from dataclasses import dataclass
+from pathlib import Path
+
+import torch
+
+PKG = Path(__file__).resolve().parent
+LIB_PATH = PKG / "libxpress.so"
+HEADER = PKG.parent / "include" / "xpress.h"
+
+OK, ERR_ARG, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3
+INIT_FROM_BASE = 1
+STOP_AT_FIXED_POINT = 2
+
+
+class XpressError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"xpress status {status}: {message}")
+        self.status = status
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("r", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("M", ctypes.c_int32), ("V", ctypes.c_int64),
+        ("w1", ctypes.c_void_p), ("down_h", ctypes.c_void_p), ("down_g", ctypes.c_void_p),
+        ("in_proj", ctypes.c_void_p), ("mix_L", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
+        ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def declared_symbols() -> list[str]:
+    """Function names declared in include/xpress.h."""
+    text = HEADER.read_text()
+    return re.findall(r"^(?:xpress_status|const char\*)\s+(xpress_\w+)\(", text, flags=re.M)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library. Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with jacobi_block_refiner_amd.build.build()")
+        L = ctypes.CDLL(str(LIB_PATH))
+        P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        W = ctypes.POINTER(_Weights)
+        sig = {
+            "xpress_workspace_size": [i32, i32, i32, i64, i32, i32, ctypes.POINTER(sz)],
+            "xpress_fold_mixer": [P, i32, i32, P, P],
+            "xpress_hidden_cache": [W, P, i32, P, P, sz, P],
+            "xpress_initial_block": [P, i64, P, i32, i32, i64, P, P],
+            "xpress_latent_pass": [W, P, P, P, i32, P, P],
+            "xpress_readout_argmax": [W, P, P, i64, i32, P, P, P, sz, P],
+            "xpress_readout_tiles": [i64, ctypes.POINTER(i32)],
+            "xpress_readout_partials": [W, P, P, i64, i32, P, P],
+            "xpress_argmax_reduce": [P, i32, i32, i32, P, P, P],
+            "xpress_topc_prepare": [W, P, i64, i32, i32, P, P, P, P, sz, P],
+            "xpress_readout_argmax_topc": [P, P, P, P, i32, i32, i32, i32, P, P, P],
+            "xpress_jacobi_step": [W, P, P, i64, P, P, i32, i32, i32, ctypes.c_uint32, P, P, P,
+                                   sz, P],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.xpress_last_error.restype = ctypes.c_char_p
+        L.xpress_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        msg = lib().xpress_last_error().decode()
+        raise XpressError(status, msg)
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _bf16(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.bfloat16 or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA bfloat16 tensor")
+    return t
+
+
+@dataclass
+class Weights:
+    """Device bf16 weights of one refiner head, ``nn.Linear`` layouts; ``mix_L`` is folded."""
+
+    w1: torch.Tensor
+    down_h: torch.Tensor
+    down_g: torch.Tensor
+    in_proj: torch.Tensor
+    mix_L: torch.Tensor
+    w_gate: torch.Tensor
+    w_up: torch.Tensor
+    w_down: torch.Tensor
+    w2: torch.Tensor
+
+    @property
+    def dims(self):
+        V, r = self.w1.shape
+        return dict(B=self.mix_L.shape[1], r=r, H=self.down_h.shape[1], M=self.w_gate.shape[0],
+                    V=V)
+
+    def struct(self) -> _Weights:
+        d = self.dims
+        s = _Weights(B=d["B"], r=d["r"], H=d["H"], M=d["M"], V=d["V"])
+        for k in ("w1", "down_h", "down_g", "in_proj", "mix_L", "w_gate", "w_up", "w_down", "w2"):
+            t = _bf16(getattr(self, k), k)
+            if not t.is_contiguous():
+                raise ValueError(f"{k} must be contiguous")
+            setattr(s, k, t.data_ptr())
+        return s
+
+
+def workspace_size(n_max: int, B: int, r: int, V: int, C: int, k_max: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().xpress_workspace_size(n_max, B, r, V, C, k_max, ctypes.byref(out)))
+    return int(out.value)
+
+
+def alloc_workspace(n_max: int, B: int, r: int, V: int, C: int, k_max: int, device="cuda"):
+    n = workspace_size(n_max, B, r, V, C, k_max)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def fold_mixer(raw: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    raw = _bf16(raw, "raw").contiguous()
+    r, B, _ = raw.shape
+    out = torch.empty_like(raw) if out is None else out
+    _check(lib().xpress_fold_mixer(_ptr(raw), r, B, _ptr(out), _stream()))
+    return out
+
+
+def hidden_cache(w: Weights, h: torch.Tensor, xh: torch.Tensor, ws: torch.Tensor) -> torch.Tensor:
+    s = w.struct()
+    N = h.shape[0]
+    _check(lib().xpress_hidden_cache(ctypes.byref(s), _ptr(_bf16(h, "h")), N, _ptr(xh), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream()))
+    return xh
+
+
+def initial_block(base: torch.Tensor, anchor: torch.Tensor, blk: torch.Tensor) -> torch.Tensor:
+    _bf16(base, "base")
+    assert base.stride(1) == 1
+    N, B = blk.shape
+    _check(lib().xpress_initial_block(ctypes.c_void_p(base.data_ptr()), base.stride(0),
+                                      _ptr(anchor), N, B, base.shape[1], _ptr(blk), _stream()))
+    return blk
+
+
+def latent_pass(w: Weights, blk, am1, xh, lat) -> torch.Tensor:
+    s = w.struct()
+    N = blk.shape[0]
+    _check(lib().xpress_latent_pass(ctypes.byref(s), _ptr(blk), _ptr(am1), _ptr(xh), N,
+                                    _ptr(lat), _stream()))
+    return lat
+
+
+def readout_argmax(w: Weights, lat, base, blk, ws, changed=None) -> torch.Tensor:
+    s = w.struct()
+    _bf16(base, "base")
+    assert base.stride(1) == 1
+    N = blk.shape[0]
+    _check(lib().xpress_readout_argmax(ctypes.byref(s), _ptr(lat), ctypes.c_void_p(base.data_ptr()),
+                                       base.stride(0), N, _ptr(blk), _ptr(changed), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream()))
+    return blk
+
+
+def readout_tiles(V: int) -> int:
+    out = ctypes.c_int32()
+    _check(lib().xpress_readout_tiles(V, ctypes.byref(out)))
+    return int(out.value)
+
+
+def readout_partials(w: Weights, lat, base, part: torch.Tensor) -> torch.Tensor:
+    """part: int32/uint32-compatible tensor [rows, ntiles, 2] (value bits, id)."""
+    s = w.struct()
+    _bf16(base, "base")
+    assert base.stride(1) == 1
+    rows = lat.numel() // lat.shape[-1]
+    N = rows // (w.dims["B"] - 1)
+    _check(lib().xpress_readout_partials(ctypes.byref(s), _ptr(lat), ctypes.c_void_p(base.data_ptr()),
+                                         base.stride(0), N, _ptr(part), _stream()))
+    return part
+
+
+def argmax_reduce(part: torch.Tensor, blk: torch.Tensor, changed=None) -> torch.Tensor:
+    N, B = blk.shape
+    ntiles = part.shape[1]
+    _check(lib().xpress_argmax_reduce(_ptr(part), ntiles, N, B, _ptr(blk), _ptr(changed),
+                                      _stream()))
+    return blk
+
+
+def topc_prepare(w: Weights, base, N: int, C: int, cand, base_c, w2c, ws=None):
+    s = w.struct()
+    _bf16(base, "base")
+    assert base.stride(1) == 1
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().xpress_topc_prepare(ctypes.byref(s), ctypes.c_void_p(base.data_ptr()),
+                                     base.stride(0), N, C, _ptr(cand), _ptr(base_c), _ptr(w2c),
+                                     _ptr(ws), nbytes, _stream()))
+    return cand, base_c, w2c
+
+
+def readout_argmax_topc(lat, w2c, base_c, cand, blk, changed=None) -> torch.Tensor:
+    N, B = blk.shape
+    rows, c, r = w2c.shape
+    _check(lib().xpress_readout_argmax_topc(_ptr(lat), _ptr(w2c), _ptr(base_c), _ptr(cand), N, B,
+                                            r, c, _ptr(blk), _ptr(changed), _stream()))
+    return blk
+
+
+def jacobi_step(w: Weights, h, base, anchor, am1, blk, *, K: int, C: int = 0,
+                flags: int = INIT_FROM_BASE, ws: torch.Tensor, passes_run=None) -> torch.Tensor:
+    s = w.struct()
+    _bf16(base, "base")
+    assert base.stride(1) == 1
+    N = blk.shape[0]
+    _check(lib().xpress_jacobi_step(ctypes.byref(s), _ptr(_bf16(h, "h")),
+                                    ctypes.c_void_p(base.data_ptr()), base.stride(0), _ptr(anchor),
+                                    _ptr(am1), N, K, C, flags, _ptr(blk), _ptr(passes_run),
+                                    _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return blk

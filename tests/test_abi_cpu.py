@@ -1,0 +1,80 @@
+"""The C-ABI library without a GPU: it loads, exports every declared entry point, and rejects bad
+arguments on the host (no kernel is launched by any call here)."""
+import ctypes
+import subprocess
+
+import pytest
+
+from jacobi_block_refiner_amd import xpress
+
+
+def test_library_exports_every_declared_symbol():
+    names = xpress.declared_symbols()
+    assert len(names) >= 10
+    L = xpress.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", str(xpress.LIB_PATH)], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+
+
+def test_workspace_size_grows_with_blocks_and_candidates():
+    a = xpress.workspace_size(32, 16, 256, 151936, 0, 15)
+    b = xpress.workspace_size(256, 16, 256, 151936, 0, 15)
+    c = xpress.workspace_size(32, 16, 256, 151936, 512, 15)
+    assert 0 < a < b
+    # top-C holds w2c [rows, C, r] bf16 = 125.8 MB at 32 blocks of 15 draft rows
+    assert c >= 480 * 512 * 256 * 2
+
+
+@pytest.mark.parametrize("B,r,V", [(1, 256, 1000), (17, 256, 1000), (16, 96, 1000),
+                                   (16, 256, 0), (16, 256, 1 << 24)])
+def test_bad_shapes_are_rejected(B, r, V):
+    out = ctypes.c_size_t()
+    st = xpress.lib().xpress_workspace_size(4, B, r, V, 0, 1, ctypes.byref(out))
+    assert st == xpress.ERR_ARG
+    assert xpress.lib().xpress_last_error()
+
+
+def test_null_weights_and_pointers_are_rejected():
+    L = xpress.lib()
+    st = L.xpress_latent_pass(None, None, None, None, 4, None, None)
+    assert st == xpress.ERR_ARG and b"NULL" in L.xpress_last_error()
+    w = xpress._Weights(B=16, r=256, H=4096, M=512, V=151936)
+    st = L.xpress_jacobi_step(ctypes.byref(w), None, None, 151936, None, None, 4, 15, 0, 1, None,
+                              None, None, 0, None)
+    assert st == xpress.ERR_ARG
+    st = L.xpress_fold_mixer(None, 256, 16, None, None)
+    assert st == xpress.ERR_ARG
+
+
+def test_n_zero_is_a_noop_and_unknown_flags_are_rejected():
+    L = xpress.lib()
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced
+    w = xpress._Weights(B=16, r=256, H=4096, M=512, V=151936, w1=fake, down_h=fake,
+                        down_g=fake, in_proj=fake, mix_L=fake, w_gate=fake, w_up=fake,
+                        w_down=fake, w2=fake)
+    assert L.xpress_latent_pass(ctypes.byref(w), fake, fake, fake, 0, fake, None) == xpress.OK
+    st = L.xpress_jacobi_step(ctypes.byref(w), fake, fake, 151936, fake, fake, 4, 15, 0, 0x10,
+                              fake, None, fake, 1 << 30, None)
+    assert st == xpress.ERR_ARG and b"flag" in L.xpress_last_error()
+
+
+def test_small_workspace_and_bad_stride_are_rejected():
+    L = xpress.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    w = xpress._Weights(B=16, r=256, H=4096, M=512, V=151936, w1=fake, down_h=fake,
+                        down_g=fake, in_proj=fake, mix_L=fake, w_gate=fake, w_up=fake,
+                        w_down=fake, w2=fake)
+    st = L.xpress_readout_argmax(ctypes.byref(w), fake, fake, 151936, 4, fake, None, fake, 16,
+                                 None)
+    assert st == xpress.ERR_WORKSPACE
+    st = L.xpress_readout_argmax(ctypes.byref(w), fake, fake, 151937, 4, fake, None, fake,
+                                 1 << 30, None)
+    assert st == xpress.ERR_ARG
+    misaligned = ctypes.c_void_p((1 << 20) + 2)
+    st = L.xpress_readout_argmax(ctypes.byref(w), misaligned, fake, 151936, 4, fake, None, fake,
+                                 1 << 30, None)
+    assert st == xpress.ERR_ARG and b"aligned" in L.xpress_last_error()

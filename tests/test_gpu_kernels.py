@@ -1,0 +1,378 @@
+"""GPU parity of each kernel of the XPress pass against the CPU oracle, on small seeded inputs
+that span several tiles and a ragged tail. Every call goes through the C ABI."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from jacobi_block_refiner_amd import synth, upload, xpress
+from oracle import oracle as O
+from tests.gpu_helpers import (LAT_RTOL, NEAR_TIE, Dev, compare_tokens, draft_rows, end_to_end_ok,
+                               lat_rel_err, lat_to_f64, log, oracle_mixer, strong)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    xpress.lib()
+    torch.cuda.set_device(0)
+
+
+def _dyadic(rng, shape, lo, hi, den):
+    return (rng.integers(lo, hi + 1, size=shape) / den).astype(np.float32)
+
+
+def _readout_case(seed, N, B, r, V, *, zero_head=False):
+    """Dyadic lat / w2 / base (exact in bf16 and in every fp32 partial sum) with planted ties."""
+    rng = np.random.default_rng(seed)
+    rows = N * (B - 1)
+    lat = _dyadic(rng, (rows, r), -4, 4, 16)
+    w2 = np.zeros((V, r), np.float32) if zero_head else _dyadic(rng, (V, r), -4, 4, 16)
+    base = _dyadic(rng, (rows, V), -8, 8, 4)
+    for p in range(0, rows, 3):  # exact top ties between a high and a low id
+        hi, lo = V - 1 - p % 7, p % 5
+        w2[lo] = w2[hi]
+        base[p, hi] = base[p, lo] = 31.75
+    return lat, w2, base
+
+
+def _weights_with(w2_np, r, B, V, device="cuda"):
+    z = lambda *s: torch.zeros(*s, dtype=torch.bfloat16, device=device)
+    return xpress.Weights(w1=z(V, r), down_h=z(r, 64), down_g=z(r, 64), in_proj=z(r, 3 * r),
+                          mix_L=z(r, B, B), w_gate=z(64, r), w_up=z(64, r), w_down=z(r, 64),
+                          w2=upload.bf16_tensor(w2_np, device))
+
+
+# ----------------------------------------------------------------------------------------------
+
+def test_fold_mixer_bit_exact():
+    rng = np.random.default_rng(0)
+    for r, B in ((64, 4), (256, 16)):
+        raw = synth.bf16_round(rng.standard_normal((r, B, B)).astype(np.float32) * 0.05)
+        got = xpress.fold_mixer(upload.bf16_tensor(raw)).float().cpu().numpy()
+        inp = replace(synth.make_inputs(1), raw_L=raw)
+        assert np.array_equal(got.astype(np.float64), oracle_mixer(inp))
+
+
+@pytest.mark.parametrize("V", [5003, 8192])
+def test_initial_block_exact(V):
+    rng = np.random.default_rng(1)
+    N, B = 5, 16
+    rows = N * (B - 1)
+    base = synth.bf16_round(rng.standard_normal((rows, V)).astype(np.float32) * 2)
+    top = base.argmax(1)
+    for p in range(0, rows, 2):  # duplicated maxima below and above the first one
+        base[p, (top[p] + 1 + p) % V] = base[p, top[p]]
+    base[3, :] = 0.0
+    base[3, 17] = -0.0  # -0 ties +0; id 0 must win
+    anchor = rng.integers(0, V, N)
+    blk = torch.full((N, B), -1, dtype=torch.int64, device="cuda")
+    xpress.initial_block(upload.base_logits(base), upload.tokens(anchor), blk)
+    torch.cuda.synchronize()
+    want = O.initial_block(base, anchor, N, B)
+    assert np.array_equal(blk.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("r,V,N", [(64, 5003, 3), (256, 5003, 5), (256, 8192, 3), (128, 700, 2)])
+def test_readout_argmax_dyadic_exact(r, V, N):
+    """Every fp32 partial sum is exact, so the GPU must match the oracle on every row, ties
+    included (lowest id), with no near-tie exemption."""
+    B = 16
+    lat, w2, base = _readout_case(2, N, B, r, V)
+    w = _weights_with(w2, r, B, V)
+    rng = np.random.default_rng(3)
+    blk0 = rng.integers(0, V, (N, B))
+    blk = upload.tokens(blk0)
+    changed = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = xpress.alloc_workspace(N, B, r, V, 0, 1)
+    log(f"readout dyadic r={r} V={V} N={N}")
+    xpress.readout_argmax(w, upload.bf16_tensor(lat), upload.base_logits(base), blk, ws, changed)
+    torch.cuda.synchronize()
+    best, gap, _ = O.readout_argmax(lat, w2, base)
+    got = blk.cpu().numpy()
+    assert np.array_equal(got[:, 0], blk0[:, 0])  # the anchor slot is never written
+    assert np.array_equal(draft_rows(got), best)
+    assert (gap == 0).sum() >= len(range(0, N * (B - 1), 3))
+    assert int(changed.item()) == int(not np.array_equal(draft_rows(blk0), best))
+
+
+def test_readout_zero_head_is_argmax_of_base():
+    N, B, r, V = 4, 16, 256, 4099
+    lat, w2, base = _readout_case(4, N, B, r, V, zero_head=True)
+    lat = lat * 1000
+    w = _weights_with(w2, r, B, V)
+    blk = torch.zeros(N, B, dtype=torch.int64, device="cuda")
+    xpress.readout_argmax(w, upload.bf16_tensor(lat), upload.base_logits(base), blk,
+                          xpress.alloc_workspace(N, B, r, V, 0, 1))
+    torch.cuda.synchronize()
+    assert np.array_equal(draft_rows(blk.cpu().numpy()), np.argmax(base, axis=1))
+
+
+def test_readout_changed_flag_stays_clear_at_a_fixed_point():
+    N, B, r, V = 2, 16, 64, 3000
+    lat, w2, base = _readout_case(5, N, B, r, V)
+    best, _, _ = O.readout_argmax(lat, w2, base)
+    blk0 = np.zeros((N, B), np.int64)
+    blk0[:, 1:] = best.reshape(N, B - 1)
+    blk = upload.tokens(blk0)
+    changed = torch.zeros(1, dtype=torch.int32, device="cuda")
+    xpress.readout_argmax(_weights_with(w2, r, B, V), upload.bf16_tensor(lat),
+                          upload.base_logits(base), blk, xpress.alloc_workspace(N, B, r, V, 0, 1),
+                          changed)
+    torch.cuda.synchronize()
+    assert int(changed.item()) == 0 and np.array_equal(blk.cpu().numpy(), blk0)
+
+
+@pytest.mark.parametrize("H,r,N,B", [(256, 64, 3, 4), (4096, 256, 3, 16), (320, 128, 2, 7)])
+def test_hidden_cache_parity(H, r, N, B):
+    base_wl = synth.WORKLOADS[1] if r == 64 else synth.WORKLOADS[3]
+    wl = replace(base_wl, N=N, B=B, H=H, r=r, V=512, M=128)
+    inp = synth.make_inputs(wl).rounded_bf16()
+    d = Dev(inp)
+    got = d.xh().cpu().numpy().astype(np.float64)
+    want = O.hidden_cache(inp.h, inp.down_h, inp.down_g, inp.in_proj)
+    err = lat_rel_err(got, want)
+    log(f"hidden cache H={H} r={r}: row-relative error {err:.2e}")
+    assert err < 1e-4
+
+
+def _latent_case(wl_id, N, seed=0, **over):
+    wl = replace(synth.WORKLOADS[wl_id], N=N, **over)
+    inp = synth.make_inputs(wl, seed=seed).rounded_bf16()
+    rng = np.random.default_rng(seed + 100)
+    xh = (rng.standard_normal((N, wl.B, wl.r)) * 0.5).astype(np.float32)
+    return inp, xh
+
+
+@pytest.mark.parametrize("wl_id,N,over", [(1, 3, {}), (3, 3, {"V": 4096}),
+                                         (1, 2, {"B": 7, "M": 256, "r": 128}),
+                                         (3, 2, {"V": 2048, "M": 1024})])
+def test_latent_parity(wl_id, N, over):
+    inp, xh = _latent_case(wl_id, N, **over)
+    d = Dev(inp)
+    lat = torch.empty(N, inp.wl.B - 1, inp.wl.r, dtype=torch.bfloat16, device="cuda")
+    xpress.latent_pass(d.w, upload.tokens(inp.blk), d.am1, torch.from_numpy(xh).cuda(), lat)
+    torch.cuda.synchronize()
+    want = O.latent(inp, oracle_mixer(inp), xh.astype(np.float64), inp.blk, inp.am1)
+    err = lat_rel_err(lat_to_f64(lat), want)
+    log(f"latent wl{wl_id} {over}: row-relative error {err:.2e}")
+    assert err < LAT_RTOL
+
+
+def test_latent_causality_bit_invariance():
+    inp, xh = _latent_case(3, 3, V=4096)
+    d = Dev(inp)
+    xh_t = torch.from_numpy(xh).cuda()
+    B = inp.wl.B
+    lat0 = torch.empty(3, B - 1, inp.wl.r, dtype=torch.bfloat16, device="cuda")
+    xpress.latent_pass(d.w, upload.tokens(inp.blk), d.am1, xh_t, lat0)
+    for b in (1, 5, 14):
+        blk2 = inp.blk.copy()
+        blk2[:, b:] = (blk2[:, b:] + 777) % inp.wl.V
+        lat1 = torch.empty_like(lat0)
+        xpress.latent_pass(d.w, upload.tokens(blk2), d.am1, xh_t, lat1)
+        torch.cuda.synchronize()
+        a = lat0.view(torch.int16).cpu().numpy()
+        c = lat1.view(torch.int16).cpu().numpy()
+        assert np.array_equal(a[:, :b], c[:, :b])
+        assert not np.array_equal(a[:, b:], c[:, b:])
+
+
+def test_latent_repeat_is_bit_identical():
+    inp, xh = _latent_case(3, 4, V=4096)
+    d = Dev(inp)
+    xh_t = torch.from_numpy(xh).cuda()
+    outs = []
+    for _ in range(3):
+        lat = torch.empty(4, inp.wl.B - 1, inp.wl.r, dtype=torch.bfloat16, device="cuda")
+        xpress.latent_pass(d.w, upload.tokens(inp.blk), d.am1, xh_t, lat)
+        outs.append(lat.view(torch.int16).cpu().numpy())
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+# ----------------------------------------------------------------------------------------------
+# one pass, teacher-forced; whole steps
+
+def _oracle_pass(inp, blk_p, cand=None):
+    L = oracle_mixer(inp)
+    xh = O.hidden_cache(inp.h, inp.down_h, inp.down_g, inp.in_proj)
+    nb, _, _, hg = O.jacobi(inp, L, xh, blk_p, K=1, stop_at_fixed_point=False, cand=cand,
+                            history=True)
+    return nb, hg[0]
+
+
+@pytest.mark.parametrize("variant", ["tiny", "strong", "wide"])
+def test_one_pass_teacher_forced(variant):
+    if variant == "tiny":
+        inp = synth.make_inputs(1).rounded_bf16()
+    elif variant == "strong":
+        inp = strong(synth.make_inputs(replace(synth.WORKLOADS[1], B=8), N=6))
+    else:
+        inp = synth.make_inputs(replace(synth.WORKLOADS[3], V=9000), N=3)
+    d = Dev(inp)
+    xh = d.xh()
+    got, _ = d.one_pass(inp.blk, xh)
+    want, gap = _oracle_pass(inp, inp.blk)
+    assert np.array_equal(got[:, 0], inp.blk[:, 0])
+    bad, exempt = compare_tokens(draft_rows(got), draft_rows(want), gap)
+    log(f"one pass {variant}: mismatches {bad}, near-tie rows {exempt}")
+    assert bad == 0
+
+
+@pytest.mark.parametrize("variant", ["tiny", "strong"])
+@pytest.mark.parametrize("init", [True, False])
+def test_step_to_fixed_point_matches_oracle(variant, init):
+    if variant == "tiny":
+        inp = synth.make_inputs(1).rounded_bf16()
+    else:
+        inp = strong(synth.make_inputs(replace(synth.WORKLOADS[1], B=8), N=6, seed=2))
+    wl = inp.wl
+    B = inp.raw_L.shape[1]
+    N = inp.blk.shape[0]
+    d = Dev(inp)
+    blk = upload.tokens(inp.blk)
+    passes = torch.zeros(1, dtype=torch.int32, device="cuda")
+    flags = xpress.STOP_AT_FIXED_POINT | (xpress.INIT_FROM_BASE if init else 0)
+    K = 2 * B
+    xpress.jacobi_step(d.w, d.h, d.base, d.anchor, d.am1, blk, K=K, flags=flags,
+                       ws=xpress.alloc_workspace(N, B, wl.r, wl.V, 0, K), passes_run=passes)
+    torch.cuda.synchronize()
+    L = oracle_mixer(inp)
+    xh = O.hidden_cache(inp.h, inp.down_h, inp.down_g, inp.in_proj)
+    start = O.initial_block(inp.base, inp.anchor, N, B) if init else inp.blk
+    want, n_pass, _, hg = O.jacobi(inp, L, xh, start, K=K, stop_at_fixed_point=True,
+                                   history=True)
+    got = blk.cpu().numpy()
+    log(f"step {variant} init={init}: passes gpu {int(passes.item())} oracle {n_pass}, "
+        f"min gap {hg.min():.3g}")
+    bad, exempt = end_to_end_ok(got, want, hg)
+    assert bad == 0
+    if exempt == 0:
+        assert np.array_equal(got, want)
+        assert int(passes.item()) == n_pass <= B
+        seq = O.sequential_greedy(inp, L, xh, inp.anchor)
+        assert np.array_equal(got, seq)
+
+
+def test_step_fixed_k_runs_every_pass_and_is_deterministic():
+    inp = strong(synth.make_inputs(replace(synth.WORKLOADS[1], B=8), N=6, seed=4))
+    N, B = inp.blk.shape
+    d = Dev(inp)
+    outs = []
+    for _ in range(2):
+        blk = upload.tokens(inp.blk)
+        passes = torch.zeros(1, dtype=torch.int32, device="cuda")
+        xpress.jacobi_step(d.w, d.h, d.base, d.anchor, d.am1, blk, K=3, flags=0,
+                           ws=xpress.alloc_workspace(N, B, inp.wl.r, inp.wl.V, 0, 3),
+                           passes_run=passes)
+        torch.cuda.synchronize()
+        assert int(passes.item()) == 3
+        outs.append(blk.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    L = oracle_mixer(inp)
+    xh = O.hidden_cache(inp.h, inp.down_h, inp.down_g, inp.in_proj)
+    start = inp.blk.copy()
+    start[:, 0] = inp.anchor
+    want, _, _, hg = O.jacobi(inp, L, xh, start, K=3, stop_at_fixed_point=False, history=True)
+    assert end_to_end_ok(outs[0], want, hg)[0] == 0
+
+
+# ----------------------------------------------------------------------------------------------
+# top-C
+
+@pytest.mark.parametrize("C,V", [(64, 5003), (512, 8192), (700, 700), (1, 3000)])
+def test_topc_prepare_exact(C, V):
+    rng = np.random.default_rng(6)
+    N, B, r = 3, 16, 64
+    rows = N * (B - 1)
+    base = (np.round(rng.standard_normal((rows, V)) * 4) / 4).astype(np.float32)  # many ties
+    base[0, :] = 0.0
+    base[0, 5] = -0.0
+    w2 = synth.bf16_round(rng.standard_normal((V, r)).astype(np.float32))
+    w = _weights_with(w2, r, B, V)
+    c = min(C, V)
+    cand = torch.empty(rows, c, dtype=torch.int64, device="cuda")
+    base_c = torch.empty(rows, c, dtype=torch.bfloat16, device="cuda")
+    w2c = torch.empty(rows, c, r, dtype=torch.bfloat16, device="cuda")
+    xpress.topc_prepare(w, upload.base_logits(base), N, C, cand, base_c, w2c)
+    torch.cuda.synchronize()
+    want = O.topc_select(base, C)
+    got = cand.cpu().numpy()
+    assert np.array_equal(got, want)
+    assert np.array_equal(base_c.float().cpu().numpy(), np.take_along_axis(base, want, axis=1))
+    assert np.array_equal(w2c.float().cpu().numpy(), w2[want])
+
+
+def test_topc_readout_dyadic_exact_and_membership():
+    rng = np.random.default_rng(7)
+    N, B, r, V, C = 4, 16, 256, 6000, 96
+    lat, w2, base = _readout_case(8, N, B, r, V)
+    w = _weights_with(w2, r, B, V)
+    rows = N * (B - 1)
+    cand = torch.empty(rows, C, dtype=torch.int64, device="cuda")
+    base_c = torch.empty(rows, C, dtype=torch.bfloat16, device="cuda")
+    w2c = torch.empty(rows, C, r, dtype=torch.bfloat16, device="cuda")
+    xpress.topc_prepare(w, upload.base_logits(base), N, C, cand, base_c, w2c)
+    blk0 = rng.integers(0, V, (N, B))
+    blk = upload.tokens(blk0)
+    xpress.readout_argmax_topc(upload.bf16_tensor(lat), w2c, base_c, cand, blk)
+    torch.cuda.synchronize()
+    cand_o = O.topc_select(base, C)
+    best, gap, _ = O.readout_argmax(lat, w2, base, cand=cand_o)
+    got = draft_rows(blk.cpu().numpy())
+    assert np.array_equal(got, best)
+    for p in range(rows):
+        assert got[p] in cand_o[p]
+
+
+@pytest.mark.parametrize("C", [1, 10 ** 6])
+def test_topc_step_limits(C):
+    """C = 1 always returns argmax(base); C >= V scores every id, as the full-vocabulary step."""
+    inp = strong(synth.make_inputs(replace(synth.WORKLOADS[1], B=8), N=4, seed=5))
+    N, B = inp.blk.shape
+    wl = inp.wl
+    d = Dev(inp)
+    blk = upload.tokens(inp.blk)
+    xpress.jacobi_step(d.w, d.h, d.base, d.anchor, d.am1, blk, K=4, C=C,
+                       flags=xpress.INIT_FROM_BASE,
+                       ws=xpress.alloc_workspace(N, B, wl.r, wl.V, C, 4))
+    torch.cuda.synchronize()
+    got = blk.cpu().numpy()
+    if C == 1:
+        assert np.array_equal(draft_rows(got), np.argmax(inp.base, axis=1))
+        return
+    L = oracle_mixer(inp)
+    xh = O.hidden_cache(inp.h, inp.down_h, inp.down_g, inp.in_proj)
+    start = O.initial_block(inp.base, inp.anchor, N, B)
+    want, _, _, hg = O.jacobi(inp, L, xh, start, K=4, stop_at_fixed_point=False, history=True)
+    assert end_to_end_ok(got, want, hg)[0] == 0
+
+
+def test_topc_step_matches_oracle():
+    inp = strong(synth.make_inputs(replace(synth.WORKLOADS[1], B=8), N=6, seed=6))
+    N, B = inp.blk.shape
+    wl = inp.wl
+    C = 48
+    d = Dev(inp)
+    blk = upload.tokens(inp.blk)
+    passes = torch.zeros(1, dtype=torch.int32, device="cuda")
+    xpress.jacobi_step(d.w, d.h, d.base, d.anchor, d.am1, blk, K=2 * B, C=C,
+                       flags=xpress.INIT_FROM_BASE | xpress.STOP_AT_FIXED_POINT,
+                       ws=xpress.alloc_workspace(N, B, wl.r, wl.V, C, 2 * B), passes_run=passes)
+    torch.cuda.synchronize()
+    L = oracle_mixer(inp)
+    xh = O.hidden_cache(inp.h, inp.down_h, inp.down_g, inp.in_proj)
+    cand = O.topc_select(inp.base, C)
+    start = O.initial_block(inp.base, inp.anchor, N, B)
+    want, n_pass, _, hg = O.jacobi(inp, L, xh, start, K=2 * B, stop_at_fixed_point=True,
+                                   cand=cand, history=True)
+    got = blk.cpu().numpy()
+    bad, exempt = end_to_end_ok(got, want, hg)
+    assert bad == 0
+    if exempt == 0:
+        assert int(passes.item()) == n_pass
+    for p, tok in enumerate(draft_rows(got)):
+        assert tok in cand[p]
