@@ -32,8 +32,8 @@ def _readout_case(seed, N, B, r, V, *, zero_head=False):
     lat = _dyadic(rng, (rows, r), -4, 4, 16)
     w2 = np.zeros((V, r), np.float32) if zero_head else _dyadic(rng, (V, r), -4, 4, 16)
     base = _dyadic(rng, (rows, V), -8, 8, 4)
-    for p in range(0, rows, 3):  # exact top ties between a high and a low id
-        hi, lo = V - 1 - p % 7, p % 5
+    for p in range(0, rows, 3):  # exact top ties between a high and a low id (distinct pairs)
+        hi, lo = V - 1 - p, p
         w2[lo] = w2[hi]
         base[p, hi] = base[p, lo] = 31.75
     return lat, w2, base
