@@ -20,7 +20,9 @@
  *     itself (host memory, read during the call only) and out-parameters named *_bytes (host).
  *   - bf16 tensors are passed as their 16-bit patterns (xpress_bf16). Token ids are int64.
  *   - Layouts are dense row-major with the shapes given, except base logits, which take a row
- *     stride (elements) base_ld >= V.
+ *     stride (elements) base_ld >= V, a multiple of 8; the base buffer must be readable for
+ *     rows * base_ld elements (the last row too is padded to the full stride): kernels read whole
+ *     8-element groups up to the padded row end and ignore the ids >= V.
  *   - Rows of the readout: row p = n*(B-1) + (b-1) is slot b (1..B-1) of block n.
  *   - Every call only enqueues work on `stream` (NULL = the null stream) and returns; none
  *     allocates, frees or synchronises, so a sequence of calls can be captured into a HIP graph.

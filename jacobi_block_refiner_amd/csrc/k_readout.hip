@@ -35,128 +35,191 @@ int env_int(const char* name, int dflt) {
 //   A (32 x 16): lane l holds row l%32, k = 8*(l/32) + e, e = 0..7
 //   B (16 x 32): lane l holds col l%32, the same k
 //   D (32 x 32): lane l, accumulator v holds row 8*(v/4) + 4*(l/32) + v%4, col l%32
-// Here A = w2 rows (vocabulary ids), B = lat rows (readout rows): D[vocab][row].
+// Here A = w2 rows (vocabulary ids), B = lat rows (readout rows): D[vocab][row]. Lane l thus
+// owns readout row l%32 and, in each group g of 8 ids, the 4 consecutive ids 8g + 4*(l/32) + 0..3.
+//
+// Work decomposition: a unit is (vocabulary tile of TV = 32*NW ids, 32-row tile). The units are
+// numbered vocabulary-tile-major and the persistent grid splits that sequence into equal
+// contiguous ranges, so every workgroup scores the same number of row tiles (to within one) and
+// reloads its w2 fragment (kept in registers) only when its range crosses into the next
+// vocabulary tile.
+//
+// Data path per unit: the lat tile [32 rows x r] (from L2) and the base tile [32 rows x TV] (from
+// HBM) are fetched with fully coalesced 16-byte loads into registers one unit ahead, written to
+// a double-buffered, padded LDS stage, and read from there by the MFMA (lat) and by the epilogue
+// (base, in the accumulator layout). Coalesced 16-byte loads stream at full HBM rate; reading
+// base directly in the accumulator layout (8 bytes per lane, 32 rows per instruction) does not.
+//
+// Iteration t (one barrier): MFMA + epilogue on stage t%2; write the registers (unit t+1) into
+// stage (t+1)%2; issue the loads of unit t+2. Each wave's per-row winners go to a double-buffered
+// LDS slot; wave 0 reduces them one unit later and stores the partials. Loads sit outside
+// data-dependent branches (rows past the end are clamped to the last row, ids past V to the
+// padded row end, which the base stride guarantees is readable), so the compiler's wait counts
+// keep them in flight across the iteration.
 template <int R, int NW>
 __global__ __launch_bounds__(NW * 64) void readout_partial_kernel(
     const uint16_t* __restrict__ lat, const uint16_t* __restrict__ w2,
-    const uint16_t* __restrict__ base, int64_t ld, int rows, int V, int ntiles, int row_groups,
+    const uint16_t* __restrict__ base, int64_t ld, int rows, int V, int ntiles,
     uint2* __restrict__ part, const int32_t* __restrict__ flags, int pass) {
   if (pass_skipped(flags, pass)) return;
-  constexpr int KS = R / 16;       // MFMA k-steps
-  constexpr int RQ = R / 8;        // uint4 (8 x bf16) per lat / w2 row
-  constexpr int LDQ = RQ + 1;      // padded LDS row stride in uint4
-  constexpr int TV = 32 * NW;      // vocabulary ids per workgroup
+  constexpr int KS = R / 16;
+  constexpr int RQ = R / 8;           // 16-byte chunks per lat row
+  constexpr int LDQ = RQ + 1;         // padded lat row stride (chunks)
+  constexpr int TV = 32 * NW;
+  constexpr int BQ = TV / 8;          // 16-byte chunks per base tile row
+  constexpr int BLD = BQ + 1;         // padded base row stride (chunks)
+  constexpr int NT = NW * 64;
+  constexpr int LQ = (32 * RQ + NT - 1) / NT;  // lat chunks per thread
+  constexpr int BQT = (32 * BQ + NT - 1) / NT; // base chunks per thread
 
-  __shared__ uint4 s_lat[32 * LDQ];
-  __shared__ float s_rv[NW][32];
-  __shared__ int s_ri[NW][32];
+  __shared__ uint4 s_lat[2][32 * LDQ];
+  __shared__ uint4 s_base[2][32 * BLD];
+  __shared__ float s_rv[2][NW][32];
+  __shared__ int s_ri[2][NW][32];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  // XCD-aware mapping: workgroup ids are dealt round-robin to the 8 XCDs, so the row groups of
-  // one vocabulary tile get ids 8 apart and share an XCD (and its L2 copy of the w2 tile).
-  const int wg = blockIdx.x;
-  const int grp = wg / (8 * row_groups);
-  const int within = wg % (8 * row_groups);
-  const int tile = grp * 8 + (within & 7);
-  const int rg = within >> 3;
-  if (tile >= ntiles) return;
-
-  const int v0 = tile * TV + wave * 32;
-  const bool wave_live = v0 < V;
-
-  bf16x8 a[KS];
-  {
-    const int v = v0 + l32;
-    if (v < V) {
-      const uint4* src = reinterpret_cast<const uint4*>(w2 + (int64_t)v * R) + half;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) a[s] = as_bf16x8(ld_nt16(src + 2 * s));
-    } else {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) a[s] = as_bf16x8(make_uint4(0, 0, 0, 0));
-    }
-  }
-  const bool tail_tile = (tile + 1) * TV > V;
   const int n_rt = (rows + 31) / 32;
+  const int64_t units = (int64_t)ntiles * n_rt;
+  const int u0 = (int)(units * blockIdx.x / gridDim.x);
+  const int u1 = (int)(units * (blockIdx.x + 1) / gridDim.x);
+  const int T = u1 - u0;
+  if (T <= 0) return;
+  const int last_chunk = (V + 7) / 8 - 1;  // last 16-byte chunk inside the padded row
 
-  for (int rt = rg; rt < n_rt; rt += row_groups) {
-    const int r0 = rt * 32;
-    for (int q = threadIdx.x; q < 32 * RQ; q += NW * 64) {
-      const int rr = q / RQ, cc = q % RQ;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (r0 + rr < rows) val = reinterpret_cast<const uint4*>(lat + (int64_t)(r0 + rr) * R)[cc];
-      s_lat[rr * LDQ + cc] = val;
+  // Prefetch cursor (unit whose data goes into the staging registers next), kept as
+  // (vocabulary tile, row tile) and advanced without divisions; it stops at the last unit.
+  int pf_tile = u0 / n_rt, pf_rt = u0 % n_rt, pf_left = T;
+  u32x4 lreg[LQ], breg[BQT];
+  auto load_next = [&]() __attribute__((always_inline)) {
+    const int r0 = pf_rt * 32;
+    const int c0 = pf_tile * BQ;
+#pragma unroll
+    for (int q = 0; q < LQ; ++q) {
+      const int idx = min(tid + q * NT, 32 * RQ - 1);
+      const int r = min(r0 + idx / RQ, rows - 1);
+      lreg[q] = reinterpret_cast<const u32x4*>(lat + (int64_t)r * R)[idx % RQ];
     }
-    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < BQT; ++q) {
+      const int idx = min(tid + q * NT, 32 * BQ - 1);
+      const int r = min(r0 + idx / BQ, rows - 1);
+      const int c = min(c0 + idx % BQ, last_chunk);
+      breg[q] = reinterpret_cast<const u32x4*>(base + (int64_t)r * ld)[c];
+    }
+    if (pf_left > 1) {
+      --pf_left;
+      if (++pf_rt == n_rt) { pf_rt = 0; ++pf_tile; }
+    }
+  };
+  auto store_staged = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < LQ; ++q) {
+      const int idx = tid + q * NT;
+      if ((32 * RQ) % NT == 0 || idx < 32 * RQ)
+        s_lat[buf][(idx / RQ) * LDQ + idx % RQ] =
+            make_uint4(lreg[q].x, lreg[q].y, lreg[q].z, lreg[q].w);
+    }
+#pragma unroll
+    for (int q = 0; q < BQT; ++q) {
+      const int idx = tid + q * NT;
+      if ((32 * BQ) % NT == 0 || idx < 32 * BQ)
+        s_base[buf][(idx / BQ) * BLD + idx % BQ] =
+            make_uint4(breg[q].x, breg[q].y, breg[q].z, breg[q].w);
+    }
+  };
+  // wave 0: winners of the unit held in s_rv/s_ri[b] across the waves -> global partials.
+  // All 64 lanes run it (lanes 32..63 repeat lanes 0..31 and store the same values).
+  auto flush = [&](int b, int tile, int rt) __attribute__((always_inline)) {
+    float v = s_rv[b][0][l32];
+    int i = s_ri[b][0][l32];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) argmax_merge(v, i, s_rv[b][w][l32], s_ri[b][w][l32]);
+    const int prow = rt * 32 + l32;
+    if (prow < rows) part[(int64_t)prow * ntiles + tile] = make_uint2(__float_as_uint(v), (unsigned)i);
+  };
 
-    float bv = -INFINITY;
-    int bi = INT_MAX;
-    const int row = r0 + l32;
-    if (wave_live) {
+  load_next();
+  store_staged(0);
+  load_next();
+  __syncthreads();
+
+  int t = 0;
+  int tile = u0 / n_rt, rt = u0 % n_rt;
+  int prev_tile = 0, prev_rt = 0;
+  bf16x8 a[KS];
+  while (t < T) {
+    // segment: the units of this workgroup's range that share vocabulary tile `tile`
+    const int seg_end = min(T, t + (n_rt - rt));
+    {
+      const int v = min(tile * TV + wave * 32 + l32, V - 1);
+      const u32x4* src = reinterpret_cast<const u32x4*>(w2 + (int64_t)v * R) + half;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) a[s] = __builtin_bit_cast(bf16x8, src[2 * s]);
+    }
+    const int vl = tile * TV + wave * 32 + 4 * half;
+    const bool full_tile = (tile + 1) * TV <= V;
+    for (; t < seg_end; ++t, ++rt) {
+      const int buf = t & 1;
       f32x16 acc = {};
+      const uint4* sl = s_lat[buf];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 b = as_bf16x8(s_lat[l32 * LDQ + 2 * s + half]);
-        acc = mfma32x32x16(a[s], b, acc);
+      for (int s = 0; s < KS; ++s)
+        acc = mfma32x32x16(a[s], as_bf16x8(sl[l32 * LDQ + 2 * s + half]), acc);
+      // this lane's base values: row l32, ids 32*wave + 8g + 4*half + 0..3 of the tile
+      const uint2* sb = reinterpret_cast<const uint2*>(s_base[buf] + l32 * BLD + wave * 4);
+      float lg[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint2 q = sb[2 * g + half];
+        lg[4 * g + 0] = acc[4 * g + 0] + bf16_lo(q.x);
+        lg[4 * g + 1] = acc[4 * g + 1] + bf16_hi(q.x);
+        lg[4 * g + 2] = acc[4 * g + 2] + bf16_lo(q.y);
+        lg[4 * g + 3] = acc[4 * g + 3] + bf16_hi(q.y);
       }
-      if (row < rows) {
-        const uint16_t* brow = base + (int64_t)row * ld;
-        const int vl = v0 + 4 * half;  // this lane's first id in each group of 8
-        if (!tail_tile) {
-          uint2 q[4];
+      float bv = lg[0];
+      int bl = 0;  // local index 4g + k of this lane's best id
+      if (full_tile) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
-            q[g] = ld_nt8(brow + vl + 8 * g);
+        for (int e = 1; e < 16; ++e) {
+          const bool gt = lg[e] > bv;
+          bv = gt ? lg[e] : bv;
+          bl = gt ? e : bl;
+        }
+      } else {  // the tile straddling V: ids >= V never win
+        bv = (vl < V) ? lg[0] : -INFINITY;
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const float l0 = acc[4 * g + 0] + bf16_lo(q[g].x);
-            const float l1 = acc[4 * g + 1] + bf16_hi(q[g].x);
-            const float l2 = acc[4 * g + 2] + bf16_lo(q[g].y);
-            const float l3 = acc[4 * g + 3] + bf16_hi(q[g].y);
-            const int id = vl + 8 * g;
-            if (l0 > bv) { bv = l0; bi = id; }
-            if (l1 > bv) { bv = l1; bi = id + 1; }
-            if (l2 > bv) { bv = l2; bi = id + 2; }
-            if (l3 > bv) { bv = l3; bi = id + 3; }
-          }
-        } else {
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int id = vl + 8 * g + e;
-              if (id < V) {
-                const float l = acc[4 * g + e] + bf16_to_f32(brow[id]);
-                if (l > bv) { bv = l; bi = id; }
-              }
-            }
+        for (int e = 1; e < 16; ++e) {
+          const bool gt = (vl + 8 * (e >> 2) + (e & 3) < V) & (lg[e] > bv);
+          bv = gt ? lg[e] : bv;
+          bl = gt ? e : bl;
         }
       }
+      int bi = vl + 8 * (bl >> 2) + (bl & 3);
+      {
+        const float ov = __shfl_xor(bv, 32);
+        const int oi = __shfl_xor(bi, 32);
+        argmax_merge(bv, bi, ov, oi);
+      }
+      if (lane < 32) {
+        s_rv[buf][wave][lane] = bv;
+        s_ri[buf][wave][lane] = bi;
+      }
+      if (t > 0 && wave == 0) flush(buf ^ 1, prev_tile, prev_rt);
+      store_staged(buf ^ 1);
+      load_next();
+      prev_tile = tile;
+      prev_rt = rt;
+      __syncthreads();
     }
-    // lanes l and l^32 hold the two interleaved halves of the same row
-    {
-      const float ov = __shfl_xor(bv, 32);
-      const int oi = __shfl_xor(bi, 32);
-      argmax_merge(bv, bi, ov, oi);
-    }
-    if (lane < 32) {
-      s_rv[wave][lane] = bv;
-      s_ri[wave][lane] = bi;
-    }
-    __syncthreads();
-    if (threadIdx.x < 32) {
-      float v = s_rv[0][threadIdx.x];
-      int i = s_ri[0][threadIdx.x];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) argmax_merge(v, i, s_rv[w][threadIdx.x], s_ri[w][threadIdx.x]);
-      const int prow = r0 + threadIdx.x;
-      if (prow < rows) part[(int64_t)prow * ntiles + tile] = make_uint2(__float_as_uint(v), (unsigned)i);
-    }
+    ++tile;
+    rt = 0;
   }
+  if (wave == 0) flush((T - 1) & 1, prev_tile, prev_rt);
 }
 
 // One workgroup per readout row: reduce the row's tile partials, write blk in place, flag changes.
@@ -201,16 +264,27 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const uint2* __restr
   }
 }
 
+int device_cus() {
+  static int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    return n;
+  }();
+  return cus;
+}
+
 template <int R, int NW>
 hipError_t launch_partial_t(const uint16_t* lat, const uint16_t* w2, const uint16_t* base,
                             int64_t ld, int rows, int64_t V, uint2* part, const int32_t* flags,
                             int pass, hipStream_t s) {
   const int ntiles = readout_tiles(V);
-  const int rg = readout_row_groups(rows, V);
-  const int groups = (ntiles + 7) / 8;
-  dim3 grid(groups * 8 * rg), block(NW * 64);
-  hipLaunchKernelGGL((readout_partial_kernel<R, NW>), grid, block, 0, s, lat, w2, base, ld, rows,
-                     (int)V, ntiles, rg, part, flags, pass);
+  const int64_t units = (int64_t)ntiles * ((rows + 31) / 32);
+  int64_t grid = (int64_t)device_cus() * readout_wgs_per_cu();
+  if (grid > units) grid = units;
+  hipLaunchKernelGGL((readout_partial_kernel<R, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s,
+                     lat, w2, base, ld, rows, (int)V, ntiles, part, flags, pass);
   return hipGetLastError();
 }
 
@@ -241,12 +315,9 @@ int readout_tiles(int64_t V) {
   return (int)((V + tv - 1) / tv);
 }
 
-int readout_row_groups(int rows, int64_t V) {
-  const int n_rt = (rows + 31) / 32;
-  const int forced = env_int("XPRESS_READOUT_ROW_GROUPS", 0);
-  int rg = forced > 0 ? forced : (1024 + readout_tiles(V) - 1) / readout_tiles(V);
-  if (rg > n_rt) rg = n_rt;
-  return rg < 1 ? 1 : rg;
+int readout_wgs_per_cu() {
+  static const int n = env_int("XPRESS_READOUT_WGS_PER_CU", 1);
+  return n;
 }
 
 hipError_t launch_readout_partial(const uint16_t* lat, const uint16_t* w2, const uint16_t* base,

@@ -7,11 +7,11 @@
 
 namespace xpress {
 
-// Readout tiling: a workgroup scores TV = 32 * readout_waves() vocabulary ids against a group of
-// 32-row tiles.
+// Readout tiling: a workgroup scores TV = 32 * readout_waves() vocabulary ids per unit against a
+// 32-row tile; a persistent grid of readout_wgs_per_cu() workgroups per CU splits the units.
 int readout_waves();
 int readout_tiles(int64_t V);
-int readout_row_groups(int rows, int64_t V);
+int readout_wgs_per_cu();
 
 // K1a: hdg[m, j] = sum_k h[m, k] * Wcat[j, k], Wcat = [down_h; down_g], m < NB, j < 2r (fp32 out).
 hipError_t launch_hidden_gemm(const uint16_t* h, const uint16_t* down_h, const uint16_t* down_g,

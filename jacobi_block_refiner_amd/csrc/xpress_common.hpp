@@ -30,10 +30,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // (value, index) arg-max combine: larger value wins; equal values keep the lower index.
 // -0.0 and +0.0 compare equal, so they tie and the lower index wins.
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {
-  if (ov > v || (ov == v && oi < i)) {
-    v = ov;
-    i = oi;
-  }
+  const bool take = (ov > v) | ((ov == v) & (oi < i));  // bitwise: no branches
+  v = take ? ov : v;
+  i = take ? oi : i;
 }
 
 __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
