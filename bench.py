@@ -122,7 +122,7 @@ def main() -> int:
     xpress.hidden_cache(w, h, xh, ws)
     lat = torch.empty(wl.N, wl.B - 1, wl.r, dtype=torch.bfloat16, device=dev)
     blk2 = blk.clone()
-    xpress.latent_pass(w, blk2, am1, xh, lat)
+    xpress.latent_pass(w, blk2, am1, xh, lat, ws)
     ntiles = xpress.readout_tiles(wl.V)
     part = torch.empty(rows, ntiles, 2, dtype=torch.int32, device=dev)
 
@@ -139,7 +139,7 @@ def main() -> int:
     reps = args.kernel_reps
     fn_readout = lambda: xpress.readout_partials(w, lat, base, part)
     fn_reduce = lambda: xpress.argmax_reduce(part, blk2)
-    fn_latent = lambda: xpress.latent_pass(w, blk2, am1, xh, lat)
+    fn_latent = lambda: xpress.latent_pass(w, blk2, am1, xh, lat, ws)
     for f in (fn_readout, fn_reduce, fn_latent):
         f()
     torch.cuda.synchronize()
@@ -152,7 +152,7 @@ def main() -> int:
 
     def loop():
         for _ in range(K):
-            xpress.latent_pass(w, blk2, am1, xh, lat)
+            xpress.latent_pass(w, blk2, am1, xh, lat, ws)
             xpress.readout_argmax(w, lat, base, blk2, ws)
 
     loop()

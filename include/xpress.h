@@ -111,12 +111,14 @@ xpress_status xpress_initial_block(const xpress_bf16* base, int64_t base_ld,
                                    int64_t* blk, xpress_stream stream);
 
 /* Latent stage of one pass (kernels page, _xpress_latent_kernel; qwen3_xpress page,
- * _refine_latent): reads blk, never writes it.
+ * _refine_latent): reads blk, never writes it. Token ids outside [0, V) contribute a zero
+ * embedding.
  * blk: [N, B]; am1: [N] (token before each anchor); xh: [N, B, r] fp32 from xpress_hidden_cache;
- * lat: [N, B-1, r] bf16 (written; row n*(B-1)+b-1 is slot b). */
+ * lat: [N, B-1, r] bf16 (written; row n*(B-1)+b-1 is slot b). ws: scratch of ws_bytes bytes
+ * (a workspace sized by xpress_workspace_size for at least N blocks is enough). */
 xpress_status xpress_latent_pass(const xpress_weights* w, const int64_t* blk, const int64_t* am1,
-                                 const float* xh, int32_t N, xpress_bf16* lat,
-                                 xpress_stream stream);
+                                 const float* xh, int32_t N, xpress_bf16* lat, void* ws,
+                                 size_t ws_bytes, xpress_stream stream);
 
 /* Full-vocabulary readout and argmax (kernels page, fused_add_argmax_to_blk; qwen3_xpress page,
  * refine_bias): blk[n, b] = argmax_v (base[p, v] + lat[p] . w2[v]) for p = n*(B-1)+b-1, written in

@@ -22,11 +22,12 @@ hipError_t launch_hidden_project(const float* hdg, const uint16_t* in_proj, int 
 // K2: blk[n, 0] = anchor[n]; blk[n, b] = argmax_v base[n*(B-1)+b-1, v].
 hipError_t launch_initial_block(const uint16_t* base, int64_t ld, const int64_t* anchor, int N,
                                 int B, int64_t V, int64_t* blk, hipStream_t s);
-// K4: fused latent stage of one pass.
+// K4: latent stage of one pass (three kernels); scratch holds u (fp32 and bf16) and s (bf16).
+size_t latent_scratch_bytes(int N, int r, int M);
 hipError_t launch_latent(const int64_t* blk, const int64_t* am1, const float* xh,
                          const uint16_t* w1, const uint16_t* in_proj, const uint16_t* mix_L,
                          const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
-                         int N, int B, int r, int M, int64_t V, uint16_t* lat,
+                         int N, int B, int r, int M, int64_t V, uint16_t* lat, void* scratch,
                          const int32_t* flags, int pass, hipStream_t s);
 // K5: per (vocab tile, row) partial argmax of base + lat . w2^T; part: [rows, ntiles].
 hipError_t launch_readout_partial(const uint16_t* lat, const uint16_t* w2, const uint16_t* base,

@@ -93,8 +93,12 @@ xpress_status check_base(const xpress_bf16* base, int64_t ld, int64_t V) {
 
 // Workspace regions of a call with N blocks.
 struct Layout {
-  size_t hdg = 0, xh = 0, lat = 0, part = 0, flags = 0, cand = 0, base_c = 0, w2c = 0, total = 0;
+  size_t hdg = 0, xh = 0, lat = 0, lscr = 0, part = 0, flags = 0, cand = 0, base_c = 0, w2c = 0,
+         total = 0;
 };
+
+// Latent scratch for the widest supported MLP (M = 1024), so the size does not depend on M.
+constexpr int kMaxM = 1024;
 
 Layout step_layout(int N, int B, int r, int64_t V, int C, int K) {
   Layout L;
@@ -109,6 +113,7 @@ Layout step_layout(int N, int B, int r, int64_t V, int C, int K) {
   L.hdg = take((size_t)N * B * 2 * r * sizeof(float));
   L.xh = take((size_t)N * B * r * sizeof(float));
   L.lat = take(rows * r * 2);
+  L.lscr = take(xpress::latent_scratch_bytes(N, r, kMaxM));
   L.part = take(C > 0 ? 0 : rows * (size_t)xpress::readout_tiles(V) * sizeof(uint2));
   L.flags = take((size_t)(K + 1) * sizeof(int32_t));
   L.cand = take(rows * c * sizeof(int64_t));
@@ -187,8 +192,8 @@ xpress_status xpress_initial_block(const xpress_bf16* base, int64_t base_ld, con
 }
 
 xpress_status xpress_latent_pass(const xpress_weights* w, const int64_t* blk, const int64_t* am1,
-                                 const float* xh, int32_t N, xpress_bf16* lat,
-                                 xpress_stream stream) {
+                                 const float* xh, int32_t N, xpress_bf16* lat, void* ws,
+                                 size_t ws_bytes, xpress_stream stream) {
   xpress_status st = check_weights(w, false, true, false);
   if (st != XPRESS_OK) return st;
   if (N < 0) return fail(XPRESS_ERR_ARG, "N=%d < 0", N);
@@ -197,8 +202,12 @@ xpress_status xpress_latent_pass(const xpress_weights* w, const int64_t* blk, co
   XP_PTR(am1);
   XP_PTR(xh);
   XP_PTR(lat);
+  XP_PTR(ws);
+  const size_t need = xpress::latent_scratch_bytes(N, w->r, w->M);
+  if (ws_bytes < need)
+    return fail(XPRESS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed for N=%d", ws_bytes, need, N);
   XP_TRY(xpress::launch_latent(blk, am1, xh, w->w1, w->in_proj, w->mix_L, w->w_gate, w->w_up,
-                               w->w_down, N, w->B, w->r, w->M, w->V, lat, nullptr, 0,
+                               w->w_down, N, w->B, w->r, w->M, w->V, lat, ws, nullptr, 0,
                                reinterpret_cast<hipStream_t>(stream)),
          "latent");
   return XPRESS_OK;
@@ -341,6 +350,7 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
   float* hdg = at<float>(ws, L.hdg);
   float* xh = at<float>(ws, L.xh);
   xpress_bf16* lat = at<xpress_bf16>(ws, L.lat);
+  void* lscr = at<char>(ws, L.lscr);
   XP_TRY(xpress::launch_hidden_gemm(h, w->down_h, w->down_g, N * B, w->H, r, hdg, s), "hidden gemm");
   XP_TRY(xpress::launch_hidden_project(hdg, w->in_proj, N, B, r, xh, s), "hidden project");
   if (flags & XPRESS_INIT_FROM_BASE)
@@ -362,7 +372,7 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
   const int ntiles = xpress::readout_tiles(V);
   for (int p = 0; p < K; ++p) {
     XP_TRY(xpress::launch_latent(blk, am1, xh, w->w1, w->in_proj, w->mix_L, w->w_gate, w->w_up,
-                                 w->w_down, N, B, r, w->M, V, lat, pf, p, s),
+                                 w->w_down, N, B, r, w->M, V, lat, lscr, pf, p, s),
            "latent");
     if (c > 0) {
       XP_TRY(xpress::launch_topc_readout(lat, w2c, base_c, cand, rows, B, r, c, blk, nullptr, pf, p, s),

@@ -62,7 +62,7 @@ def lib() -> ctypes.CDLL:
             "xpress_fold_mixer": [P, i32, i32, P, P],
             "xpress_hidden_cache": [W, P, i32, P, P, sz, P],
             "xpress_initial_block": [P, i64, P, i32, i32, i64, P, P],
-            "xpress_latent_pass": [W, P, P, P, i32, P, P],
+            "xpress_latent_pass": [W, P, P, P, i32, P, P, sz, P],
             "xpress_readout_argmax": [W, P, P, i64, i32, P, P, P, sz, P],
             "xpress_readout_tiles": [i64, ctypes.POINTER(i32)],
             "xpress_readout_partials": [W, P, P, i64, i32, P, P],
@@ -173,11 +173,12 @@ def initial_block(base: torch.Tensor, anchor: torch.Tensor, blk: torch.Tensor) -
     return blk
 
 
-def latent_pass(w: Weights, blk, am1, xh, lat) -> torch.Tensor:
+def latent_pass(w: Weights, blk, am1, xh, lat, ws: torch.Tensor) -> torch.Tensor:
     s = w.struct()
     N = blk.shape[0]
     _check(lib().xpress_latent_pass(ctypes.byref(s), _ptr(blk), _ptr(am1), _ptr(xh), N,
-                                    _ptr(lat), _stream()))
+                                    _ptr(lat), _ptr(ws), ws.numel() * ws.element_size(),
+                                    _stream()))
     return lat
 
 

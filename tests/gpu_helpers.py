@@ -67,7 +67,8 @@ class Dev:
         """Latent + readout + argmax from the block blk_np; returns (new blk, lat)."""
         blk = upload.tokens(blk_np, self.device)
         lat = torch.empty(self.N, self.B - 1, self.r, dtype=torch.bfloat16, device=self.device)
-        xpress.latent_pass(self.w, blk, self.am1, xh, lat)
+        ws = ws if ws is not None else self.ws()
+        xpress.latent_pass(self.w, blk, self.am1, xh, lat, ws)
         if cand is None:
             xpress.readout_argmax(self.w, lat, self.base, blk, ws if ws is not None else self.ws())
         else:

@@ -40,7 +40,7 @@ def test_bad_shapes_are_rejected(B, r, V):
 
 def test_null_weights_and_pointers_are_rejected():
     L = xpress.lib()
-    st = L.xpress_latent_pass(None, None, None, None, 4, None, None)
+    st = L.xpress_latent_pass(None, None, None, None, 4, None, None, 0, None)
     assert st == xpress.ERR_ARG and b"NULL" in L.xpress_last_error()
     w = xpress._Weights(B=16, r=256, H=4096, M=512, V=151936)
     st = L.xpress_jacobi_step(ctypes.byref(w), None, None, 151936, None, None, 4, 15, 0, 1, None,
@@ -56,7 +56,7 @@ def test_n_zero_is_a_noop_and_unknown_flags_are_rejected():
     w = xpress._Weights(B=16, r=256, H=4096, M=512, V=151936, w1=fake, down_h=fake,
                         down_g=fake, in_proj=fake, mix_L=fake, w_gate=fake, w_up=fake,
                         w_down=fake, w2=fake)
-    assert L.xpress_latent_pass(ctypes.byref(w), fake, fake, fake, 0, fake, None) == xpress.OK
+    assert L.xpress_latent_pass(ctypes.byref(w), fake, fake, fake, 0, fake, fake, 0, None) == xpress.OK
     st = L.xpress_jacobi_step(ctypes.byref(w), fake, fake, 151936, fake, fake, 4, 15, 0, 0x10,
                               fake, None, fake, 1 << 30, None)
     assert st == xpress.ERR_ARG and b"flag" in L.xpress_last_error()

@@ -97,7 +97,7 @@ def test_step_reaches_fixed_point_and_matches_oracle(wl_id, n_sample):
     lat = torch.empty(wl.N, wl.B - 1, wl.r, dtype=torch.bfloat16, device="cuda")
     xh = d.xh()
     after = blk.clone()
-    xpress.latent_pass(d.w, after, d.am1, xh, lat)
+    xpress.latent_pass(d.w, after, d.am1, xh, lat, ws)
     xpress.readout_argmax(d.w, lat, d.base, after, ws, changed)
     torch.cuda.synchronize()
     assert int(changed.item()) == 0 and torch.equal(after, blk)
@@ -169,7 +169,7 @@ def test_topc_full_size():
     after = blk.clone()
     changed = torch.zeros(1, dtype=torch.int32, device="cuda")
     lat2 = torch.empty(wl.N, wl.B - 1, wl.r, dtype=torch.bfloat16, device="cuda")
-    xpress.latent_pass(d.w, after, d.am1, xh, lat2)
+    xpress.latent_pass(d.w, after, d.am1, xh, lat2, ws)
     xpress.readout_argmax_topc(lat2, w2c, base_c, cand, after, changed)
     torch.cuda.synchronize()
     assert int(changed.item()) == 0 and torch.equal(after, blk)

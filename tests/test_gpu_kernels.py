@@ -154,7 +154,7 @@ def test_latent_parity(wl_id, N, over):
     inp, xh = _latent_case(wl_id, N, **over)
     d = Dev(inp)
     lat = torch.empty(N, inp.wl.B - 1, inp.wl.r, dtype=torch.bfloat16, device="cuda")
-    xpress.latent_pass(d.w, upload.tokens(inp.blk), d.am1, torch.from_numpy(xh).cuda(), lat)
+    xpress.latent_pass(d.w, upload.tokens(inp.blk), d.am1, torch.from_numpy(xh).cuda(), lat, d.ws())
     torch.cuda.synchronize()
     want = O.latent(inp, oracle_mixer(inp), xh.astype(np.float64), inp.blk, inp.am1)
     err = lat_rel_err(lat_to_f64(lat), want)
@@ -168,12 +168,13 @@ def test_latent_causality_bit_invariance():
     xh_t = torch.from_numpy(xh).cuda()
     B = inp.wl.B
     lat0 = torch.empty(3, B - 1, inp.wl.r, dtype=torch.bfloat16, device="cuda")
-    xpress.latent_pass(d.w, upload.tokens(inp.blk), d.am1, xh_t, lat0)
+    ws = d.ws()
+    xpress.latent_pass(d.w, upload.tokens(inp.blk), d.am1, xh_t, lat0, ws)
     for b in (1, 5, 14):
         blk2 = inp.blk.copy()
         blk2[:, b:] = (blk2[:, b:] + 777) % inp.wl.V
         lat1 = torch.empty_like(lat0)
-        xpress.latent_pass(d.w, upload.tokens(blk2), d.am1, xh_t, lat1)
+        xpress.latent_pass(d.w, upload.tokens(blk2), d.am1, xh_t, lat1, ws)
         torch.cuda.synchronize()
         a = lat0.view(torch.int16).cpu().numpy()
         c = lat1.view(torch.int16).cpu().numpy()
@@ -188,7 +189,7 @@ def test_latent_repeat_is_bit_identical():
     outs = []
     for _ in range(3):
         lat = torch.empty(4, inp.wl.B - 1, inp.wl.r, dtype=torch.bfloat16, device="cuda")
-        xpress.latent_pass(d.w, upload.tokens(inp.blk), d.am1, xh_t, lat)
+        xpress.latent_pass(d.w, upload.tokens(inp.blk), d.am1, xh_t, lat, d.ws())
         outs.append(lat.view(torch.int16).cpu().numpy())
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
