@@ -6,8 +6,9 @@
 //
 // The mean commutes with the linear map down_g, so down_g . mean_b h = mean_b (down_g . h[b]).
 // That keeps both projections on exact bf16 operands: K1a runs one bf16 MFMA GEMM
-// hdg = h . [down_h; down_g]^T over all N*B slot rows (fp32 accumulate, fp32 out), and K1b takes
-// the slot mean of the down_g half and applies in_proj's hidden half in fp32.
+// hdg = h . [down_h; down_g]^T over all N*B slot rows (fp32 accumulate), split over K into
+// partial sums when there are few output tiles; K1b adds the partials in a fixed order, takes the
+// slot mean of the down_g half and applies in_proj's hidden half in fp32.
 #include "launch.hpp"
 #include "xpress_common.hpp"
 
@@ -20,31 +21,52 @@ constexpr int kTN = 64;  // output columns per workgroup
 constexpr int kTK = 64;  // k chunk
 constexpr int kLQ = kTK / 8 + 1;  // padded LDS row stride (uint4)
 
+// Split-K partial products: part[ks, m, j] = sum_{k in slice ks} h[m, k] * Wcat[j, k].
 // 4 waves as a 2 x 2 grid of 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16, layout as in the
-// readout kernel: D[row = 8*(v/4) + 4*(l/32) + v%4][col = l%32]).
+// readout kernel: D[row = 8*(v/4) + 4*(l/32) + v%4][col = l%32]). The next k chunk is loaded into
+// registers while the current one is multiplied out of LDS.
 __global__ __launch_bounds__(256) void hidden_gemm_kernel(const uint16_t* __restrict__ h,
                                                           const uint16_t* __restrict__ down_h,
                                                           const uint16_t* __restrict__ down_g,
-                                                          int NB, int H, int r,
-                                                          float* __restrict__ hdg) {
+                                                          int NB, int H, int r, int kslice,
+                                                          float* __restrict__ part) {
   __shared__ uint4 s_a[kTM * kLQ];
   __shared__ uint4 s_b[kTN * kLQ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int m0 = blockIdx.x * kTM, n0 = blockIdx.y * kTN;
+  const int ks = blockIdx.z;
+  const int kbeg = ks * kslice, kend = min(H, kbeg + kslice);
   const int l32 = lane & 31, half = lane >> 5;
+  // this thread's two 16-byte chunks of each k chunk: rows rr0, rr0 + 32 at column cc
+  const int rr0 = tid / (kTK / 8), cc = tid % (kTK / 8);
+  const uint16_t* arow[2];
+  const uint16_t* brow[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int rr = rr0 + 32 * q;
+    arow[q] = h + (int64_t)min(m0 + rr, NB - 1) * H;
+    const int j = n0 + rr;  // output column = row of [down_h; down_g]
+    brow[q] = (j < r) ? down_h + (int64_t)j * H : down_g + (int64_t)(j - r) * H;
+  }
+  uint4 ra[2], rb[2];
+  auto load = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      ra[q] = reinterpret_cast<const uint4*>(arow[q] + k0)[cc];
+      rb[q] = reinterpret_cast<const uint4*>(brow[q] + k0)[cc];
+    }
+  };
   f32x16 acc = {};
-  for (int k0 = 0; k0 < H; k0 += kTK) {
-    for (int q = tid; q < kTM * (kTK / 8); q += 256) {
-      const int rr = q / (kTK / 8), cc = q % (kTK / 8);
-      uint4 va = make_uint4(0, 0, 0, 0);
-      if (m0 + rr < NB) va = reinterpret_cast<const uint4*>(h + (int64_t)(m0 + rr) * H + k0)[cc];
-      s_a[rr * kLQ + cc] = va;
-      const int j = n0 + rr;  // output column = row of [down_h; down_g]
-      const uint16_t* wrow = (j < r) ? down_h + (int64_t)j * H : down_g + (int64_t)(j - r) * H;
-      s_b[rr * kLQ + cc] = reinterpret_cast<const uint4*>(wrow + k0)[cc];
+  load(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += kTK) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      s_a[(rr0 + 32 * q) * kLQ + cc] = ra[q];
+      s_b[(rr0 + 32 * q) * kLQ + cc] = rb[q];
     }
     __syncthreads();
+    if (k0 + kTK < kend) load(k0 + kTK);
 #pragma unroll
     for (int s = 0; s < kTK / 16; ++s) {
       const bf16x8 a = as_bf16x8(s_a[(32 * wm + l32) * kLQ + 2 * s + half]);
@@ -54,75 +76,151 @@ __global__ __launch_bounds__(256) void hidden_gemm_kernel(const uint16_t* __rest
     __syncthreads();
   }
   const int col = n0 + 32 * wn + l32;
+  float* out = part + (int64_t)ks * NB * (2 * r);
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int row = m0 + 32 * wm + 8 * (v / 4) + 4 * half + (v % 4);
-    if (row < NB) hdg[(int64_t)row * (2 * r) + col] = acc[v];
+    if (row < NB) out[(int64_t)row * (2 * r) + col] = acc[v];
   }
 }
 
-// One workgroup per block n: mean of the down_g half over the B slots, then in_proj's hidden half.
+// Split-K reduction, once per element: hd[m, k] = sum_s part[s, m, k] and
+// hg[n, k] = (1/B) sum_b sum_s part[s, n*B + b, r + k], both summed in a fixed order.
+__global__ __launch_bounds__(256) void hidden_reduce_kernel(const float* __restrict__ part,
+                                                            int nsplit, int N, int B, int r,
+                                                            float* __restrict__ hd,
+                                                            float* __restrict__ hg) {
+  const int NB = N * B;
+  const int64_t stride = (int64_t)NB * 2 * r;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < (int64_t)NB * r) {
+    const int64_t m = i / r, k = i % r;
+    float v = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) v += part[sp * stride + m * 2 * r + k];
+    hd[i] = v;
+  } else if (i < (int64_t)NB * r + (int64_t)N * r) {
+    const int64_t j = i - (int64_t)NB * r;
+    const int64_t n = j / r, k = j % r;
+    float sum = 0.f;
+    for (int b = 0; b < B; ++b) {
+      float v = 0.f;
+      for (int sp = 0; sp < nsplit; ++sp) v += part[sp * stride + (n * B + b) * 2 * r + r + k];
+      sum += v;
+    }
+    hg[j] = sum / (float)B;
+  }
+}
+
+// One workgroup per (block n, 64 output channels), in fp32:
+//   xh[n, b, c] = sum_k P[c, k] hd[n, b, k] + sum_k P[c, r + k] hg[n, k].
+// The in_proj slice is staged transposed (k-major) in LDS so neighbouring threads (channels) read
+// neighbouring addresses.
 template <int R>
-__global__ __launch_bounds__(256) void hidden_project_kernel(const float* __restrict__ hdg,
+__global__ __launch_bounds__(256) void hidden_project_kernel(const float* __restrict__ hd,
+                                                             const float* __restrict__ hg,
                                                              const uint16_t* __restrict__ in_proj,
                                                              int B, float* __restrict__ xh) {
   __shared__ float s_hd[16][R];
   __shared__ float s_hg[R];
-  const int n = blockIdx.x, tid = threadIdx.x;
-  const float* base = hdg + (int64_t)n * B * (2 * R);
-  for (int q = tid; q < B * R; q += 256) s_hd[q / R][q % R] = base[(int64_t)(q / R) * 2 * R + q % R];
-  for (int k = tid; k < R; k += 256) {
-    float s = 0.f;
-    for (int b = 0; b < B; ++b) s += base[(int64_t)b * 2 * R + R + k];
-    s_hg[k] = s / (float)B;
+  __shared__ float s_gp[64];
+  __shared__ uint16_t s_p[2 * R][64];  // in_proj[c0 + c, k] for k < 2R, stored [k][c]
+  const int n = blockIdx.x, c0 = blockIdx.y * 64, tid = threadIdx.x;
+  for (int q = tid; q < 16 * R; q += 256) {
+    const int b = q / R, k = q % R;
+    s_hd[b][k] = b < B ? hd[((int64_t)n * B + b) * R + k] : 0.f;
+  }
+  for (int k = tid; k < R; k += 256) s_hg[k] = hg[(int64_t)n * R + k];
+  for (int q = tid; q < 64 * (2 * R / 8); q += 256) {
+    const int c = q / (2 * R / 8), kq = q % (2 * R / 8);
+    const uint4 u = reinterpret_cast<const uint4*>(in_proj + (int64_t)(c0 + c) * 3 * R)[kq];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s_p[8 * kq + 2 * e][c] = (uint16_t)(w[e] & 0xffffu);
+      s_p[8 * kq + 2 * e + 1][c] = (uint16_t)(w[e] >> 16);
+    }
   }
   __syncthreads();
-  for (int i = tid; i < R; i += 256) {
-    float acc[16];
-#pragma unroll
-    for (int b = 0; b < 16; ++b) acc[b] = 0.f;
+  const int c = tid & 63, grp = tid >> 6;  // grp: slots 4*grp .. 4*grp+3
+  if (grp == 0) {
     float g = 0.f;
-    const uint4* prow = reinterpret_cast<const uint4*>(in_proj + (int64_t)i * 3 * R);
-    for (int kq = 0; kq < R / 8; ++kq) {
-      const uint4 p1 = prow[kq];
-      const uint4 p2 = prow[R / 8 + kq];
-      const float w1v[8] = {bf16_lo(p1.x), bf16_hi(p1.x), bf16_lo(p1.y), bf16_hi(p1.y),
-                            bf16_lo(p1.z), bf16_hi(p1.z), bf16_lo(p1.w), bf16_hi(p1.w)};
-      const float w2v[8] = {bf16_lo(p2.x), bf16_hi(p2.x), bf16_lo(p2.y), bf16_hi(p2.y),
-                            bf16_lo(p2.z), bf16_hi(p2.z), bf16_lo(p2.w), bf16_hi(p2.w)};
+    for (int k = 0; k < R; ++k) g = fmaf(bf16_to_f32(s_p[R + k][c]), s_hg[k], g);
+    s_gp[c] = g;
+  }
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < R; ++k) {
+    const float p = bf16_to_f32(s_p[k][c]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int k = kq * 8 + e;
-        g = fmaf(w2v[e], s_hg[k], g);
+    for (int v = 0; v < 4; ++v) acc[v] = fmaf(p, s_hd[4 * grp + v][k], acc[v]);
+  }
+  __syncthreads();
 #pragma unroll
-        for (int b = 0; b < 16; ++b)
-          if (b < B) acc[b] = fmaf(w1v[e], s_hd[b][k], acc[b]);
-      }
-    }
-    for (int b = 0; b < B; ++b) xh[((int64_t)n * B + b) * R + i] = acc[b] + g;
+  for (int v = 0; v < 4; ++v) {
+    const int b = 4 * grp + v;
+    if (b < B) xh[((int64_t)n * B + b) * R + c0 + c] = acc[v] + s_gp[c];
   }
 }
 
 }  // namespace
 
+// k chunks per split-K slice; every slice holds at least one chunk.
+int hidden_chunks_per_split(int NB, int H, int r) {
+  const int tiles = ((NB + kTM - 1) / kTM) * ((2 * r) / kTN);
+  const int kchunks = H / kTK;
+  int s = (512 + tiles - 1) / tiles;  // aim for >= 512 workgroups
+  if (s > kchunks) s = kchunks;
+  if (s < 1) s = 1;
+  return (kchunks + s - 1) / s;
+}
+
+int hidden_splits(int NB, int H, int r) {
+  const int cps = hidden_chunks_per_split(NB, H, r);
+  return (H / kTK + cps - 1) / cps;
+}
+
+// split-K partials, then hd [NB, r] and hg [N, r] (N = NB / B <= NB)
+size_t hidden_scratch_bytes(int NB, int H, int r) {
+  return (size_t)hidden_splits(NB, H, r) * NB * 2 * r * sizeof(float) +
+         (size_t)NB * r * sizeof(float) * 2;
+}
+
+// An upper bound of hidden_scratch_bytes over every H (the split count never exceeds the target
+// number of splits, whatever H is).
+size_t hidden_scratch_bytes_any_h(int NB, int r) {
+  const int tiles = ((NB + kTM - 1) / kTM) * ((2 * r) / kTN);
+  const int smax = (512 + tiles - 1) / tiles;
+  return (size_t)smax * NB * 2 * r * sizeof(float) + (size_t)NB * r * sizeof(float) * 2;
+}
+
 hipError_t launch_hidden_gemm(const uint16_t* h, const uint16_t* down_h, const uint16_t* down_g,
-                              int NB, int H, int r, float* hdg, hipStream_t s) {
-  dim3 grid((NB + kTM - 1) / kTM, (2 * r) / kTN);
-  hipLaunchKernelGGL(hidden_gemm_kernel, grid, dim3(256), 0, s, h, down_h, down_g, NB, H, r, hdg);
+                              int NB, int H, int r, float* part, hipStream_t s) {
+  const int ns = hidden_splits(NB, H, r);
+  const int kslice = hidden_chunks_per_split(NB, H, r) * kTK;
+  dim3 grid((NB + kTM - 1) / kTM, (2 * r) / kTN, ns);
+  hipLaunchKernelGGL(hidden_gemm_kernel, grid, dim3(256), 0, s, h, down_h, down_g, NB, H, r,
+                     kslice, part);
   return hipGetLastError();
 }
 
-hipError_t launch_hidden_project(const float* hdg, const uint16_t* in_proj, int N, int B, int r,
-                                 float* xh, hipStream_t s) {
+hipError_t launch_hidden_project(const float* part, int H, const uint16_t* in_proj, int N, int B,
+                                 int r, float* xh, hipStream_t s) {
+  const int NB = N * B;
+  const int ns = hidden_splits(NB, H, r);
+  float* hd = const_cast<float*>(part) + (size_t)ns * NB * 2 * r;
+  float* hg = hd + (size_t)NB * r;
+  const int64_t total = (int64_t)NB * r + (int64_t)N * r;
+  hipLaunchKernelGGL(hidden_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                     part, ns, N, B, r, hd, hg);
+  dim3 grid(N, r / 64);
   switch (r) {
     case 64:
-      hipLaunchKernelGGL(hidden_project_kernel<64>, dim3(N), dim3(256), 0, s, hdg, in_proj, B, xh);
+      hipLaunchKernelGGL(hidden_project_kernel<64>, grid, dim3(256), 0, s, hd, hg, in_proj, B, xh);
       break;
     case 128:
-      hipLaunchKernelGGL(hidden_project_kernel<128>, dim3(N), dim3(256), 0, s, hdg, in_proj, B, xh);
+      hipLaunchKernelGGL(hidden_project_kernel<128>, grid, dim3(256), 0, s, hd, hg, in_proj, B, xh);
       break;
     case 256:
-      hipLaunchKernelGGL(hidden_project_kernel<256>, dim3(N), dim3(256), 0, s, hdg, in_proj, B, xh);
+      hipLaunchKernelGGL(hidden_project_kernel<256>, grid, dim3(256), 0, s, hd, hg, in_proj, B, xh);
       break;
     default: return hipErrorInvalidValue;
   }

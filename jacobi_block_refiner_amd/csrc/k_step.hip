@@ -24,15 +24,28 @@ __global__ __launch_bounds__(256) void initial_block_kernel(const uint16_t* __re
   float bv = -INFINITY;
   int bi = INT_MAX;
   const int64_t nq = V / 8;
-  for (int64_t q = tid; q < nq; q += 256) {
-    const uint4 u = ld_nt16(reinterpret_cast<const uint4*>(row) + q);
-    const int id = (int)(q * 8);
+  const uint4* rq = reinterpret_cast<const uint4*>(row);
+  auto scan = [&](const uint4& u, int id) __attribute__((always_inline)) {
     const float v8[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
                          bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (v8[e] > bv) { bv = v8[e]; bi = id + e; }
+    for (int e = 0; e < 8; ++e) {
+      const bool gt = v8[e] > bv;
+      bv = gt ? v8[e] : bv;
+      bi = gt ? id + e : bi;
+    }
+  };
+  // four independent 16-byte loads in flight per thread; a thread's ids only increase, so the
+  // strict > keeps its lowest id among equal values
+  int64_t q = tid;
+  for (; q + 3 * 256 < nq; q += 4 * 256) {
+    const uint4 u0 = rq[q], u1 = rq[q + 256], u2 = rq[q + 512], u3 = rq[q + 768];
+    scan(u0, (int)(q * 8));
+    scan(u1, (int)((q + 256) * 8));
+    scan(u2, (int)((q + 512) * 8));
+    scan(u3, (int)((q + 768) * 8));
   }
+  for (; q < nq; q += 256) scan(rq[q], (int)(q * 8));
   for (int64_t v = nq * 8 + tid; v < V; v += 256) argmax_merge(bv, bi, bf16_to_f32(row[v]), (int)v);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {

@@ -13,12 +13,18 @@ int readout_waves();
 int readout_tiles(int64_t V);
 int readout_wgs_per_cu();
 
-// K1a: hdg[m, j] = sum_k h[m, k] * Wcat[j, k], Wcat = [down_h; down_g], m < NB, j < 2r (fp32 out).
+// K1a: split-K partials of hdg[m, j] = sum_k h[m, k] * Wcat[j, k], Wcat = [down_h; down_g],
+// m < NB = N*B, j < 2r; scratch [hidden_splits, NB, 2r] fp32.
+int hidden_splits(int NB, int H, int r);
+size_t hidden_scratch_bytes(int NB, int H, int r);
+size_t hidden_scratch_bytes_any_h(int NB, int r);
 hipError_t launch_hidden_gemm(const uint16_t* h, const uint16_t* down_h, const uint16_t* down_g,
-                              int NB, int H, int r, float* hdg, hipStream_t s);
-// K1b: xh[n, b] = in_proj[:, :r] . hdg[n, b, :r] + in_proj[:, r:2r] . mean_b hdg[n, b, r:].
-hipError_t launch_hidden_project(const float* hdg, const uint16_t* in_proj, int N, int B, int r,
-                                 float* xh, hipStream_t s);
+                              int NB, int H, int r, float* part, hipStream_t s);
+// K1b: reduce the partials (fixed order), then
+// xh[n, b] = in_proj[:, :r] . hdg[n, b, :r] + in_proj[:, r:2r] . mean_b hdg[n, b, r:]; `part` is
+// the scratch of launch_hidden_gemm (hidden_scratch_bytes long).
+hipError_t launch_hidden_project(const float* part, int H, const uint16_t* in_proj, int N, int B,
+                                 int r, float* xh, hipStream_t s);
 // K2: blk[n, 0] = anchor[n]; blk[n, b] = argmax_v base[n*(B-1)+b-1, v].
 hipError_t launch_initial_block(const uint16_t* base, int64_t ld, const int64_t* anchor, int N,
                                 int B, int64_t V, int64_t* blk, hipStream_t s);

@@ -11,6 +11,11 @@
 
 namespace {
 
+// Scratch is sized for the widest supported MLP (M = 1024) and hidden size, so
+// xpress_workspace_size does not depend on M or H.
+constexpr int kMaxM = 1024;
+constexpr int kMaxH = 16384;
+
 thread_local std::string g_err;
 
 xpress_status fail(xpress_status st, const char* fmt, ...) {
@@ -64,7 +69,8 @@ xpress_status check_weights(const xpress_weights* w, bool need_hidden, bool need
   xpress_status st = check_dims(w->B, w->r, w->V);
   if (st != XPRESS_OK) return st;
   if (need_hidden) {
-    if (w->H < 64 || w->H % 64) return fail(XPRESS_ERR_ARG, "H=%d not a positive multiple of 64", w->H);
+    if (w->H < 64 || w->H % 64 || w->H > kMaxH)
+      return fail(XPRESS_ERR_ARG, "H=%d not a multiple of 64 in [64, %d]", w->H, kMaxH);
     XP_PTR(w->down_h);
     XP_PTR(w->down_g);
     XP_PTR(w->in_proj);
@@ -97,10 +103,8 @@ struct Layout {
          total = 0;
 };
 
-// Latent scratch for the widest supported MLP (M = 1024), so the size does not depend on M.
-constexpr int kMaxM = 1024;
 
-Layout step_layout(int N, int B, int r, int64_t V, int C, int K) {
+Layout step_layout(int N, int B, int r, int H, int64_t V, int C, int K) {
   Layout L;
   const size_t rows = (size_t)N * (B - 1);
   const size_t c = C > 0 ? (size_t)(C < V ? C : V) : 0;
@@ -110,7 +114,8 @@ Layout step_layout(int N, int B, int r, int64_t V, int C, int K) {
     off += up256(bytes);
     return at;
   };
-  L.hdg = take((size_t)N * B * 2 * r * sizeof(float));
+  (void)H;
+  L.hdg = take(xpress::hidden_scratch_bytes_any_h(N * B, r));
   L.xh = take((size_t)N * B * r * sizeof(float));
   L.lat = take(rows * r * 2);
   L.lscr = take(xpress::latent_scratch_bytes(N, r, kMaxM));
@@ -140,7 +145,7 @@ xpress_status xpress_workspace_size(int32_t n_max, int32_t B, int32_t r, int64_t
   if (n_max < 0 || C < 0 || k_max < 0) return fail(XPRESS_ERR_ARG, "negative n_max, C or k_max");
   xpress_status st = check_dims(B, r, V);
   if (st != XPRESS_OK) return st;
-  *bytes = step_layout(n_max, B, r, V, C, k_max).total;
+  *bytes = step_layout(n_max, B, r, kMaxH, V, C, k_max).total;
   return XPRESS_OK;
 }
 
@@ -164,13 +169,13 @@ xpress_status xpress_hidden_cache(const xpress_weights* w, const xpress_bf16* h,
   XP_PTR(h);
   XP_PTR(xh);
   XP_PTR(ws);
-  const size_t need = (size_t)N * w->B * 2 * w->r * sizeof(float);
+  const size_t need = xpress::hidden_scratch_bytes(N * w->B, w->H, w->r);
   if (ws_bytes < need)
     return fail(XPRESS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed for N=%d", ws_bytes, need, N);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   float* hdg = static_cast<float*>(ws);
   XP_TRY(xpress::launch_hidden_gemm(h, w->down_h, w->down_g, N * w->B, w->H, w->r, hdg, s), "hidden gemm");
-  XP_TRY(xpress::launch_hidden_project(hdg, w->in_proj, N, w->B, w->r, xh, s), "hidden project");
+  XP_TRY(xpress::launch_hidden_project(hdg, w->H, w->in_proj, N, w->B, w->r, xh, s), "hidden project");
   return XPRESS_OK;
 }
 
@@ -340,7 +345,7 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
   XP_PTR(am1);
   XP_PTR(blk);
   XP_PTR(ws);
-  const Layout L = step_layout(N, w->B, w->r, w->V, C, K);
+  const Layout L = step_layout(N, w->B, w->r, w->H, w->V, C, K);
   if (ws_bytes < L.total)
     return fail(XPRESS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed for N=%d, C=%d, K=%d",
                 ws_bytes, L.total, N, C, K);
@@ -352,7 +357,7 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
   xpress_bf16* lat = at<xpress_bf16>(ws, L.lat);
   void* lscr = at<char>(ws, L.lscr);
   XP_TRY(xpress::launch_hidden_gemm(h, w->down_h, w->down_g, N * B, w->H, r, hdg, s), "hidden gemm");
-  XP_TRY(xpress::launch_hidden_project(hdg, w->in_proj, N, B, r, xh, s), "hidden project");
+  XP_TRY(xpress::launch_hidden_project(hdg, w->H, w->in_proj, N, B, r, xh, s), "hidden project");
   if (flags & XPRESS_INIT_FROM_BASE)
     XP_TRY(xpress::launch_initial_block(base, base_ld, anchor, N, B, V, blk, s), "initial block");
   else
