@@ -84,74 +84,67 @@ __global__ __launch_bounds__(256) void hidden_gemm_kernel(const uint16_t* __rest
   }
 }
 
-// Split-K reduction, once per element: hd[m, k] = sum_s part[s, m, k] and
-// hg[n, k] = (1/B) sum_b sum_s part[s, n*B + b, r + k], both summed in a fixed order.
-__global__ __launch_bounds__(256) void hidden_reduce_kernel(const float* __restrict__ part,
-                                                            int nsplit, int N, int B, int r,
-                                                            float* __restrict__ hd,
-                                                            float* __restrict__ hg) {
-  const int NB = N * B;
-  const int64_t stride = (int64_t)NB * 2 * r;
+// Split-K reduction, once per element, in a fixed order: hdg[m, j] = sum_s part[s, m, j].
+__global__ __launch_bounds__(256) void hidden_reduce_kernel(const float4* __restrict__ part,
+                                                            int nsplit, int64_t n4,
+                                                            float4* __restrict__ hdg) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < (int64_t)NB * r) {
-    const int64_t m = i / r, k = i % r;
-    float v = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) v += part[sp * stride + m * 2 * r + k];
-    hd[i] = v;
-  } else if (i < (int64_t)NB * r + (int64_t)N * r) {
-    const int64_t j = i - (int64_t)NB * r;
-    const int64_t n = j / r, k = j % r;
-    float sum = 0.f;
-    for (int b = 0; b < B; ++b) {
-      float v = 0.f;
-      for (int sp = 0; sp < nsplit; ++sp) v += part[sp * stride + (n * B + b) * 2 * r + r + k];
-      sum += v;
-    }
-    hg[j] = sum / (float)B;
+  if (i >= n4) return;
+  float4 v = part[i];
+  for (int sp = 1; sp < nsplit; ++sp) {
+    const float4 u = part[sp * n4 + i];
+    v.x += u.x;
+    v.y += u.y;
+    v.z += u.z;
+    v.w += u.w;
   }
+  hdg[i] = v;
 }
 
 // One workgroup per (block n, 64 output channels), in fp32:
-//   xh[n, b, c] = sum_k P[c, k] hd[n, b, k] + sum_k P[c, r + k] hg[n, k].
-// The in_proj slice is staged transposed (k-major) in LDS so neighbouring threads (channels) read
-// neighbouring addresses.
+//   hg[k] = (1/B) sum_b hdg[n, b, r + k]
+//   xh[n, b, c] = sum_k P[c, k] hdg[n, b, k] + sum_k P[c, r + k] hg[k].
+// hd and hg sit in LDS (read as broadcasts); each thread streams its in_proj row from L2.
 template <int R>
-__global__ __launch_bounds__(256) void hidden_project_kernel(const float* __restrict__ hd,
-                                                             const float* __restrict__ hg,
+__global__ __launch_bounds__(256) void hidden_project_kernel(const float* __restrict__ hdg,
                                                              const uint16_t* __restrict__ in_proj,
                                                              int B, float* __restrict__ xh) {
   __shared__ float s_hd[16][R];
   __shared__ float s_hg[R];
   __shared__ float s_gp[64];
-  __shared__ uint16_t s_p[2 * R][64];  // in_proj[c0 + c, k] for k < 2R, stored [k][c]
   const int n = blockIdx.x, c0 = blockIdx.y * 64, tid = threadIdx.x;
   for (int q = tid; q < 16 * R; q += 256) {
     const int b = q / R, k = q % R;
-    s_hd[b][k] = b < B ? hd[((int64_t)n * B + b) * R + k] : 0.f;
+    s_hd[b][k] = b < B ? hdg[((int64_t)n * B + b) * 2 * R + k] : 0.f;
   }
-  for (int k = tid; k < R; k += 256) s_hg[k] = hg[(int64_t)n * R + k];
-  for (int q = tid; q < 64 * (2 * R / 8); q += 256) {
-    const int c = q / (2 * R / 8), kq = q % (2 * R / 8);
-    const uint4 u = reinterpret_cast<const uint4*>(in_proj + (int64_t)(c0 + c) * 3 * R)[kq];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s_p[8 * kq + 2 * e][c] = (uint16_t)(w[e] & 0xffffu);
-      s_p[8 * kq + 2 * e + 1][c] = (uint16_t)(w[e] >> 16);
-    }
+  for (int k = tid; k < R; k += 256) {
+    float sum = 0.f;
+    for (int b = 0; b < B; ++b) sum += hdg[((int64_t)n * B + b) * 2 * R + R + k];
+    s_hg[k] = sum / (float)B;
   }
   __syncthreads();
   const int c = tid & 63, grp = tid >> 6;  // grp: slots 4*grp .. 4*grp+3
+  const uint4* prow = reinterpret_cast<const uint4*>(in_proj + (int64_t)(c0 + c) * 3 * R);
   if (grp == 0) {
     float g = 0.f;
-    for (int k = 0; k < R; ++k) g = fmaf(bf16_to_f32(s_p[R + k][c]), s_hg[k], g);
+    for (int kq = 0; kq < R / 8; ++kq) {
+      const uint4 u = prow[R / 8 + kq];
+      const float w8[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
+                           bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g = fmaf(w8[e], s_hg[8 * kq + e], g);
+    }
     s_gp[c] = g;
   }
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < R; ++k) {
-    const float p = bf16_to_f32(s_p[k][c]);
+  for (int kq = 0; kq < R / 8; ++kq) {
+    const uint4 u = prow[kq];
+    const float w8[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
+                         bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w)};
 #pragma unroll
-    for (int v = 0; v < 4; ++v) acc[v] = fmaf(p, s_hd[4 * grp + v][k], acc[v]);
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] = fmaf(w8[e], s_hd[4 * grp + v][8 * kq + e], acc[v]);
   }
   __syncthreads();
 #pragma unroll
@@ -178,10 +171,9 @@ int hidden_splits(int NB, int H, int r) {
   return (H / kTK + cps - 1) / cps;
 }
 
-// split-K partials, then hd [NB, r] and hg [N, r] (N = NB / B <= NB)
+// split-K partials, then the reduced hdg [NB, 2r]
 size_t hidden_scratch_bytes(int NB, int H, int r) {
-  return (size_t)hidden_splits(NB, H, r) * NB * 2 * r * sizeof(float) +
-         (size_t)NB * r * sizeof(float) * 2;
+  return ((size_t)hidden_splits(NB, H, r) + 1) * NB * 2 * r * sizeof(float);
 }
 
 // An upper bound of hidden_scratch_bytes over every H (the split count never exceeds the target
@@ -189,7 +181,7 @@ size_t hidden_scratch_bytes(int NB, int H, int r) {
 size_t hidden_scratch_bytes_any_h(int NB, int r) {
   const int tiles = ((NB + kTM - 1) / kTM) * ((2 * r) / kTN);
   const int smax = (512 + tiles - 1) / tiles;
-  return (size_t)smax * NB * 2 * r * sizeof(float) + (size_t)NB * r * sizeof(float) * 2;
+  return ((size_t)smax + 1) * NB * 2 * r * sizeof(float);
 }
 
 hipError_t launch_hidden_gemm(const uint16_t* h, const uint16_t* down_h, const uint16_t* down_g,
@@ -206,21 +198,20 @@ hipError_t launch_hidden_project(const float* part, int H, const uint16_t* in_pr
                                  int r, float* xh, hipStream_t s) {
   const int NB = N * B;
   const int ns = hidden_splits(NB, H, r);
-  float* hd = const_cast<float*>(part) + (size_t)ns * NB * 2 * r;
-  float* hg = hd + (size_t)NB * r;
-  const int64_t total = (int64_t)NB * r + (int64_t)N * r;
-  hipLaunchKernelGGL(hidden_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                     part, ns, N, B, r, hd, hg);
+  float* hdg = const_cast<float*>(part) + (size_t)ns * NB * 2 * r;
+  const int64_t n4 = (int64_t)NB * 2 * r / 4;
+  hipLaunchKernelGGL(hidden_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const float4*>(part), ns, n4, reinterpret_cast<float4*>(hdg));
   dim3 grid(N, r / 64);
   switch (r) {
     case 64:
-      hipLaunchKernelGGL(hidden_project_kernel<64>, grid, dim3(256), 0, s, hd, hg, in_proj, B, xh);
+      hipLaunchKernelGGL(hidden_project_kernel<64>, grid, dim3(256), 0, s, hdg, in_proj, B, xh);
       break;
     case 128:
-      hipLaunchKernelGGL(hidden_project_kernel<128>, grid, dim3(256), 0, s, hd, hg, in_proj, B, xh);
+      hipLaunchKernelGGL(hidden_project_kernel<128>, grid, dim3(256), 0, s, hdg, in_proj, B, xh);
       break;
     case 256:
-      hipLaunchKernelGGL(hidden_project_kernel<256>, grid, dim3(256), 0, s, hd, hg, in_proj, B, xh);
+      hipLaunchKernelGGL(hidden_project_kernel<256>, grid, dim3(256), 0, s, hdg, in_proj, B, xh);
       break;
     default: return hipErrorInvalidValue;
   }
