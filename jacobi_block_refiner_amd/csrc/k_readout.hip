@@ -50,12 +50,16 @@ int env_int(const char* name, int dflt) {
 // (base, in the accumulator layout). Coalesced 16-byte loads stream at full HBM rate; reading
 // base directly in the accumulator layout (8 bytes per lane, 32 rows per instruction) does not.
 //
-// Iteration t (one barrier): MFMA + epilogue on stage t%2; write the registers (unit t+1) into
-// stage (t+1)%2; issue the loads of unit t+2. Each wave's per-row winners go to a double-buffered
-// LDS slot; wave 0 reduces them one unit later and stores the partials. Loads sit outside
-// data-dependent branches (rows past the end are clamped to the last row, ids past V to the
-// padded row end, which the base stride guarantees is readable), so the compiler's wait counts
-// keep them in flight across the iteration.
+// Iteration t (one barrier) is software-pipelined: the MFMA chain of unit t+1 (into a second
+// accumulator, with unit t+1's base values read from LDS into registers) and the epilogue of unit t
+// form one branch-free block, so the VALU can work on unit t while the matrix core works on
+// unit t+1; then the register set holding
+// unit t+2 is written into the freed LDS stage and refilled with the loads of unit t+4 (two
+// register sets alternate, so every load has two iterations to arrive). Each wave's
+// per-row winners go to a double-buffered LDS slot; wave 0 reduces them one unit later and stores
+// the partials. Loads sit outside data-dependent branches (rows past the end are clamped to the
+// last row, ids past V to the padded row end, which the base stride guarantees is readable), so
+// the compiler's wait counts keep them in flight across the iteration.
 template <int R, int NW>
 __global__ __launch_bounds__(NW * 64) void readout_partial_kernel(
     const uint16_t* __restrict__ lat, const uint16_t* __restrict__ w2,
@@ -94,8 +98,11 @@ __global__ __launch_bounds__(NW * 64) void readout_partial_kernel(
   // Prefetch cursor (unit whose data goes into the staging registers next), kept as
   // (vocabulary tile, row tile) and advanced without divisions; it stops at the last unit.
   int pf_tile = u0 / n_rt, pf_rt = u0 % n_rt, pf_left = T;
-  u32x4 lreg[LQ], breg[BQT];
-  auto load_next = [&]() __attribute__((always_inline)) {
+  // two register sets: loads run two iterations ahead; set_tile[k] is the vocabulary tile of the
+  // unit held in set k
+  u32x4 lreg_s[2][LQ], breg_s[2][BQT];
+  int set_tile[2];
+  auto load_next = [&](u32x4 (&lreg)[LQ], u32x4 (&breg)[BQT], int& stile) __attribute__((always_inline)) {
     const int r0 = pf_rt * 32;
     const int c0 = pf_tile * BQ;
 #pragma unroll
@@ -108,15 +115,19 @@ __global__ __launch_bounds__(NW * 64) void readout_partial_kernel(
     for (int q = 0; q < BQT; ++q) {
       const int idx = min(tid + q * NT, 32 * BQ - 1);
       const int r = min(r0 + idx / BQ, rows - 1);
-      const int c = min(c0 + idx % BQ, last_chunk);
-      breg[q] = reinterpret_cast<const u32x4*>(base + (int64_t)r * ld)[c];
+      breg[q] = reinterpret_cast<const u32x4*>(base + (int64_t)r * ld)[min(c0 + idx % BQ, last_chunk)];
     }
+    stile = pf_tile;
     if (pf_left > 1) {
       --pf_left;
       if (++pf_rt == n_rt) { pf_rt = 0; ++pf_tile; }
     }
   };
-  auto store_staged = [&](int buf) __attribute__((always_inline)) {
+  // Register set -> LDS stage. Base values of ids >= V (the padding of the last chunk, and chunks
+  // past V in the tile that straddles V) become -inf, so they never win and the epilogue needs no
+  // bound check. The masking runs here, where the loaded values are consumed anyway, not right
+  // after the loads (which would wait for them).
+  auto store_staged = [&](int buf, const u32x4 (&lreg)[LQ], const u32x4 (&breg)[BQT], int stile) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < LQ; ++q) {
       const int idx = tid + q * NT;
@@ -127,9 +138,16 @@ __global__ __launch_bounds__(NW * 64) void readout_partial_kernel(
 #pragma unroll
     for (int q = 0; q < BQT; ++q) {
       const int idx = tid + q * NT;
+      const int id0 = 8 * (stile * BQ + idx % BQ);
+      u32x4 v = breg[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = (id0 + 2 * e < V) ? (v[e] & 0xffffu) : 0xff80u;
+        const uint32_t hi = (id0 + 2 * e + 1 < V) ? (v[e] >> 16) : 0xff80u;
+        v[e] = lo | (hi << 16);
+      }
       if ((32 * BQ) % NT == 0 || idx < 32 * BQ)
-        s_base[buf][(idx / BQ) * BLD + idx % BQ] =
-            make_uint4(breg[q].x, breg[q].y, breg[q].z, breg[q].w);
+        s_base[buf][(idx / BQ) * BLD + idx % BQ] = make_uint4(v.x, v.y, v.z, v.w);
     }
   };
   // wave 0: winners of the unit held in s_rv/s_ri[b] across the waves -> global partials.
@@ -143,83 +161,99 @@ __global__ __launch_bounds__(NW * 64) void readout_partial_kernel(
     if (prow < rows) part[(int64_t)prow * ntiles + tile] = make_uint2(__float_as_uint(v), (unsigned)i);
   };
 
-  load_next();
-  store_staged(0);
-  load_next();
-  __syncthreads();
-
-  int t = 0;
-  int tile = u0 / n_rt, rt = u0 % n_rt;
-  int prev_tile = 0, prev_rt = 0;
   bf16x8 a[KS];
-  while (t < T) {
-    // segment: the units of this workgroup's range that share vocabulary tile `tile`
-    const int seg_end = min(T, t + (n_rt - rt));
-    {
-      const int v = min(tile * TV + wave * 32 + l32, V - 1);
-      const u32x4* src = reinterpret_cast<const u32x4*>(w2 + (int64_t)v * R) + half;
+  int cur_tile = -1;
+  auto load_w2 = [&](int tile) __attribute__((always_inline)) {
+    const int v = min(tile * TV + wave * 32 + l32, V - 1);
+    const u32x4* src = reinterpret_cast<const u32x4*>(w2 + (int64_t)v * R) + half;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) a[s] = __builtin_bit_cast(bf16x8, src[2 * s]);
+    for (int s = 0; s < KS; ++s) a[s] = __builtin_bit_cast(bf16x8, src[2 * s]);
+    // Wait for these loads here, in the (rare) tile-change branch. Otherwise the MFMA chain,
+    // which is shared by both paths, would carry a conservative wait for every load in flight
+    // (vmcnt 0) on every unit and defeat the prefetch of the staged units.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt untouched
+    cur_tile = tile;
+  };
+  auto mfma_unit = [&](int buf, f32x16& acc, uint2 (&bq)[4]) __attribute__((always_inline)) {
+    acc = f32x16{};
+    const uint4* sl = s_lat[buf];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      acc = mfma32x32x16(a[s], as_bf16x8(sl[l32 * LDQ + 2 * s + half]), acc);
+    // this lane's base values: row l32, ids 32*wave + 8g + 4*half + 0..3 of the tile
+    const uint2* sb = reinterpret_cast<const uint2*>(s_base[buf] + l32 * BLD + wave * 4);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) bq[g] = sb[2 * g + half];
+  };
+  auto epilogue = [&](int t, int tile, const f32x16& acc, const uint2 (&bq)[4]) __attribute__((always_inline)) {
+    float lg[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      lg[4 * g + 0] = acc[4 * g + 0] + bf16_lo(bq[g].x);
+      lg[4 * g + 1] = acc[4 * g + 1] + bf16_hi(bq[g].x);
+      lg[4 * g + 2] = acc[4 * g + 2] + bf16_lo(bq[g].y);
+      lg[4 * g + 3] = acc[4 * g + 3] + bf16_hi(bq[g].y);
     }
     const int vl = tile * TV + wave * 32 + 4 * half;
-    const bool full_tile = (tile + 1) * TV <= V;
-    for (; t < seg_end; ++t, ++rt) {
-      const int buf = t & 1;
-      f32x16 acc = {};
-      const uint4* sl = s_lat[buf];
+    float bv = lg[0];
+    int bl = 0;  // local index 4g + k of this lane's best id
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        acc = mfma32x32x16(a[s], as_bf16x8(sl[l32 * LDQ + 2 * s + half]), acc);
-      // this lane's base values: row l32, ids 32*wave + 8g + 4*half + 0..3 of the tile
-      const uint2* sb = reinterpret_cast<const uint2*>(s_base[buf] + l32 * BLD + wave * 4);
-      float lg[16];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint2 q = sb[2 * g + half];
-        lg[4 * g + 0] = acc[4 * g + 0] + bf16_lo(q.x);
-        lg[4 * g + 1] = acc[4 * g + 1] + bf16_hi(q.x);
-        lg[4 * g + 2] = acc[4 * g + 2] + bf16_lo(q.y);
-        lg[4 * g + 3] = acc[4 * g + 3] + bf16_hi(q.y);
-      }
-      float bv = lg[0];
-      int bl = 0;  // local index 4g + k of this lane's best id
-      if (full_tile) {
-#pragma unroll
-        for (int e = 1; e < 16; ++e) {
-          const bool gt = lg[e] > bv;
-          bv = gt ? lg[e] : bv;
-          bl = gt ? e : bl;
-        }
-      } else {  // the tile straddling V: ids >= V never win
-        bv = (vl < V) ? lg[0] : -INFINITY;
-#pragma unroll
-        for (int e = 1; e < 16; ++e) {
-          const bool gt = (vl + 8 * (e >> 2) + (e & 3) < V) & (lg[e] > bv);
-          bv = gt ? lg[e] : bv;
-          bl = gt ? e : bl;
-        }
-      }
-      int bi = vl + 8 * (bl >> 2) + (bl & 3);
-      {
-        const float ov = __shfl_xor(bv, 32);
-        const int oi = __shfl_xor(bi, 32);
-        argmax_merge(bv, bi, ov, oi);
-      }
-      if (lane < 32) {
-        s_rv[buf][wave][lane] = bv;
-        s_ri[buf][wave][lane] = bi;
-      }
-      if (t > 0 && wave == 0) flush(buf ^ 1, prev_tile, prev_rt);
-      store_staged(buf ^ 1);
-      load_next();
-      prev_tile = tile;
-      prev_rt = rt;
-      __syncthreads();
+    for (int e = 1; e < 16; ++e) {
+      const bool gt = lg[e] > bv;
+      bv = gt ? lg[e] : bv;
+      bl = gt ? e : bl;
     }
-    ++tile;
-    rt = 0;
+    int bi = vl + 8 * (bl >> 2) + (bl & 3);
+    const float ov = __shfl_xor(bv, 32);
+    const int oi = __shfl_xor(bi, 32);
+    argmax_merge(bv, bi, ov, oi);
+    // lanes l and l^32 now hold the same winner: both write it (same address, same value)
+    s_rv[t & 1][wave][l32] = bv;
+    s_ri[t & 1][wave][l32] = bi;
+  };
+
+  // prologue: stage 0 <- unit 0, stage 1 <- unit 1, register sets <- units 2 and 3,
+  // acc <- unit 0
+  load_next(lreg_s[0], breg_s[0], set_tile[0]);
+  store_staged(0, lreg_s[0], breg_s[0], set_tile[0]);
+  load_next(lreg_s[1], breg_s[1], set_tile[1]);
+  store_staged(1, lreg_s[1], breg_s[1], set_tile[1]);
+  load_next(lreg_s[0], breg_s[0], set_tile[0]);
+  load_next(lreg_s[1], breg_s[1], set_tile[1]);
+  __syncthreads();
+  int tile = u0 / n_rt, rt = u0 % n_rt;  // unit t
+  int ntile = tile, nrt = rt;            // unit t+1
+  if (++nrt == n_rt) { nrt = 0; ++ntile; }
+  int ptile = 0, prt = 0;                // unit t-1
+  f32x16 acc0, acc1;
+  uint2 bq0[4], bq1[4];
+  load_w2(tile);
+  mfma_unit(0, acc0, bq0);
+  __syncthreads();  // stage 0 is rewritten (unit 2) in the first iteration
+
+  auto iter = [&](int t, f32x16& acc_cur, uint2 (&bq_cur)[4], f32x16& acc_nxt,
+                  uint2 (&bq_nxt)[4], u32x4 (&lreg)[LQ], u32x4 (&breg)[BQT], int& stile)
+                  __attribute__((always_inline)) {
+    if (ntile != cur_tile) load_w2(ntile);  // workgroup-uniform, rare
+    mfma_unit((t + 1) & 1, acc_nxt, bq_nxt);  // past the last unit: recomputes a staged unit
+    epilogue(t, tile, acc_cur, bq_cur);
+    if (t > 0 && wave == 0) flush((t - 1) & 1, ptile, prt);
+    // stage t%2 (unit t) was last read by the MFMA and base reads of the previous iteration,
+    // which every wave finished before that iteration's barrier
+    store_staged(t & 1, lreg, breg, stile);  // unit t+2 (register set t%2)
+    load_next(lreg, breg, stile);            // unit t+4
+    __syncthreads();
+    ptile = tile; prt = rt;
+    tile = ntile; rt = nrt;
+    if (++nrt == n_rt) { nrt = 0; ++ntile; }
+  };
+  int t = 0;
+  for (; t + 1 < T; t += 2) {
+    iter(t, acc0, bq0, acc1, bq1, lreg_s[0], breg_s[0], set_tile[0]);
+    iter(t + 1, acc1, bq1, acc0, bq0, lreg_s[1], breg_s[1], set_tile[1]);
   }
-  if (wave == 0) flush((T - 1) & 1, prev_tile, prev_rt);
+  if (t < T) iter(t, acc0, bq0, acc1, bq1, lreg_s[0], breg_s[0], set_tile[0]);
+  if (wave == 0) flush((T - 1) & 1, ptile, prt);
 }
 
 // One workgroup per readout row: reduce the row's tile partials, write blk in place, flag changes.
