@@ -7,11 +7,9 @@
 
 namespace xpress {
 
-// Readout tiling: a workgroup scores TV = 32 * readout_waves() vocabulary ids per unit against a
-// 32-row tile; a persistent grid of readout_wgs_per_cu() workgroups per CU splits the units.
-int readout_waves();
+// Readout partials per row: the vocabulary is cut into min(256, ceil(V/32)) contiguous ranges of
+// 32-id steps; the readout kernel leaves one (max, lowest id) partial per (row, range).
 int readout_tiles(int64_t V);
-int readout_wgs_per_cu();
 
 // K1a: split-K partials of hdg[m, j] = sum_k h[m, k] * Wcat[j, k], Wcat = [down_h; down_g],
 // m < NB = N*B, j < 2r; scratch [hidden_splits, NB, 2r] fp32.
