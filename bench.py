@@ -127,7 +127,7 @@ def main() -> int:
     blk2 = blk.clone()
     xpress.latent_pass(w, blk2, am1, xh, lat, ws)
     ntiles = xpress.readout_tiles(wl.V)
-    part = torch.empty(rows, ntiles, 2, dtype=torch.int32, device=dev)
+    part = torch.empty(ntiles, rows, 2, dtype=torch.int32, device=dev)
 
     def timed(fn, reps):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))

@@ -136,9 +136,9 @@ xpress_status xpress_readout_argmax(const xpress_weights* w, const xpress_bf16* 
  * _xpress_add_argmax_reduce_to_blk_kernel).
  * xpress_readout_tiles: number of partials per readout row: the vocabulary is cut into
  *   ntiles = min(256, ceil(V / 32)) contiguous ranges of whole 32-id steps (depends on V only).
- * xpress_readout_partials: part[p * ntiles + t] = {bits of the fp32 maximum of base + lat . w2
- *   over range t of row p, the lowest vocabulary id attaining it}. part: [N*(B-1), ntiles] pairs
- *   of uint32 (caller-owned, 8 bytes each).
+ * xpress_readout_partials: part[t * N*(B-1) + p] = {bits of the fp32 maximum of base + lat . w2
+ *   over range t of row p, the lowest vocabulary id attaining it}. part: [ntiles, N*(B-1)] pairs
+ *   of uint32, range-major (caller-owned, 8 bytes each).
  * xpress_argmax_reduce: blk[n, b] = the id of the largest pair of row p = n*(B-1)+b-1 (ties:
  *   lowest id), written in place; `changed` as in xpress_readout_argmax. */
 xpress_status xpress_readout_tiles(int64_t V, int32_t* ntiles);

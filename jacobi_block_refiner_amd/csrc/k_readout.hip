@@ -14,11 +14,11 @@
 // w2 and base stream from HBM once per pass. A workgroup owns a chunk of up to 8*RW 32-row tiles
 // and a contiguous range of 32-id vocabulary steps; each of its 8 waves keeps the lat fragments
 // of its RW row tiles in registers for the whole launch. Per step, the w2 tile [32 ids x r] and
-// the base tile [chunk rows x 32 ids] are fetched with coalesced 16-byte loads into registers
-// one step ahead, written into a double-buffered LDS stage, and every wave multiplies the shared
-// w2 tile against its own rows. Each w2 fragment read from LDS feeds RW MFMAs, and the per-row
-// winners stay in registers across the whole range: one partial per (row, range) is written at
-// the end. The ranges of one row chunk split the vocabulary evenly over the workgroups.
+// the base tile [chunk rows x 32 ids] are copied from HBM straight into LDS by the load units
+// (global_load_lds_dwordx4: no registers, no VALU), into a ring of three stages, so two steps are
+// in flight while one is computed. Every wave multiplies the shared w2 tile against its own rows;
+// each w2 fragment read from LDS feeds RW MFMAs, and the per-row winners stay in registers across
+// the whole range: one partial per (row, range) is written at the end.
 #include "launch.hpp"
 #include "xpress_common.hpp"
 
@@ -28,36 +28,55 @@ namespace xpress {
 
 namespace {
 
-constexpr int kNW = 8;              // waves per workgroup
-constexpr int kNT = 64 * kNW;       // threads per workgroup
 constexpr int kMaxRanges = 256;     // vocabulary ranges per row chunk (partials per row)
-constexpr int kBaseUnits = 9;       // 8-byte LDS units per base row of a step (64 bytes + pad)
 
 // v_mfma_f32_32x32x16_bf16 operand layout (wave64):
 //   A (32 x 16): lane l holds row l%32, k = 8*(l/32) + e, e = 0..7
 //   B (16 x 32): lane l holds col l%32, the same k
 //   D (32 x 32): lane l, accumulator v holds row 8*(v/4) + 4*(l/32) + v%4, col l%32
-// Here A = w2 rows (vocabulary ids), B = lat rows (readout rows): D[vocab][row]. Lane l thus
-// owns readout row l%32 and, in each group g of 8 ids of a step, the 4 consecutive ids
-// 8g + 4*(l/32) + 0..3, which it visits in increasing id order.
+// Here A = w2 rows, B = lat rows: D[vocab][row]. A-row i of a step holds vocabulary id
+// 16*((i/4)%2) + 4*(i/8) + i%4 of the step, so that lane l, accumulator v scores readout row l%32
+// against id 16*(l/32) + v: each lane owns 16 consecutive ids of its row (two 16-byte base chunks)
+// and visits them in increasing order.
 //
-// LDS layouts. w2 tile: id i's 16-byte chunk c sits at i*RQ + (c ^ (i % RQ)), so the 16 lanes of
-// an A-fragment read (16 ids, one chunk) hit 16 different bank groups. base tile: row stride of
-// 72 bytes, so the 8-byte reads of 32 rows (one per lane) spread over all banks.
-template <int R, int RW>
-__global__ __launch_bounds__(kNT) void readout_partial_kernel(
+// LDS stage layout (16-byte chunks): w2 A-row i, chunk c at i*RQ + (c ^ (i % RQ)); base row rr,
+// chunk c at 4*rr + (c ^ ((rr / 4) % 4)). Both XOR swizzles make the 16-lane phases of the
+// fragment reads hit 16 different bank groups. The copy engine writes lane j of a
+// global_load_lds_dwordx4 to M0 + 16*j, so each copy instruction fills 64 consecutive chunks and
+// its lanes fetch whichever global chunks belong there.
+__device__ __forceinline__ int w2_row_id(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
+
+// One 1 KiB copy: this lane's 16 bytes at gbase + off (a scalar base pointer and a per-lane
+// 32-bit byte offset) to LDS byte address lds_base + 16 * lane. Written as inline assembly so
+// the compiler's wait-count bookkeeping stays out of it (the kernel waits for the copies itself,
+// with vmcnt, before the barrier that publishes a stage).
+__device__ __forceinline__ void lds_copy16(const void* gbase, uint32_t off, uint32_t lds_base) {
+  // one wait state between the M0 write and the copy that reads it
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_base), "v"(off), "s"(gbase) : "memory");
+}
+
+template <int R, int kNW, int RW>
+__global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
     const uint16_t* __restrict__ lat, const uint16_t* __restrict__ w2,
     const uint16_t* __restrict__ base, int64_t ld, int rows, int V, int nvr, int n_rc,
     uint2* __restrict__ part, const int32_t* __restrict__ flags, int pass) {
   if (pass_skipped(flags, pass)) return;
   constexpr int KS = R / 16;
-  constexpr int RQ = R / 8;                        // 16-byte chunks per w2 / lat row
-  constexpr int CH = kNW * RW * 32;                // rows per row chunk
-  constexpr int WQ = (32 * RQ + kNT - 1) / kNT;    // w2 chunks per thread per step
-  constexpr int BQ = CH * 4 / kNT;                 // base chunks per thread per step
+  constexpr int RQ = R / 8;                     // 16-byte chunks per w2 / lat row
+  constexpr int CH = kNW * RW * 32;             // rows per row chunk
+  constexpr int WCH = 32 * RQ;                  // w2 chunks per stage
+  constexpr int BCH = CH * 4;                   // base chunks per stage
+  constexpr int SCH = WCH + BCH;                // chunks per stage
+  // copy instructions per wave per step; when the w2 tile has fewer than kNW * 64 chunks, the
+  // waves past it repeat the first ones (same bytes to the same place), so every wave issues the
+  // same number of copies and one vmcnt value fits all
+  constexpr int WI = (WCH / 64 + kNW - 1) / kNW;
+  constexpr int BI = BCH / 64 / kNW;
+  constexpr int DI = WI + BI;
+  static_assert(BCH % (64 * kNW) == 0, "base stage must split evenly over the waves");
 
-  __shared__ uint4 s_w2[2][32 * RQ];
-  __shared__ uint2 s_base[2][CH * kBaseUnits];
+  __shared__ uint4 s_stage[3][SCH];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -65,14 +84,13 @@ __global__ __launch_bounds__(kNT) void readout_partial_kernel(
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  // (row chunk, vocabulary range) of this workgroup. With several row chunks and ranges in
-  // multiples of 8, the chunks of one range go to workgroups on the same XCD (workgroups are
-  // dealt round-robin over the 8 XCDs), so its w2 tiles are fetched into that XCD's L2 once.
   int rc, vr;
   if (n_rc == 1) {
     rc = 0;
     vr = blockIdx.x;
   } else if ((nvr & 7) == 0) {
+    // the row chunks of one range on one XCD (workgroups are dealt round-robin over the 8
+    // XCDs), so its w2 tiles reach that XCD's L2 once
     const int j = blockIdx.x >> 3;
     rc = j % n_rc;
     vr = (j / n_rc) * 8 + (blockIdx.x & 7);
@@ -96,51 +114,74 @@ __global__ __launch_bounds__(kNT) void readout_partial_kernel(
 #pragma unroll
     for (int s = 0; s < KS; ++s) bl[k][s] = __builtin_bit_cast(bf16x8, src[2 * s + half]);
   }
+  // These loads complete here, so no wait for them lands inside the loop (where it would also
+  // wait for the stage copies in flight).
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   const bool active = row0 + wave * RW * 32 < rows;  // wave-uniform: the wave has real rows
 
-  // staging registers: the next step's w2 and base chunks
-  u32x4 wreg[WQ], breg[BQ];
-  auto load_step = [&](int t) __attribute__((always_inline)) {
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&s_stage[0][0];
+  // Per-lane byte offsets of the copies, relative to the step's w2 tile and to the chunk's base
+  // rows at the step's first id (loop-invariant; the step only moves the scalar base pointers).
+  // In the last step of the vocabulary, ids past V are clamped instead (w2 row V-1, the padded
+  // row's last chunk).
+  uint32_t offw[WI], offb[BI];
 #pragma unroll
-    for (int i = 0; i < WQ; ++i) {
-      const int q = min(tid + i * kNT, 32 * RQ - 1);
-      const int v = min(32 * t + q / RQ, V - 1);
-      wreg[i] = reinterpret_cast<const u32x4*>(w2 + (int64_t)v * R)[q % RQ];
+  for (int q = 0; q < WI; ++q) {
+    const int ins = (wave + q * kNW) % (WCH / 64);  // copy instruction index in the w2 tile
+    const int p = ins * 64 + lane;                   // chunk position in the stage
+    const int i = p / RQ, c = (p % RQ) ^ (i % RQ);
+    offw[q] = (uint32_t)((w2_row_id(i) * R + 8 * c) * 2);
+  }
+#pragma unroll
+  for (int q = 0; q < BI; ++q) {
+    const int p = (wave + q * kNW) * 64 + lane;      // base chunk position
+    const int rr = p >> 2, c = (p & 3) ^ ((rr >> 2) & 3);
+    offb[q] = (uint32_t)(((int64_t)(min(row0 + rr, rows - 1) - row0) * ld + 8 * c) * 2);
+  }
+  const uint16_t* base_rc = base + (int64_t)row0 * ld;
+  // Issue the copies of step t into stage st.
+  auto copy_step = [&](int t, int st) __attribute__((always_inline)) {
+    const uint32_t sbase = lds0 + (uint32_t)st * (SCH * 16);
+    const uint16_t* gw = w2 + (int64_t)t * 32 * R;
+    const uint16_t* gb = base_rc + 32 * t;
+    const bool tail = 32 * t + 32 > V;  // uniform
+#pragma unroll
+    for (int q = 0; q < WI; ++q) {
+      const int ins = (wave + q * kNW) % (WCH / 64);
+      uint32_t off = offw[q];
+      if (tail) {
+        const int p = ins * 64 + lane;
+        const int i = p / RQ, c = (p % RQ) ^ (i % RQ);
+        off = (uint32_t)(((min(32 * t + w2_row_id(i), V - 1) - 32 * t) * R + 8 * c) * 2);
+      }
+      lds_copy16(gw, off, __builtin_amdgcn_readfirstlane(sbase + ins * 1024));
     }
 #pragma unroll
-    for (int i = 0; i < BQ; ++i) {
-      const int q = tid + i * kNT;
-      const int r = min(row0 + (q >> 2), rows - 1);
-      breg[i] = reinterpret_cast<const u32x4*>(base + (int64_t)r * ld)[min(4 * t + (q & 3), last_chunk)];
+    for (int q = 0; q < BI; ++q) {
+      const int ins = wave + q * kNW;
+      uint32_t off = offb[q];
+      if (tail) {
+        const int p = ins * 64 + lane;
+        const int rr = p >> 2, c = (p & 3) ^ ((rr >> 2) & 3);
+        off = (uint32_t)(((int64_t)(min(row0 + rr, rows - 1) - row0) * ld +
+                          8 * (min(4 * t + c, last_chunk) - 4 * t)) * 2);
+      }
+      lds_copy16(gb, off, __builtin_amdgcn_readfirstlane(sbase + (WCH + ins * 64) * 16));
     }
   };
-  // Registers -> LDS stage. Base values of ids >= V (the padding of the last chunk, and chunks
-  // past V in the last step) become -inf, so they never win.
-  auto store_step = [&](int buf, int t) __attribute__((always_inline)) {
+
+  // The base tile enters the accumulators through the matrix core: two extra MFMAs per row tile
+  // with A = a 0/1 selection matrix (A-row i picks id w2_row_id(i)) and B = the row's base
+  // values, 8 consecutive ids per lane, which is a plain 16-byte chunk of the base row. The
+  // products are exact (x * 1, x * 0) and so is their sum, so the accumulator starts at exactly
+  // base[row, id]; no VALU conversion or add is left in the epilogue.
+  bf16x8 sel[2];
 #pragma unroll
-    for (int i = 0; i < WQ; ++i) {
-      const int q = tid + i * kNT;
-      if ((32 * RQ) % kNT == 0 || q < 32 * RQ) {
-        const int id = q / RQ, c = q % RQ;
-        s_w2[buf][id * RQ + (c ^ (id % RQ))] = make_uint4(wreg[i].x, wreg[i].y, wreg[i].z, wreg[i].w);
-      }
-    }
+  for (int sg = 0; sg < 2; ++sg) {
+    const int e1 = w2_row_id(l32) - 16 * sg - 8 * half;  // the one k of this lane's A-row hit
 #pragma unroll
-    for (int i = 0; i < BQ; ++i) {
-      const int q = tid + i * kNT;
-      const int id0 = 32 * t + 8 * (q & 3);
-      u32x4 v = breg[i];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = (id0 + 2 * e < V) ? (v[e] & 0xffffu) : 0xff80u;
-        const uint32_t hi = (id0 + 2 * e + 1 < V) ? (v[e] >> 16) : 0xff80u;
-        v[e] = lo | (hi << 16);
-      }
-      uint2* d = &s_base[buf][(q >> 2) * kBaseUnits + 2 * (q & 3)];
-      d[0] = make_uint2(v.x, v.y);
-      d[1] = make_uint2(v.z, v.w);
-    }
-  };
+    for (int e = 0; e < 8; ++e) sel[sg][e] = (e == e1) ? (__bf16)1.0f : (__bf16)0.0f;
+  }
 
   float bv[RW];
   int bi[RW];
@@ -149,45 +190,63 @@ __global__ __launch_bounds__(kNT) void readout_partial_kernel(
     bv[k] = -INFINITY;
     bi[k] = 32 * t0;
   }
-  // Step t of row tile k: logits of this lane's row for its 16 ids of the step, folded into
-  // the running winner. Within the step the ids rise with e, and steps rise with t, so a strict
-  // comparison keeps the lowest id among equal values.
-  auto epilogue = [&](int buf, int t, int k, const f32x16& acc) __attribute__((always_inline)) {
-    const uint2* sb = &s_base[buf][((wave * RW + k) * 32 + l32) * kBaseUnits + half];
+  // Step t of row tile k: the 16 logits of this lane's row (ids 32t + 16*half + e, e = 0..15)
+  // folded into the running winner. The step maximum comes from a tree of max operations; the
+  // lowest e holding it from a descent that prefers the lower half at every level. Steps rise
+  // with t, so a strict comparison keeps the lowest id among equal values.
+  auto epilogue = [&](int t, int k, const f32x16& acc) __attribute__((always_inline)) {
     float lg[16];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint2 q = sb[2 * g];
-      lg[4 * g + 0] = acc[4 * g + 0] + bf16_lo(q.x);
-      lg[4 * g + 1] = acc[4 * g + 1] + bf16_hi(q.x);
-      lg[4 * g + 2] = acc[4 * g + 2] + bf16_lo(q.y);
-      lg[4 * g + 3] = acc[4 * g + 3] + bf16_hi(q.y);
-    }
-    float sv = lg[0];
-    int se = 0;
+    for (int e = 0; e < 16; ++e) lg[e] = acc[e];
+    if (32 * t + 32 > V) {  // the last step of the vocabulary: ids >= V never win
 #pragma unroll
-    for (int e = 1; e < 16; ++e) {
-      const bool gt = lg[e] > sv;
-      sv = gt ? lg[e] : sv;
-      se = gt ? e : se;
+      for (int e = 0; e < 16; ++e)
+        if (32 * t + 16 * half + e >= V) lg[e] = -INFINITY;
     }
+    float m2[8], m4[4], m8[2];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m2[e] = fmaxf(lg[2 * e], lg[2 * e + 1]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m4[e] = fmaxf(m2[2 * e], m2[2 * e + 1]);
+    m8[0] = fmaxf(m4[0], m4[1]);
+    m8[1] = fmaxf(m4[2], m4[3]);
+    const float sv = fmaxf(m8[0], m8[1]);
+    const int s8 = m8[0] == sv ? 0 : 1;
+    const int s4 = 2 * s8 + ((s8 ? m4[2] : m4[0]) == sv ? 0 : 1);
+    const float a2 = s8 ? (s4 & 1 ? m2[6] : m2[4]) : (s4 & 1 ? m2[2] : m2[0]);
+    const int s2 = 2 * s4 + (a2 == sv ? 0 : 1);
+    float a1 = lg[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) a1 = s2 == e ? lg[2 * e] : a1;
+    const int se = 2 * s2 + (a1 == sv ? 0 : 1);
     const bool gt = sv > bv[k];
     bv[k] = gt ? sv : bv[k];
-    bi[k] = gt ? 32 * t + 4 * half + 8 * (se >> 2) + (se & 3) : bi[k];
+    bi[k] = gt ? 32 * t + 16 * half + se : bi[k];
   };
 
-  // prologue: stage 0 <- step t0, registers <- step t0+1
-  load_step(t0);
-  store_step(0, t0);
-  load_step(min(t0 + 1, t1 - 1));
-  __syncthreads();
+  // prologue: steps t0 and t0+1 in flight
+  copy_step(t0, 0);
+  copy_step(min(t0 + 1, t1 - 1), 1);
+  int st = 0;
   for (int t = t0; t < t1; ++t) {
-    const int buf = (t - t0) & 1;
+    // this wave's copies of step t are done (those of step t+1 may still run); after the
+    // barrier every wave's are, and every wave has finished step t-1 (its stage is free)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (DI & 15) | ((DI >> 4) << 14));  // vmcnt(DI)
+    __syncthreads();
+    copy_step(min(t + 2, t1 - 1), st == 0 ? 2 : st - 1);  // past the range end: refetches (L2)
     if (active) {
+      const uint4* sp = s_stage[st];
       f32x16 acc[RW];
 #pragma unroll
-      for (int k = 0; k < RW; ++k) acc[k] = f32x16{};
-      const uint4* sw = s_w2[buf] + l32 * RQ;
+      for (int k = 0; k < RW; ++k) {
+        const int rr = (wave * RW + k) * 32 + l32;
+        const int sw = (rr >> 2) & 3;
+        const bf16x8 b0 = as_bf16x8(sp[WCH + 4 * rr + ((2 * 0 + half) ^ sw)]);
+        const bf16x8 b1 = as_bf16x8(sp[WCH + 4 * rr + ((2 * 1 + half) ^ sw)]);
+        acc[k] = mfma32x32x16(sel[0], b0, f32x16{});
+        acc[k] = mfma32x32x16(sel[1], b1, acc[k]);
+      }
+      const uint4* sw = sp + l32 * RQ;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const bf16x8 a = as_bf16x8(sw[(2 * s + half) ^ (l32 % RQ)]);
@@ -195,15 +254,14 @@ __global__ __launch_bounds__(kNT) void readout_partial_kernel(
         for (int k = 0; k < RW; ++k) acc[k] = mfma32x32x16(a, bl[k][s], acc[k]);
       }
 #pragma unroll
-      for (int k = 0; k < RW; ++k) epilogue(buf, t, k, acc[k]);
+      for (int k = 0; k < RW; ++k) epilogue(t, k, acc[k]);
     }
-    // stage buf^1 was last read in the previous step, before its barrier
-    store_step(buf ^ 1, min(t + 1, t1 - 1));
-    load_step(min(t + 2, t1 - 1));  // past the range end: reloads the last step (L2 hits)
-    __syncthreads();
+    st = st == 2 ? 0 : st + 1;
   }
+  // drain the trailing copies before the workgroup's LDS can be handed to another workgroup
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
-  // lanes l and l^32 hold the same row with interleaved ids
+  // lanes l and l^32 hold the same row with the two halves of each step
 #pragma unroll
   for (int k = 0; k < RW; ++k) {
     float v = bv[k];
@@ -212,41 +270,49 @@ __global__ __launch_bounds__(kNT) void readout_partial_kernel(
     const int oi = __shfl_xor(i, 32);
     argmax_merge(v, i, ov, oi);
     const int row = row0 + (wave * RW + k) * 32 + l32;
-    if (half == 0 && row < rows) part[(int64_t)row * nvr + vr] = make_uint2(__float_as_uint(v), (unsigned)i);
+    // range-major partials: the 32 lanes store 256 contiguous bytes (scattered 8-byte stores
+    // into row-major partials cost a partial-line write-back per row at the end of the kernel)
+    if (half == 0 && row < rows) part[(int64_t)vr * rows + row] = make_uint2(__float_as_uint(v), (unsigned)i);
   }
 }
 
-// One workgroup per readout row: reduce the row's range partials, write blk in place, flag changes.
+// Partials of 64 consecutive rows per workgroup: thread (row lr, slice j) scans ranges j, j+4, ...
+// (each wave reads 64 consecutive rows of one range: 512 contiguous bytes), the four slice
+// winners of a row are merged in LDS, and the row's winner is written into blk in place.
 __global__ __launch_bounds__(256) void argmax_reduce_kernel(const uint2* __restrict__ part,
                                                             int ntiles, int rows, int B,
                                                             int64_t* __restrict__ blk,
                                                             int32_t* changed, int32_t* flags,
                                                             int pass) {
   if (pass_skipped(flags, pass)) return;
-  __shared__ float s_v[4];
-  __shared__ int s_i[4];
-  const int p = blockIdx.x;
+  __shared__ float s_v[4][64];
+  __shared__ int s_i[4][64];
+  const int lr = threadIdx.x & 63, j = threadIdx.x >> 6;
+  const int p = blockIdx.x * 64 + lr;
   float bv = -INFINITY;
   int bi = INT_MAX;
-  const uint2* pr = part + (int64_t)p * ntiles;
-  for (int t = threadIdx.x; t < ntiles; t += 256) {
-    const uint2 q = pr[t];
-    argmax_merge(bv, bi, __uint_as_float(q.x), (int)q.y);
-  }
+  if (p < rows) {
+    const uint2* pr = part + p;
+    int t = j;
+#pragma unroll 1
+    for (; t + 12 < ntiles; t += 16) {
+      uint2 q[4];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(bv, off);
-    const int oi = __shfl_xor(bi, off);
-    argmax_merge(bv, bi, ov, oi);
+      for (int u = 0; u < 4; ++u) q[u] = pr[(int64_t)(t + 4 * u) * rows];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) argmax_merge(bv, bi, __uint_as_float(q[u].x), (int)q[u].y);
+    }
+    for (; t < ntiles; t += 4) {
+      const uint2 q = pr[(int64_t)t * rows];
+      argmax_merge(bv, bi, __uint_as_float(q.x), (int)q.y);
+    }
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) {
-    s_v[wave] = bv;
-    s_i[wave] = bi;
-  }
+  s_v[j][lr] = bv;
+  s_i[j][lr] = bi;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < 4; ++w) argmax_merge(bv, bi, s_v[w], s_i[w]);
+  if (j == 0 && p < rows) {
+#pragma unroll
+    for (int u = 1; u < 4; ++u) argmax_merge(bv, bi, s_v[u][lr], s_i[u][lr]);
     const int n = p / (B - 1), b = 1 + p % (B - 1);
     int64_t* slot = blk + (int64_t)n * B + b;
     const int64_t nv = (int64_t)bi;
@@ -269,26 +335,29 @@ int device_cus() {
   return cus;
 }
 
-template <int R, int RW>
+template <int R, int NW, int RW>
 hipError_t launch_partial_t(const uint16_t* lat, const uint16_t* w2, const uint16_t* base,
                             int64_t ld, int rows, int64_t V, uint2* part, const int32_t* flags,
                             int pass, hipStream_t s) {
   const int nvr = readout_tiles(V);
-  constexpr int CH = kNW * RW * 32;
+  constexpr int CH = NW * RW * 32;
   const int n_rc = (rows + CH - 1) / CH;
-  hipLaunchKernelGGL((readout_partial_kernel<R, RW>), dim3((unsigned)(nvr * n_rc)), dim3(kNT), 0, s,
-                     lat, w2, base, ld, rows, (int)V, nvr, n_rc, part, flags, pass);
+  hipLaunchKernelGGL((readout_partial_kernel<R, NW, RW>), dim3((unsigned)(nvr * n_rc)), dim3(64 * NW),
+                     0, s, lat, w2, base, ld, rows, (int)V, nvr, n_rc, part, flags, pass);
   return hipGetLastError();
 }
 
-template <int RW>
-hipError_t launch_partial_rw(const uint16_t* lat, const uint16_t* w2, const uint16_t* base,
-                             int64_t ld, int rows, int64_t V, int r, uint2* part,
-                             const int32_t* flags, int pass, hipStream_t s) {
+// Row chunk shape: up to 256 rows, 8 waves of one 32-row tile each; more rows, 8 waves of two
+// 32-row tiles each (512 rows per chunk), so each w2 fragment read from LDS feeds two MFMAs.
+// (Four waves of four tiles, or sixteen of one, measured slower at 480 rows.)
+template <int NW, int RW>
+hipError_t launch_partial_shape(const uint16_t* lat, const uint16_t* w2, const uint16_t* base,
+                                int64_t ld, int rows, int64_t V, int r, uint2* part,
+                                const int32_t* flags, int pass, hipStream_t s) {
   switch (r) {
-    case 64: return launch_partial_t<64, RW>(lat, w2, base, ld, rows, V, part, flags, pass, s);
-    case 128: return launch_partial_t<128, RW>(lat, w2, base, ld, rows, V, part, flags, pass, s);
-    case 256: return launch_partial_t<256, RW>(lat, w2, base, ld, rows, V, part, flags, pass, s);
+    case 64: return launch_partial_t<64, NW, RW>(lat, w2, base, ld, rows, V, part, flags, pass, s);
+    case 128: return launch_partial_t<128, NW, RW>(lat, w2, base, ld, rows, V, part, flags, pass, s);
+    case 256: return launch_partial_t<256, NW, RW>(lat, w2, base, ld, rows, V, part, flags, pass, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -303,14 +372,14 @@ int readout_tiles(int64_t V) {
 hipError_t launch_readout_partial(const uint16_t* lat, const uint16_t* w2, const uint16_t* base,
                                   int64_t ld, int rows, int64_t V, int r, uint2* part,
                                   const int32_t* flags, int pass, hipStream_t s) {
-  if (rows <= kNW * 32) return launch_partial_rw<1>(lat, w2, base, ld, rows, V, r, part, flags, pass, s);
-  return launch_partial_rw<2>(lat, w2, base, ld, rows, V, r, part, flags, pass, s);
+  if (rows <= 256) return launch_partial_shape<8, 1>(lat, w2, base, ld, rows, V, r, part, flags, pass, s);
+  return launch_partial_shape<8, 2>(lat, w2, base, ld, rows, V, r, part, flags, pass, s);
 }
 
 hipError_t launch_argmax_reduce(const uint2* part, int ntiles, int rows, int B, int64_t* blk,
                                 int32_t* changed, int32_t* flags, int pass, hipStream_t s) {
-  hipLaunchKernelGGL(argmax_reduce_kernel, dim3(rows), dim3(256), 0, s, part, ntiles, rows, B,
-                     blk, changed, flags, pass);
+  hipLaunchKernelGGL(argmax_reduce_kernel, dim3((rows + 63) / 64), dim3(256), 0, s, part, ntiles,
+                     rows, B, blk, changed, flags, pass);
   return hipGetLastError();
 }
 

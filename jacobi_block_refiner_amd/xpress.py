@@ -200,7 +200,7 @@ def readout_tiles(V: int) -> int:
 
 
 def readout_partials(w: Weights, lat, base, part: torch.Tensor) -> torch.Tensor:
-    """part: int32/uint32-compatible tensor [rows, ntiles, 2] (value bits, id)."""
+    """part: int32/uint32-compatible tensor [ntiles, rows, 2] (value bits, id), range-major."""
     s = w.struct()
     _bf16(base, "base")
     assert base.stride(1) == 1
@@ -213,7 +213,7 @@ def readout_partials(w: Weights, lat, base, part: torch.Tensor) -> torch.Tensor:
 
 def argmax_reduce(part: torch.Tensor, blk: torch.Tensor, changed=None) -> torch.Tensor:
     N, B = blk.shape
-    ntiles = part.shape[1]
+    ntiles = part.shape[0]
     _check(lib().xpress_argmax_reduce(_ptr(part), ntiles, N, B, _ptr(blk), _ptr(changed),
                                       _stream()))
     return blk
