@@ -68,7 +68,9 @@ typedef struct {
   const xpress_bf16* down_g;  /* [r, H]   projection of the block-mean hidden state            */
   const xpress_bf16* in_proj; /* [r, 3r]  columns [0,r) act on down_h, [r,2r) on down_g,
                                           [2r,3r) on the token embedding                       */
-  const xpress_bf16* mix_L;   /* [r, B, B] FOLDED mixer, L[c,b,j] = raw[c,b,j]*[j<=b] + [j==b]
+  const xpress_bf16* mix_L;   /* [B, B, r] FOLDED mixer, channel innermost (the layout of the
+                                           kernels page's latent kernel):
+                                           mix_L[(b*B + j)*r + c] = raw[c,b,j]*[j<=b] + [j==b]
                                            (qwen3_xpress page, fold_from_raw_); only j <= b is
                                            read                                                */
   const xpress_bf16* w_gate;  /* [M, r]                                                        */
@@ -90,9 +92,11 @@ xpress_status xpress_workspace_size(int32_t n_max, int32_t B, int32_t r, int64_t
                                     int32_t k_max, size_t* bytes);
 
 /* Fold of a raw (training-form) mixer into its serving form (qwen3_xpress page,
- * XPressRefinerHead.fold_from_raw_): mix_L[c,b,j] = raw[c,b,j] * [j <= b] + [j == b], computed in
- * fp32 and rounded to bf16 (round to nearest even), as copying into a bf16 parameter does.
- * raw, mix_L: [r, B, B] bf16 (mix_L written; must not alias raw). */
+ * XPressRefinerHead.fold_from_raw_): L[c,b,j] = raw[c,b,j] * [j <= b] + [j == b], computed in
+ * fp32 and rounded to bf16 (round to nearest even), as copying into a bf16 parameter does, and
+ * stored channel innermost: mix_L[(b*B + j)*r + c] = L[c,b,j].
+ * raw: [r, B, B] bf16 (the parameter's own layout); mix_L: [B, B, r] bf16 (written; must not
+ * alias raw). */
 xpress_status xpress_fold_mixer(const xpress_bf16* raw, int32_t r, int32_t B, xpress_bf16* mix_L,
                                 xpress_stream stream);
 

@@ -5,14 +5,15 @@
 // XPressRefinerHead._refine_latent):
 //   1. gather the embedding of each slot's previous token: slot 0 reads am1, slot b reads blk[b-1];
 //   2. x = xh + P_e . e with P_e = in_proj[:, 2r:3r];
-//   3. per-channel causal mixer u[b, c] = sum_{j<=b} L[c, b, j] x[j, c];
+//   3. per-channel causal mixer u[b, c] = sum_{j<=b} L[b, j, c] x[j, c] (L stored [B, B, r]);
 //   4. SwiGLU: s = silu(w_gate . u) * (w_up . u);
 //   5. lat = u + w_down . s for slots 1..B-1 (slot 0 is never read out).
 // A block's 16 slots (padded with zero rows past B) are the M = 16 rows of a
 // v_mfma_f32_16x16x32_bf16 tile. One workgroup per block cannot keep enough CUs busy at small N
 // (each block-pass needs ~1 MB of weights, which one CU pulls from L2 in several microseconds), so
 // the stage is split where a full reduction over channels is needed:
-//   latent_mix_kernel   (block, 16-channel slice): steps 1-3, u in fp32 and bf16 to scratch;
+//   latent_mix_kernel   (block, 64-channel slice): steps 1-3, u in fp32 and bf16 to scratch
+//                       (inside a step it also finishes the previous pass's argmax);
 //   latent_gate_kernel  (row tile, 64 hidden units): step 4, s in bf16 to scratch;
 //   latent_down_kernel  (row tile, 64 channels): step 5, lat in bf16.
 // Each workgroup reads at most 64 KB of weights; row tiles of 64 rows (4 blocks) share weight
@@ -25,60 +26,134 @@
 #include "launch.hpp"
 #include "xpress_common.hpp"
 
+#include <limits.h>
+
 namespace xpress {
 
 namespace {
 
-// Steps 1-3 for one block and 16 channels c0..c0+15; one wave.
+// Steps 1-3 for one block and 64 channels (blockIdx.y); 4 waves. With `part` given (inside a
+// step), the block first finishes the previous pass: the partial winners of its readout rows
+// (range-major, `ntiles` <= 256 ranges) are reduced to the block's new tokens -- the work of the
+// argmax-reduce kernel for these rows, without its launch. Every channel slice of the block
+// reduces them (the same result); slice 0 writes them into blk and raises flags[pass-1] on a
+// change.
 template <int R>
-__global__ __launch_bounds__(64) void latent_mix_kernel(
-    const int64_t* __restrict__ blk, const int64_t* __restrict__ am1,
-    const float* __restrict__ xh, const uint16_t* __restrict__ w1,
+__global__ __launch_bounds__(256) void latent_mix_kernel(
+    const uint2* __restrict__ part, int ntiles, int rows, int64_t* __restrict__ blk,
+    const int64_t* __restrict__ am1, const float* __restrict__ xh, const uint16_t* __restrict__ w1,
     const uint16_t* __restrict__ in_proj, const uint16_t* __restrict__ mix_L, int B, int64_t V,
-    float* __restrict__ u32, uint16_t* __restrict__ u16, const int32_t* __restrict__ flags,
-    int pass) {
-  if (pass_skipped(flags, pass)) return;
-  __shared__ float s_x[16][17];
-  const int n = blockIdx.x;
-  const int c0 = blockIdx.y * 16;
-  const int lane = threadIdx.x, l16 = lane & 15, q4 = lane >> 4;
+    float* __restrict__ u32, uint16_t* __restrict__ u16, int32_t* __restrict__ flags, int pass) {
+  // fused: runs when the previous pass ran; plain: when this pass runs
+  if (part ? pass_skipped(flags, pass - 1) : pass_skipped(flags, pass)) return;
+  __shared__ int64_t s_tok[16];
+  __shared__ float s_x[16][65];
+  const int n = blockIdx.x, c0 = blockIdx.y * 64, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
 
-  // token of slot l16 (slot 0 reads am1, slot b reads blk[b-1]); slots >= B and ids outside
-  // [0, V) contribute a zero embedding
-  int64_t tok = -1;
-  if (l16 == 0) tok = am1[n];
-  else if (l16 < B) tok = blk[(int64_t)n * B + l16 - 1];
-  const bool live = tok >= 0 && tok < V;
-  const uint4* erow = reinterpret_cast<const uint4*>(w1 + (live ? tok : 0) * R);
-  const uint4* prow = reinterpret_cast<const uint4*>(in_proj + (int64_t)(c0 + l16) * 3 * R + 2 * R);
-
-  f32x4 acc = {0, 0, 0, 0};
+  // Mixer taps of this thread's channel c0 + lane for slots 4*wave .. 4*wave+3 (independent of
+  // the tokens, so loaded first): mix_L is [B, B, r], channel innermost, so a tap is one
+  // coalesced 2-byte load across the wave. Taps past B or above the diagonal are not used.
+  uint16_t tap[4][16];
+  {
+    const int bb = min(4 * wave, B - 1);
 #pragma unroll
-  for (int s = 0; s < R / 32; ++s) {
-    uint4 e = erow[4 * s + q4];
-    if (!live) e = make_uint4(0, 0, 0, 0);
-    acc = mfma16x16x32(as_bf16x8(e), as_bf16x8(prow[4 * s + q4]), acc);
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int b = min(bb + k, B - 1), jj = min(j, B - 1);
+        tap[k][j] = mix_L[(int64_t)(b * B + jj) * R + c0 + lane];
+      }
   }
-  // x for slot 4*q4 + v, channel c0 + l16
+
+  // step 0 (fused only): new tokens of the block; all 16 loads per thread are issued before the
+  // first merge (clamped repeats change nothing)
+  if (part) {
+    const int rb = tid >> 4, j = tid & 15;  // readout row rb of the block, range slice j
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    const uint2* pr = part + (int64_t)n * (B - 1) + min(rb, B - 2);
+    uint2 q[16];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int slot = 4 * q4 + v;
-    const float h = slot < B ? xh[((int64_t)n * B + slot) * R + c0 + l16] : 0.f;
-    s_x[slot][l16] = acc[v] + h;
+    for (int k = 0; k < 16; ++k) q[k] = pr[(int64_t)min(j + 16 * k, ntiles - 1) * rows];
+    if (rb < B - 1) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) argmax_merge(bv, bi, __uint_as_float(q[k].x), (int)q[k].y);
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) {  // the 16 slices are 16 consecutive lanes
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      argmax_merge(bv, bi, ov, oi);
+    }
+    if (j == 0 && rb < B - 1) {
+      const int64_t nv = (int64_t)bi;
+      if (blockIdx.y == 0) {
+        int64_t* slot = blk + (int64_t)n * B + 1 + rb;
+        if (*slot != nv) {
+          *slot = nv;
+          if (flags) __hip_atomic_store(flags + pass - 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      if (rb + 2 < B) s_tok[rb + 2] = nv;  // slot b reads blk[b-1]
+    }
+    if (tid == 0) {
+      s_tok[0] = am1[n];
+      s_tok[1] = blk[(int64_t)n * B];
+    }
+  } else if (tid < 16) {
+    s_tok[tid] = tid == 0 ? am1[n] : (tid < B ? blk[(int64_t)n * B + tid - 1] : -1);
   }
   __syncthreads();
-  // mixer: this lane -> channel c0 + l16, slots 4*q4 .. 4*q4+3
-  const int c = c0 + l16;
+
+  // steps 1-2: x[slot, c] = xh[slot, c] + sum_k P_e[c, k] w1[tok(slot), k]; wave w computes the
+  // 16 x 16 tile of channels c0 + 16w .. +15 (A: the 16 slots' embeddings, B: P_e rows)
+  {
+    const int64_t tok = l16 < B ? s_tok[l16] : -1;
+    const bool live = tok >= 0 && tok < V;
+    const uint4* erow = reinterpret_cast<const uint4*>(w1 + (live ? tok : 0) * R);
+    const int c = c0 + 16 * wave + l16;
+    const uint4* prow = reinterpret_cast<const uint4*>(in_proj + (int64_t)c * 3 * R + 2 * R);
+    bf16x8 a[R / 32], b[R / 32];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int b = 4 * q4 + v;
-    float u = 0.f;
-    if (b < B) {
-      const uint16_t* lrow = mix_L + ((int64_t)c * B + b) * B;
-      for (int j = 0; j <= b; ++j) u = fmaf(bf16_to_f32(lrow[j]), s_x[j][l16], u);
+    for (int s2 = 0; s2 < R / 32; ++s2) {
+      uint4 e = erow[4 * s2 + q4];
+      if (!live) e = make_uint4(0, 0, 0, 0);
+      a[s2] = as_bf16x8(e);
+      b[s2] = as_bf16x8(prow[4 * s2 + q4]);
     }
-    u32[((int64_t)n * 16 + b) * R + c] = u;
-    u16[((int64_t)n * 16 + b) * R + c] = f32_to_bf16(u);
+    float h[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int slot = 4 * q4 + v;
+      h[v] = slot < B ? xh[((int64_t)n * B + slot) * R + c] : 0.f;
+    }
+    f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int s2 = 0; s2 < R / 32; ++s2) acc = mfma16x16x32(a[s2], b[s2], acc);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s_x[4 * q4 + v][16 * wave + l16] = acc[v] + h[v];
+  }
+  __syncthreads();
+
+  // step 3: u[b, c] = sum_{j<=b} L[b, j, c] x[j, c]; thread -> channel c0 + lane, slots
+  // 4*wave .. 4*wave+3
+  {
+    float x[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = s_x[j][lane];
+    float* o32 = u32 + (int64_t)n * 16 * R + c0 + lane;
+    uint16_t* o16 = u16 + (int64_t)n * 16 * R + c0 + lane;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int b = 4 * wave + k;
+      float u = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        u = (j <= b && b < B) ? fmaf(bf16_to_f32(tap[k][j]), x[j], u) : u;
+      o32[(int64_t)b * R] = u;
+      o16[(int64_t)b * R] = f32_to_bf16(u);
+    }
   }
 }
 
@@ -99,18 +174,25 @@ __global__ __launch_bounds__(256) void latent_gate_kernel(
   f32x4 ag[G], au[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) ag[g] = au[g] = f32x4{0, 0, 0, 0};
+  // all operands are loaded before the first MFMA, so their latencies overlap
+  bf16x8 bg[R / 32], bu[R / 32], a[G][R / 32];
 #pragma unroll
   for (int s = 0; s < R / 32; ++s) {
-    const bf16x8 bg = as_bf16x8(grow[4 * s + q4]);
-    const bf16x8 bu = as_bf16x8(urow[4 * s + q4]);
+    bg[s] = as_bf16x8(grow[4 * s + q4]);
+    bu[s] = as_bf16x8(urow[4 * s + q4]);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int r = min(r0 + 16 * g + l16, nrows - 1);
-      const bf16x8 a = as_bf16x8(reinterpret_cast<const uint4*>(u16 + (int64_t)r * R)[4 * s + q4]);
-      ag[g] = mfma16x16x32(a, bg, ag[g]);
-      au[g] = mfma16x16x32(a, bu, au[g]);
+      a[g][s] = as_bf16x8(reinterpret_cast<const uint4*>(u16 + (int64_t)r * R)[4 * s + q4]);
     }
   }
+#pragma unroll
+  for (int s = 0; s < R / 32; ++s)
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      ag[g] = mfma16x16x32(a[g][s], bg[s], ag[g]);
+      au[g] = mfma16x16x32(a[g][s], bu[s], au[g]);
+    }
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -139,14 +221,27 @@ __global__ __launch_bounds__(256) void latent_down_kernel(
   f32x4 acc[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) acc[g] = f32x4{0, 0, 0, 0};
-  for (int s = 0; s < M / 32; ++s) {
-    const bf16x8 b = as_bf16x8(drow[4 * s + q4]);
+  // k in chunks of KC MFMA steps (M/32 >= 2): a chunk's loads are all issued before its MFMAs;
+  // indexes past the end are clamped and their MFMAs skipped
+  constexpr int KC = G == 1 ? 16 : 8;
+  const int ns = M / 32;
+  for (int s0 = 0; s0 < ns; s0 += KC) {
+    bf16x8 b[KC], a[G][KC];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int r = min(r0 + 16 * g + l16, nrows - 1);
-      const bf16x8 a = as_bf16x8(reinterpret_cast<const uint4*>(s16 + (int64_t)r * M)[4 * s + q4]);
-      acc[g] = mfma16x16x32(a, b, acc[g]);
+    for (int i = 0; i < KC; ++i) {
+      const int s = min(s0 + i, ns - 1);
+      b[i] = as_bf16x8(drow[4 * s + q4]);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int r = min(r0 + 16 * g + l16, nrows - 1);
+        a[g][i] = as_bf16x8(reinterpret_cast<const uint4*>(s16 + (int64_t)r * M)[4 * s + q4]);
+      }
     }
+#pragma unroll
+    for (int i = 0; i < KC; ++i)
+      if (s0 + i < ns)
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[g] = mfma16x16x32(a[g][i], b[i], acc[g]);
   }
 #pragma unroll
   for (int g = 0; g < G; ++g)
@@ -161,16 +256,17 @@ __global__ __launch_bounds__(256) void latent_down_kernel(
 }
 
 template <int R>
-hipError_t launch_r(const int64_t* blk, const int64_t* am1, const float* xh, const uint16_t* w1,
-                    const uint16_t* in_proj, const uint16_t* mix_L, const uint16_t* w_gate,
-                    const uint16_t* w_up, const uint16_t* w_down, int N, int B, int M, int64_t V,
-                    uint16_t* lat, void* scratch, const int32_t* flags, int pass, hipStream_t s) {
+hipError_t launch_r(const uint2* part, int ntiles, int64_t* blk, const int64_t* am1,
+                    const float* xh, const uint16_t* w1, const uint16_t* in_proj,
+                    const uint16_t* mix_L, const uint16_t* w_gate, const uint16_t* w_up,
+                    const uint16_t* w_down, int N, int B, int M, int64_t V, uint16_t* lat,
+                    void* scratch, int32_t* flags, int pass, hipStream_t s) {
   const int nrows = N * 16;
   float* u32 = static_cast<float*>(scratch);
   uint16_t* u16 = reinterpret_cast<uint16_t*>(u32 + (size_t)nrows * R);
   uint16_t* s16 = u16 + (size_t)nrows * R;
-  hipLaunchKernelGGL(latent_mix_kernel<R>, dim3(N, R / 16), dim3(64), 0, s, blk, am1, xh, w1,
-                     in_proj, mix_L, B, V, u32, u16, flags, pass);
+  hipLaunchKernelGGL(latent_mix_kernel<R>, dim3(N, R / 64), dim3(256), 0, s, part, ntiles, N * (B - 1),
+                     blk, am1, xh, w1, in_proj, mix_L, B, V, u32, u16, flags, pass);
   const bool wide = N >= 128;  // 4 blocks per workgroup: weights read once per 64 rows
   const int G = wide ? 4 : 1;
   dim3 g2((nrows + 16 * G - 1) / (16 * G), M / 64), g3((nrows + 16 * G - 1) / (16 * G), R / 64);
@@ -195,15 +291,15 @@ size_t latent_scratch_bytes(int N, int r, int M) {
   return nrows * r * 4 + nrows * r * 2 + nrows * M * 2;
 }
 
-hipError_t launch_latent(const int64_t* blk, const int64_t* am1, const float* xh,
-                         const uint16_t* w1, const uint16_t* in_proj, const uint16_t* mix_L,
-                         const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
-                         int N, int B, int r, int M, int64_t V, uint16_t* lat, void* scratch,
-                         const int32_t* flags, int pass, hipStream_t s) {
+hipError_t launch_latent(const uint2* part, int ntiles, int64_t* blk, const int64_t* am1,
+                         const float* xh, const uint16_t* w1, const uint16_t* in_proj,
+                         const uint16_t* mix_L, const uint16_t* w_gate, const uint16_t* w_up,
+                         const uint16_t* w_down, int N, int B, int r, int M, int64_t V,
+                         uint16_t* lat, void* scratch, int32_t* flags, int pass, hipStream_t s) {
   switch (r) {
-    case 64: return launch_r<64>(blk, am1, xh, w1, in_proj, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, scratch, flags, pass, s);
-    case 128: return launch_r<128>(blk, am1, xh, w1, in_proj, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, scratch, flags, pass, s);
-    case 256: return launch_r<256>(blk, am1, xh, w1, in_proj, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, scratch, flags, pass, s);
+    case 64: return launch_r<64>(part, ntiles, blk, am1, xh, w1, in_proj, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, scratch, flags, pass, s);
+    case 128: return launch_r<128>(part, ntiles, blk, am1, xh, w1, in_proj, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, scratch, flags, pass, s);
+    case 256: return launch_r<256>(part, ntiles, blk, am1, xh, w1, in_proj, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, scratch, flags, pass, s);
     default: return hipErrorInvalidValue;
   }
 }

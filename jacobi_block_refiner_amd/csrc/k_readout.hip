@@ -56,7 +56,7 @@ __device__ __forceinline__ void lds_copy16(const void* gbase, uint32_t off, uint
                :: "s"(lds_base), "v"(off), "s"(gbase) : "memory");
 }
 
-template <int R, int kNW, int RW>
+template <int R, int kNW, int RW, int NS>
 __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
     const uint16_t* __restrict__ lat, const uint16_t* __restrict__ w2,
     const uint16_t* __restrict__ base, int64_t ld, int rows, int V, int nvr, int n_rc,
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
   constexpr int DI = WI + BI;
   static_assert(BCH % (64 * kNW) == 0, "base stage must split evenly over the waves");
 
-  __shared__ uint4 s_stage[3][SCH];
+  __shared__ uint4 s_stage[NS][SCH];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -224,16 +224,18 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
     bi[k] = gt ? 32 * t + 16 * half + se : bi[k];
   };
 
-  // prologue: steps t0 and t0+1 in flight
-  copy_step(t0, 0);
-  copy_step(min(t0 + 1, t1 - 1), 1);
+  // prologue: steps t0 .. t0+NS-2 in flight
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) copy_step(min(t0 + i, t1 - 1), i);
+  constexpr int VW = (NS - 2) * DI;  // copies allowed in flight past step t
   int st = 0;
   for (int t = t0; t < t1; ++t) {
-    // this wave's copies of step t are done (those of step t+1 may still run); after the
+    // this wave's copies of step t are done (those of later steps may still run); after the
     // barrier every wave's are, and every wave has finished step t-1 (its stage is free)
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (DI & 15) | ((DI >> 4) << 14));  // vmcnt(DI)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (VW & 15) | ((VW >> 4) << 14));  // vmcnt(VW)
     __syncthreads();
-    copy_step(min(t + 2, t1 - 1), st == 0 ? 2 : st - 1);  // past the range end: refetches (L2)
+    // into the stage of step t-1; past the range end this refetches the last step (L2 hits)
+    copy_step(min(t + NS - 1, t1 - 1), st == 0 ? NS - 1 : st - 1);
     if (active) {
       const uint4* sp = s_stage[st];
       f32x16 acc[RW];
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
 #pragma unroll
       for (int k = 0; k < RW; ++k) epilogue(t, k, acc[k]);
     }
-    st = st == 2 ? 0 : st + 1;
+    st = st == NS - 1 ? 0 : st + 1;
   }
   // drain the trailing copies before the workgroup's LDS can be handed to another workgroup
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -335,14 +337,14 @@ int device_cus() {
   return cus;
 }
 
-template <int R, int NW, int RW>
+template <int R, int NW, int RW, int NS>
 hipError_t launch_partial_t(const uint16_t* lat, const uint16_t* w2, const uint16_t* base,
                             int64_t ld, int rows, int64_t V, uint2* part, const int32_t* flags,
                             int pass, hipStream_t s) {
   const int nvr = readout_tiles(V);
   constexpr int CH = NW * RW * 32;
   const int n_rc = (rows + CH - 1) / CH;
-  hipLaunchKernelGGL((readout_partial_kernel<R, NW, RW>), dim3((unsigned)(nvr * n_rc)), dim3(64 * NW),
+  hipLaunchKernelGGL((readout_partial_kernel<R, NW, RW, NS>), dim3((unsigned)(nvr * n_rc)), dim3(64 * NW),
                      0, s, lat, w2, base, ld, rows, (int)V, nvr, n_rc, part, flags, pass);
   return hipGetLastError();
 }
@@ -350,14 +352,14 @@ hipError_t launch_partial_t(const uint16_t* lat, const uint16_t* w2, const uint1
 // Row chunk shape: up to 256 rows, 8 waves of one 32-row tile each; more rows, 8 waves of two
 // 32-row tiles each (512 rows per chunk), so each w2 fragment read from LDS feeds two MFMAs.
 // (Four waves of four tiles, or sixteen of one, measured slower at 480 rows.)
-template <int NW, int RW>
+template <int NW, int RW, int NS>
 hipError_t launch_partial_shape(const uint16_t* lat, const uint16_t* w2, const uint16_t* base,
                                 int64_t ld, int rows, int64_t V, int r, uint2* part,
                                 const int32_t* flags, int pass, hipStream_t s) {
   switch (r) {
-    case 64: return launch_partial_t<64, NW, RW>(lat, w2, base, ld, rows, V, part, flags, pass, s);
-    case 128: return launch_partial_t<128, NW, RW>(lat, w2, base, ld, rows, V, part, flags, pass, s);
-    case 256: return launch_partial_t<256, NW, RW>(lat, w2, base, ld, rows, V, part, flags, pass, s);
+    case 64: return launch_partial_t<64, NW, RW, NS>(lat, w2, base, ld, rows, V, part, flags, pass, s);
+    case 128: return launch_partial_t<128, NW, RW, NS>(lat, w2, base, ld, rows, V, part, flags, pass, s);
+    case 256: return launch_partial_t<256, NW, RW, NS>(lat, w2, base, ld, rows, V, part, flags, pass, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -372,8 +374,8 @@ int readout_tiles(int64_t V) {
 hipError_t launch_readout_partial(const uint16_t* lat, const uint16_t* w2, const uint16_t* base,
                                   int64_t ld, int rows, int64_t V, int r, uint2* part,
                                   const int32_t* flags, int pass, hipStream_t s) {
-  if (rows <= 256) return launch_partial_shape<8, 1>(lat, w2, base, ld, rows, V, r, part, flags, pass, s);
-  return launch_partial_shape<8, 2>(lat, w2, base, ld, rows, V, r, part, flags, pass, s);
+  if (rows <= 256) return launch_partial_shape<8, 1, 3>(lat, w2, base, ld, rows, V, r, part, flags, pass, s);
+  return launch_partial_shape<8, 2, 3>(lat, w2, base, ld, rows, V, r, part, flags, pass, s);
 }
 
 hipError_t launch_argmax_reduce(const uint2* part, int ntiles, int rows, int B, int64_t* blk,

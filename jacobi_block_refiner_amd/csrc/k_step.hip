@@ -73,10 +73,10 @@ __global__ void fold_mixer_kernel(const uint16_t* __restrict__ raw, int r, int B
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t n = (int64_t)r * B * B;
   if (i >= n) return;
-  const int j = (int)(i % B), b = (int)((i / B) % B);
+  const int j = (int)(i % B), b = (int)((i / B) % B), c = (int)(i / ((int64_t)B * B));
   float v = (j <= b) ? bf16_to_f32(raw[i]) : 0.f;
   if (j == b) v += 1.f;
-  mix_L[i] = f32_to_bf16(v);
+  mix_L[((int64_t)b * B + j) * r + c] = f32_to_bf16(v);  // stored [B, B, r]
 }
 
 __global__ void set_anchor_kernel(const int64_t* anchor, int N, int B, int64_t* blk) {

@@ -28,11 +28,14 @@ hipError_t launch_initial_block(const uint16_t* base, int64_t ld, const int64_t*
                                 int B, int64_t V, int64_t* blk, hipStream_t s);
 // K4: latent stage of one pass (three kernels); scratch holds u (fp32 and bf16) and s (bf16).
 size_t latent_scratch_bytes(int N, int r, int M);
-hipError_t launch_latent(const int64_t* blk, const int64_t* am1, const float* xh,
-                         const uint16_t* w1, const uint16_t* in_proj, const uint16_t* mix_L,
-                         const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
-                         int N, int B, int r, int M, int64_t V, uint16_t* lat, void* scratch,
-                         const int32_t* flags, int pass, hipStream_t s);
+// Steps 1-5 of the latent. With part != nullptr (inside a step, pass >= 1) the mix kernel first
+// reduces the previous pass's range-major partials into blk for its block and raises
+// flags[pass-1] on a change; blk is then written. Otherwise blk is only read.
+hipError_t launch_latent(const uint2* part, int ntiles, int64_t* blk, const int64_t* am1,
+                         const float* xh, const uint16_t* w1, const uint16_t* in_proj,
+                         const uint16_t* mix_L, const uint16_t* w_gate, const uint16_t* w_up,
+                         const uint16_t* w_down, int N, int B, int r, int M, int64_t V,
+                         uint16_t* lat, void* scratch, int32_t* flags, int pass, hipStream_t s);
 // K5: per (vocab tile, row) partial argmax of base + lat . w2^T; part: [rows, ntiles].
 hipError_t launch_readout_partial(const uint16_t* lat, const uint16_t* w2, const uint16_t* base,
                                   int64_t ld, int rows, int64_t V, int r, uint2* part,

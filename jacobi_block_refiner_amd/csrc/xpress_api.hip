@@ -211,9 +211,9 @@ xpress_status xpress_latent_pass(const xpress_weights* w, const int64_t* blk, co
   const size_t need = xpress::latent_scratch_bytes(N, w->r, w->M);
   if (ws_bytes < need)
     return fail(XPRESS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed for N=%d", ws_bytes, need, N);
-  XP_TRY(xpress::launch_latent(blk, am1, xh, w->w1, w->in_proj, w->mix_L, w->w_gate, w->w_up,
-                               w->w_down, N, w->B, w->r, w->M, w->V, lat, ws, nullptr, 0,
-                               reinterpret_cast<hipStream_t>(stream)),
+  XP_TRY(xpress::launch_latent(nullptr, 0, const_cast<int64_t*>(blk), am1, xh, w->w1, w->in_proj,
+                               w->mix_L, w->w_gate, w->w_up, w->w_down, N, w->B, w->r, w->M, w->V,
+                               lat, ws, nullptr, 0, reinterpret_cast<hipStream_t>(stream)),
          "latent");
   return XPRESS_OK;
 }
@@ -375,9 +375,13 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
   if (stop) XP_TRY(xpress::launch_flags_reset(pf, K + 1, s), "flags reset");
   uint2* part = at<uint2>(ws, L.part);
   const int ntiles = xpress::readout_tiles(V);
+  // Full vocabulary: the argmax reduce of pass p-1 runs inside pass p's first latent kernel (each
+  // block finishes its own rows); only the last pass's reduce is a launch of its own.
   for (int p = 0; p < K; ++p) {
-    XP_TRY(xpress::launch_latent(blk, am1, xh, w->w1, w->in_proj, w->mix_L, w->w_gate, w->w_up,
-                                 w->w_down, N, B, r, w->M, V, lat, lscr, pf, p, s),
+    const uint2* prev = (c == 0 && p > 0) ? part : nullptr;
+    XP_TRY(xpress::launch_latent(prev, ntiles, blk, am1, xh, w->w1, w->in_proj, w->mix_L,
+                                 w->w_gate, w->w_up, w->w_down, N, B, r, w->M, V, lat, lscr, pf,
+                                 p, s),
            "latent");
     if (c > 0) {
       XP_TRY(xpress::launch_topc_readout(lat, w2c, base_c, cand, rows, B, r, c, blk, nullptr, pf, p, s),
@@ -385,10 +389,11 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
     } else {
       XP_TRY(xpress::launch_readout_partial(lat, w->w2, base, base_ld, rows, V, r, part, pf, p, s),
              "readout");
-      XP_TRY(xpress::launch_argmax_reduce(part, ntiles, rows, B, blk, nullptr, pf, p, s),
-             "argmax reduce");
     }
   }
+  if (c == 0 && K > 0)
+    XP_TRY(xpress::launch_argmax_reduce(part, ntiles, rows, B, blk, nullptr, pf, K - 1, s),
+           "argmax reduce");
   if (passes_run) XP_TRY(xpress::launch_count_passes(pf, K, stop ? 1 : 0, passes_run, s), "count passes");
   return XPRESS_OK;
 }

@@ -108,7 +108,8 @@ def _bf16(t: torch.Tensor, name: str) -> torch.Tensor:
 
 @dataclass
 class Weights:
-    """Device bf16 weights of one refiner head, ``nn.Linear`` layouts; ``mix_L`` is folded."""
+    """Device bf16 weights of one refiner head, ``nn.Linear`` layouts; ``mix_L`` is folded and
+    stored [B, B, r]."""
 
     w1: torch.Tensor
     down_h: torch.Tensor
@@ -149,9 +150,10 @@ def alloc_workspace(n_max: int, B: int, r: int, V: int, C: int, k_max: int, devi
 
 
 def fold_mixer(raw: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """raw: [r, B, B] bf16 -> folded mixer [B, B, r] (channel innermost)."""
     raw = _bf16(raw, "raw").contiguous()
     r, B, _ = raw.shape
-    out = torch.empty_like(raw) if out is None else out
+    out = torch.empty(B, B, r, dtype=raw.dtype, device=raw.device) if out is None else out
     _check(lib().xpress_fold_mixer(_ptr(raw), r, B, _ptr(out), _stream()))
     return out
 

@@ -53,8 +53,9 @@ def test_fold_mixer_bit_exact():
     for r, B in ((64, 4), (256, 16)):
         raw = synth.bf16_round(rng.standard_normal((r, B, B)).astype(np.float32) * 0.05)
         got = xpress.fold_mixer(upload.bf16_tensor(raw)).float().cpu().numpy()
+        assert got.shape == (B, B, r)  # stored channel innermost
         inp = replace(synth.make_inputs(1), raw_L=raw)
-        assert np.array_equal(got.astype(np.float64), oracle_mixer(inp))
+        assert np.array_equal(got.transpose(2, 0, 1).astype(np.float64), oracle_mixer(inp))
 
 
 @pytest.mark.parametrize("V", [5003, 8192])
