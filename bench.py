@@ -3,6 +3,8 @@
 A step is one xpress_jacobi_step over the synthetic 32-block, full-vocabulary workload (N=32
 blocks of B=16 slots, r=256, H=4096, M=512, V=151936): hidden cache, starting block from the base
 argmax, then K=15 Jacobi passes (latent + readout GEMM + fused add/argmax), inputs resident in HBM.
+The step is recorded once as a HIP graph (xpress_jacobi_step_graph) and replayed, one launch per
+step; the eager (kernel-by-kernel) rate is reported beside it, and both must give the same draft.
 
 Prints one JSON line. `value` is Jacobi passes per second of whole steps (per-step setup
 included). Also reported:
@@ -99,24 +101,35 @@ def main() -> int:
         xpress.jacobi_step(w, h, base, anchor, am1, blk, K=K, C=wl.C,
                            flags=xpress.INIT_FROM_BASE, ws=ws)
 
-    log(f"warmup {args.warmup} steps")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"timing {args.steps} steps of {K} passes")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = e0.elapsed_time(e1)
-    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
-    passes_per_s = K / (ms_per_step / 1e3)
+    def time_steps(fn, label):
+        log(f"{label}: warmup {args.warmup} steps")
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        log(f"{label}: timing {args.steps} steps of {K} passes")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return max(e0.elapsed_time(e1), wall * 1e3) / args.steps
+
+    eager_ms = time_steps(step, "eager")
+    draft_eager = blk.cpu().numpy()
+    # The same step recorded once as a HIP graph and replayed (one launch per step).
+    graph = xpress.StepGraph(w, h, base, anchor, am1, blk, K=K, C=wl.C,
+                             flags=xpress.INIT_FROM_BASE, ws=ws)
+    graph_ms = time_steps(graph.launch, "graph")
     draft = blk.cpu().numpy()
+    graph.close()
+    if not np.array_equal(draft, draft_eager):
+        raise SystemExit("graph replay and eager step disagree")
+    ms_per_step = graph_ms
+    passes_per_s = K / (ms_per_step / 1e3)
 
     # Per-kernel timing with HIP events on the launch stream (the current torch stream), same
     # inputs and launch configuration as inside the step.
@@ -208,6 +221,8 @@ def main() -> int:
         },
         "extra": {
             "rows_x_V_scored_per_s": round(rows * wl.V * passes_per_s, 1),
+            "eager_ms_per_step": round(eager_ms, 4),
+            "eager_passes_per_s": round(K / (eager_ms / 1e3), 2),
             "loop_only_passes_per_s": round(K / (loop_us * 1e-6), 1),
             "readout_mfma_tflops": round(mfma_tflops, 1),
             "readout_mfma_frac_of_bf16_peak": round(mfma_tflops / MFMA_BF16_PEAK_TFLOPS, 4),

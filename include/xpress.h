@@ -183,6 +183,26 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
                                  uint32_t flags, int64_t* blk, int32_t* passes_run, void* ws,
                                  size_t ws_bytes, xpress_stream stream);
 
+/* A draft step recorded once as a HIP graph and replayed with one launch (the pages capture
+ * the pass loop in a graph with fixed buffer addresses: qwen3_xpress page, jacobi_refine_greedy;
+ * kernels page, module docstring). xpress_jacobi_step_graph checks the arguments exactly as
+ * xpress_jacobi_step does, then records that step's kernels on a private stream into a graph and
+ * instantiates it; nothing runs. *graph receives an opaque handle. Every xpress_graph_launch
+ * enqueues the whole step on `stream` with the recorded pointers and sizes, so the buffers must
+ * stay allocated, and their contents are read at launch time (new h, base, anchor, am1 values are
+ * picked up; blk is rewritten). With XPRESS_STOP_AT_FIXED_POINT the passes after convergence
+ * exit on the device, as in the eager call. Creating a graph allocates host-side objects; the
+ * launch allocates nothing. xpress_graph_destroy releases the handle (NULL is a no-op). Errors:
+ * those of xpress_jacobi_step, XPRESS_ERR_HIP if recording or instantiation fails. */
+xpress_status xpress_jacobi_step_graph(const xpress_weights* w, const xpress_bf16* h,
+                                       const xpress_bf16* base, int64_t base_ld,
+                                       const int64_t* anchor, const int64_t* am1, int32_t N,
+                                       int32_t K, int32_t C, uint32_t flags, int64_t* blk,
+                                       int32_t* passes_run, void* ws, size_t ws_bytes,
+                                       void** graph);
+xpress_status xpress_graph_launch(void* graph, xpress_stream stream);
+xpress_status xpress_graph_destroy(void* graph);
+
 /* Message of the last non-OK status returned on the calling thread ("" if none). */
 const char* xpress_last_error(void);
 

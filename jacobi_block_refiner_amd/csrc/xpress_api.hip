@@ -398,4 +398,52 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
   return XPRESS_OK;
 }
 
+xpress_status xpress_jacobi_step_graph(const xpress_weights* w, const xpress_bf16* h,
+                                       const xpress_bf16* base, int64_t base_ld,
+                                       const int64_t* anchor, const int64_t* am1, int32_t N,
+                                       int32_t K, int32_t C, uint32_t flags, int64_t* blk,
+                                       int32_t* passes_run, void* ws, size_t ws_bytes,
+                                       void** graph) {
+  XP_PTR(graph);
+  *graph = nullptr;
+  hipStream_t cs = nullptr;
+  XP_TRY(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking), "capture stream");
+  hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    (void)hipStreamDestroy(cs);
+    return fail(XPRESS_ERR_HIP, "begin capture: %s", hipGetErrorString(e));
+  }
+  const xpress_status st = xpress_jacobi_step(w, h, base, base_ld, anchor, am1, N, K, C, flags,
+                                              blk, passes_run, ws, ws_bytes,
+                                              reinterpret_cast<xpress_stream>(cs));
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(cs, &g);
+  (void)hipStreamDestroy(cs);
+  if (st != XPRESS_OK) {
+    if (g) (void)hipGraphDestroy(g);
+    return st;
+  }
+  if (e != hipSuccess) return fail(XPRESS_ERR_HIP, "end capture: %s", hipGetErrorString(e));
+  hipGraphExec_t ge = nullptr;
+  e = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if (e != hipSuccess) return fail(XPRESS_ERR_HIP, "instantiate: %s", hipGetErrorString(e));
+  *graph = ge;
+  return XPRESS_OK;
+}
+
+xpress_status xpress_graph_launch(void* graph, xpress_stream stream) {
+  XP_PTR(graph);
+  XP_TRY(hipGraphLaunch(reinterpret_cast<hipGraphExec_t>(graph),
+                        reinterpret_cast<hipStream_t>(stream)),
+         "graph launch");
+  return XPRESS_OK;
+}
+
+xpress_status xpress_graph_destroy(void* graph) {
+  if (!graph) return XPRESS_OK;
+  XP_TRY(hipGraphExecDestroy(reinterpret_cast<hipGraphExec_t>(graph)), "graph destroy");
+  return XPRESS_OK;
+}
+
 }  // extern "C"

@@ -71,6 +71,10 @@ def lib() -> ctypes.CDLL:
             "xpress_readout_argmax_topc": [P, P, P, P, i32, i32, i32, i32, P, P, P],
             "xpress_jacobi_step": [W, P, P, i64, P, P, i32, i32, i32, ctypes.c_uint32, P, P, P,
                                    sz, P],
+            "xpress_jacobi_step_graph": [W, P, P, i64, P, P, i32, i32, i32, ctypes.c_uint32, P, P,
+                                         P, sz, ctypes.POINTER(ctypes.c_void_p)],
+            "xpress_graph_launch": [P, P],
+            "xpress_graph_destroy": [P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -251,3 +255,38 @@ def jacobi_step(w: Weights, h, base, anchor, am1, blk, *, K: int, C: int = 0,
                                     _ptr(am1), N, K, C, flags, _ptr(blk), _ptr(passes_run),
                                     _ptr(ws), ws.numel() * ws.element_size(), _stream()))
     return blk
+
+
+class StepGraph:
+    """A draft step recorded once as a HIP graph (``xpress_jacobi_step_graph``); ``launch()``
+    replays the whole step on the current stream with one call. The tensors given at creation are
+    kept referenced: the graph reads and writes them in place on every launch."""
+
+    def __init__(self, w: Weights, h, base, anchor, am1, blk, *, K: int, C: int = 0,
+                 flags: int = INIT_FROM_BASE, ws: torch.Tensor, passes_run=None):
+        s = w.struct()
+        _bf16(base, "base")
+        assert base.stride(1) == 1
+        self._keep = (w, h, base, anchor, am1, blk, ws, passes_run)
+        self._handle = ctypes.c_void_p()
+        N = blk.shape[0]
+        _check(lib().xpress_jacobi_step_graph(
+            ctypes.byref(s), _ptr(_bf16(h, "h")), ctypes.c_void_p(base.data_ptr()),
+            base.stride(0), _ptr(anchor), _ptr(am1), N, K, C, flags, _ptr(blk), _ptr(passes_run),
+            _ptr(ws), ws.numel() * ws.element_size(), ctypes.byref(self._handle)))
+
+    def launch(self) -> None:
+        if not self._handle:
+            raise RuntimeError("graph was closed")
+        _check(lib().xpress_graph_launch(self._handle, _stream()))
+
+    def close(self) -> None:
+        if self._handle:
+            _check(lib().xpress_graph_destroy(self._handle))
+            self._handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
