@@ -90,8 +90,22 @@ __global__ __launch_bounds__(256) void hidden_reduce_kernel(const float4* __rest
                                                             float4* __restrict__ hdg) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
+  // splits in ascending order (fixed summation order); 8 loads in flight at a time
   float4 v = part[i];
-  for (int sp = 1; sp < nsplit; ++sp) {
+  int sp = 1;
+  for (; sp + 8 <= nsplit; sp += 8) {
+    float4 u[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) u[j] = part[(sp + j) * n4 + i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v.x += u[j].x;
+      v.y += u[j].y;
+      v.z += u[j].z;
+      v.w += u[j].w;
+    }
+  }
+  for (; sp < nsplit; ++sp) {
     const float4 u = part[sp * n4 + i];
     v.x += u.x;
     v.y += u.y;

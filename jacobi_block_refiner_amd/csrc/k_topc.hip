@@ -190,19 +190,26 @@ __global__ __launch_bounds__(256) void topc_gather_kernel(const int64_t* __restr
 }
 
 // One workgroup per draft row. Lanes form groups of G = R/8 that each hold one candidate's w2c
-// row (16 bytes per lane); the group's partial dot products are summed with xor shuffles.
+// row (16 bytes per lane, so a wave reads 1 KiB of contiguous rows per load); the group's
+// partial dot products are summed with xor shuffles. Each lane keeps U loads in flight per round
+// (the gathered rows stream once per pass: the kernel is bound by how many bytes are in flight).
+// The winner is tracked by candidate index -- cand is ascending, so the lowest index is the lowest
+// vocabulary id -- and translated to its id once at the end.
 template <int R>
 __global__ __launch_bounds__(256) void topc_readout_kernel(
     const uint16_t* __restrict__ lat, const uint16_t* __restrict__ w2c,
     const uint16_t* __restrict__ base_c, const int64_t* __restrict__ cand, int B, int c,
     int64_t* __restrict__ blk, int32_t* changed, int32_t* flags, int pass) {
   if (pass_skipped(flags, pass)) return;
-  constexpr int G = R / 8;
-  constexpr int CPW = 64 / G;
+  constexpr int G = R / 8;        // lanes per candidate
+  constexpr int CPW = 64 / G;     // candidates per wave per load
+  constexpr int U = 8;            // loads in flight per lane
+  constexpr int CPR = 4 * CPW * U;  // candidates per workgroup round
   __shared__ float s_v[4];
   __shared__ int s_i[4];
   const int p = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane % G, sub = lane / G;
+  const uint16_t* bc = base_c + (int64_t)p * c;
   float lv[8];
   {
     const uint4 u = reinterpret_cast<const uint4*>(lat + (int64_t)p * R)[q];
@@ -210,46 +217,51 @@ __global__ __launch_bounds__(256) void topc_readout_kernel(
     lv[4] = bf16_lo(u.z); lv[5] = bf16_hi(u.z); lv[6] = bf16_lo(u.w); lv[7] = bf16_hi(u.w);
   }
   const uint4* wrow = reinterpret_cast<const uint4*>(w2c + (int64_t)p * c * R);
-  const uint16_t* bc = base_c + (int64_t)p * c;
-  const int64_t* cd = cand + (int64_t)p * c;
   float bv = -INFINITY;
-  int bi = INT_MAX;
-  const int step = 4 * CPW;
-  for (int k0 = 0; k0 < c; k0 += step) {
-    const int k = k0 + wave * CPW + sub;
-    float d = 0.f;
-    if (k < c) {
-      const uint4 u = ld_nt16(wrow + (int64_t)k * G + q);
-      d = lv[0] * bf16_lo(u.x);
-      d = fmaf(lv[1], bf16_hi(u.x), d);
-      d = fmaf(lv[2], bf16_lo(u.y), d);
-      d = fmaf(lv[3], bf16_hi(u.y), d);
-      d = fmaf(lv[4], bf16_lo(u.z), d);
-      d = fmaf(lv[5], bf16_hi(u.z), d);
-      d = fmaf(lv[6], bf16_lo(u.w), d);
-      d = fmaf(lv[7], bf16_hi(u.w), d);
+  int bk = INT_MAX;
+  for (int k0 = 0; k0 < c; k0 += CPR) {
+    uint4 u[U];
+    uint16_t bk16[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int k = min(k0 + (j * 4 + wave) * CPW + sub, c - 1);  // past c: repeats, masked
+      u[j] = wrow[(int64_t)k * G + q];
+      bk16[j] = bc[k];
     }
 #pragma unroll
-    for (int off = G / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off);
-    if (q == 0 && k < c) argmax_merge(bv, bi, bf16_to_f32(bc[k]) + d, (int)cd[k]);
+    for (int j = 0; j < U; ++j) {
+      float d = lv[0] * bf16_lo(u[j].x);
+      d = fmaf(lv[1], bf16_hi(u[j].x), d);
+      d = fmaf(lv[2], bf16_lo(u[j].y), d);
+      d = fmaf(lv[3], bf16_hi(u[j].y), d);
+      d = fmaf(lv[4], bf16_lo(u[j].z), d);
+      d = fmaf(lv[5], bf16_hi(u[j].z), d);
+      d = fmaf(lv[6], bf16_lo(u[j].w), d);
+      d = fmaf(lv[7], bf16_hi(u[j].w), d);
+#pragma unroll
+      for (int off = G / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+      const int k = k0 + (j * 4 + wave) * CPW + sub;
+      argmax_merge(bv, bk, k < c ? bf16_to_f32(bk16[j]) + d : -INFINITY, k);
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     const float ov = __shfl_xor(bv, off);
-    const int oi = __shfl_xor(bi, off);
-    argmax_merge(bv, bi, ov, oi);
+    const int oi = __shfl_xor(bk, off);
+    argmax_merge(bv, bk, ov, oi);
   }
   if (lane == 0) {
     s_v[wave] = bv;
-    s_i[wave] = bi;
+    s_i[wave] = bk;
   }
   __syncthreads();
   if (tid == 0) {
-    for (int w = 1; w < 4; ++w) argmax_merge(bv, bi, s_v[w], s_i[w]);
+    for (int w = 1; w < 4; ++w) argmax_merge(bv, bk, s_v[w], s_i[w]);
+    const int64_t id = cand[(int64_t)p * c + bk];
     const int n = p / (B - 1), b = 1 + p % (B - 1);
     int64_t* slot = blk + (int64_t)n * B + b;
-    if (*slot != (int64_t)bi) {
-      *slot = bi;
+    if (*slot != id) {
+      *slot = id;
       if (changed) __hip_atomic_store(changed, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (flags) __hip_atomic_store(flags + pass, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
