@@ -71,15 +71,12 @@ __device__ __forceinline__ void load8_keys(const uint16_t* row, int64_t id0, int
   }
 }
 
-__global__ __launch_bounds__(256) void topc_select_kernel(const uint16_t* __restrict__ base,
-                                                          int64_t ld, int64_t V, int c,
-                                                          int64_t* __restrict__ cand,
-                                                          uint16_t* __restrict__ base_c) {
-  __shared__ uint32_t s_hist[256];
-  __shared__ int s_tmp[4];
-  __shared__ uint32_t s_par[4];
-  const int p = blockIdx.x, tid = threadIdx.x;
-  const uint16_t* row = base + (int64_t)p * ld;
+// Exact selection of one row by a two-level radix select over the whole row, then an ordered
+// compaction. Called by the whole workgroup (256 threads).
+__device__ void select_row_exact(const uint16_t* __restrict__ row, int64_t V, int c,
+                                 int64_t* __restrict__ out_id, uint16_t* __restrict__ out_b,
+                                 uint32_t* s_hist, int* s_tmp, uint32_t* s_par) {
+  const int tid = threadIdx.x;
   const int64_t nchunk = (V + 7) / 8;
 
   // pass 1: high byte histogram
@@ -135,8 +132,6 @@ __global__ __launch_bounds__(256) void topc_select_kernel(const uint16_t* __rest
 
   // pass 3: ordered compaction, 2048 ids per round, ascending id order
   int eq_carry = 0, sel_carry = 0;
-  int64_t* out_id = cand + (int64_t)p * c;
-  uint16_t* out_b = base_c + (int64_t)p * c;
   for (int64_t id_base = 0; id_base < V && sel_carry < c; id_base += 2048) {
     const int64_t id0 = id_base + (int64_t)tid * 8;
     uint32_t key[8];
@@ -174,6 +169,207 @@ __global__ __launch_bounds__(256) void topc_select_kernel(const uint16_t* __rest
       }
     eq_carry += eq_total;
     sel_carry += sel_total;
+  }
+}
+
+// Fast path for c <= 1024, exact. Each thread splits the ids it visits (in increasing order) into
+// at most 8 groups and records each group's largest key: at most 2048 group maxima, which are
+// distinct elements of the row. t0 = the c-th largest of them is then at most the c-th largest
+// key of the row, so every element of the answer -- ties at the boundary included -- has a key
+// >= t0. A second pass appends the elements with key >= t0 to an LDS buffer (at least c of them;
+// if more than the buffer holds, the row falls back to select_row_exact), and the exact selection
+// runs on the buffer: threshold by radix select, the boundary ties by id rank, and each winner
+// written at its rank by id (ascending id order).
+constexpr int kBuf = 2048;
+constexpr int kEq = 512;
+__device__ __forceinline__ uint32_t radix_kth(const uint32_t* keys, int n, int k, uint32_t* s_hist,
+                                              uint32_t* s_par, uint32_t* above_out) {
+  // keys: 17-bit (key + 1, 0 = empty); returns the k-th largest non-empty key and sets
+  // *above_out = number of keys strictly above it. Whole workgroup.
+  const int tid = threadIdx.x;
+  s_hist[tid] = 0;
+  if (tid < 256) s_hist[256 + tid] = 0;
+  __syncthreads();
+  for (int j = tid; j < n; j += 256) {
+    const uint32_t k1 = keys[j];
+    if (k1) atomicAdd(&s_hist[k1 >> 8], 1u);  // 0x10000 >> 8 = 256: bin 256 only for key 0xffff+1
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t acc = 0;
+    int hb = 0;
+    for (int b = 256; b >= 0; --b) {
+      if (acc + s_hist[b] >= (uint32_t)k) { hb = b; break; }
+      acc += s_hist[b];
+    }
+    s_par[0] = (uint32_t)hb;
+    s_par[1] = acc;
+  }
+  __syncthreads();
+  const uint32_t h1 = s_par[0], a1 = s_par[1];
+  s_hist[tid] = 0;
+  __syncthreads();
+  for (int j = tid; j < n; j += 256) {
+    const uint32_t k1 = keys[j];
+    if (k1 && (k1 >> 8) == h1) atomicAdd(&s_hist[k1 & 0xffu], 1u);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t rem = (uint32_t)k - a1;
+    uint32_t acc = 0;
+    int lb = 0;
+    for (int b = 255; b >= 0; --b) {
+      if (acc + s_hist[b] >= rem) { lb = b; break; }
+      acc += s_hist[b];
+    }
+    s_par[2] = (h1 << 8) | (uint32_t)lb;
+    s_par[3] = a1 + acc;
+  }
+  __syncthreads();
+  const uint32_t t = s_par[2];
+  *above_out = s_par[3];
+  __syncthreads();
+  return t;
+}
+
+__global__ __launch_bounds__(256) void topc_select_kernel(const uint16_t* __restrict__ base,
+                                                          int64_t ld, int64_t V, int c,
+                                                          int64_t* __restrict__ cand,
+                                                          uint16_t* __restrict__ base_c) {
+  __shared__ uint32_t s_hist[512];
+  __shared__ int s_tmp[4];
+  __shared__ uint32_t s_par[4];
+  __shared__ uint32_t s_key[kBuf];  // key + 1 (0: empty)
+  __shared__ int s_id[kBuf];
+  __shared__ int s_eq[kEq];         // ids of the boundary ties
+  __shared__ int s_sel[1024];       // ids of the winners
+  __shared__ int s_cnt[2];
+  const int p = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const uint16_t* row = base + (int64_t)p * ld;
+  int64_t* out_id = cand + (int64_t)p * c;
+  uint16_t* out_b = base_c + (int64_t)p * c;
+  const int64_t nchunk = (V + 7) / 8;
+  if (c > 1024 || nchunk > (int64_t)256 * 1024) {
+    select_row_exact(row, V, c, out_id, out_b, s_hist, s_tmp, s_par);
+    return;
+  }
+  // 1. group maxima: thread tid visits chunks tid + 256 i; groups of gv visits (<= 8 groups)
+  const int nv_max = (int)((nchunk + 255) / 256);
+  const int gv = (nv_max + 7) / 8;
+  {
+    uint32_t gm = 0;
+    int g = 0, inside = 0;
+    for (int64_t q = tid; q < nchunk; q += 256) {
+      uint32_t key[8];
+      uint16_t bits[8];
+      load8_keys(row, q * 8, V, key, bits);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gm = max(gm, key[e] <= 0xffffu ? key[e] + 1 : 0u);
+      if (++inside == gv) {
+        s_key[tid * 8 + g] = gm;
+        ++g;
+        inside = 0;
+        gm = 0;
+      }
+    }
+    if (inside) s_key[tid * 8 + g++] = gm;
+    for (; g < 8; ++g) s_key[tid * 8 + g] = 0;
+  }
+  if (tid == 0) s_cnt[0] = 0;
+  __syncthreads();
+  // 2. t0: the c-th largest group maximum (every group maximum is non-empty if its group had an
+  // id below V; with fewer than c of them t0 is the smallest key, 1)
+  int ngm = 0;
+  for (int j = tid; j < kBuf; j += 256) ngm += s_key[j] != 0;
+  int ngm_total;
+  (void)block_exclusive_scan(ngm, s_tmp, ngm_total);
+  uint32_t above;
+  const uint32_t t0 = ngm_total >= c ? radix_kth(s_key, kBuf, c, s_hist, s_par, &above) : 1u;
+  // 3. every element with key >= t0 into the buffer (wave-aggregated appends; lane 0 has the
+  // wave's lowest chunk, so it is active whenever any lane of its wave is)
+  for (int64_t q = tid; q < nchunk; q += 256) {
+    uint32_t key[8];
+    uint16_t bits[8];
+    load8_keys(row, q * 8, V, key, bits);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool hit = key[e] <= 0xffffu && key[e] + 1 >= t0;
+      const uint64_t m = __ballot(hit);
+      if (m) {
+        int basei = 0;
+        if (lane == 0) basei = atomicAdd(&s_cnt[0], __popcll(m));
+        basei = __shfl(basei, 0);
+        const int pos = basei + __popcll(m & ((1ull << lane) - 1));
+        if (hit && pos < kBuf) {
+          s_key[pos] = key[e] + 1;
+          s_id[pos] = (int)(q * 8 + e);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int nbuf = s_cnt[0];
+  if (nbuf > kBuf) {  // uniform
+    select_row_exact(row, V, c, out_id, out_b, s_hist, s_tmp, s_par);
+    return;
+  }
+  for (int j = nbuf + tid; j < kBuf; j += 256) s_key[j] = 0;
+  __syncthreads();
+  // 4. exact selection on the buffer: threshold T (c-th largest), every key above it, and the
+  // need_eq lowest ids among the keys equal to it (the boundary ties, compacted first)
+  const uint32_t T = radix_kth(s_key, kBuf, c, s_hist, s_par, &above);
+  const int need_eq = c - (int)above;
+  int n_eq = 0;
+  for (int j = tid; j < nbuf; j += 256) n_eq += s_key[j] == T;
+  int eq_total;
+  int epos = block_exclusive_scan(n_eq, s_tmp, eq_total);
+  for (int j = tid; j < nbuf; j += 256)
+    if (s_key[j] == T) {
+      if (epos < kEq) s_eq[epos] = s_id[j];
+      ++epos;
+    }
+  __syncthreads();
+  int n_sel = 0;
+  for (int j = tid; j < nbuf; j += 256) {
+    const uint32_t k1 = s_key[j];
+    bool sel = k1 > T;
+    if (k1 == T) {
+      const int id = s_id[j];
+      int lower = 0;
+      if (eq_total <= kEq) {
+        for (int i2 = 0; i2 < eq_total; ++i2) lower += s_eq[i2] < id;
+      } else {
+        for (int i2 = 0; i2 < nbuf; ++i2) lower += s_key[i2] == T && s_id[i2] < id;
+      }
+      sel = lower < need_eq;
+    }
+    n_sel += sel;
+  }
+  int sel_total;
+  int spos = block_exclusive_scan(n_sel, s_tmp, sel_total);
+  for (int j = tid; j < nbuf; j += 256) {
+    const uint32_t k1 = s_key[j];
+    bool sel = k1 > T;
+    if (k1 == T) {
+      const int id = s_id[j];
+      int lower = 0;
+      if (eq_total <= kEq) {
+        for (int i2 = 0; i2 < eq_total; ++i2) lower += s_eq[i2] < id;
+      } else {
+        for (int i2 = 0; i2 < nbuf; ++i2) lower += s_key[i2] == T && s_id[i2] < id;
+      }
+      sel = lower < need_eq;
+    }
+    if (sel) s_sel[spos++] = s_id[j];
+  }
+  __syncthreads();
+  // 5. each winner at its rank by id (ascending id order)
+  for (int k = tid; k < c; k += 256) {
+    const int id = s_sel[k];
+    int rank = 0;
+    for (int i2 = 0; i2 < c; ++i2) rank += s_sel[i2] < id;
+    out_id[rank] = id;
+    out_b[rank] = row[id];
   }
 }
 

@@ -42,7 +42,7 @@ def _readout_case(seed, N, B, r, V, *, zero_head=False):
 def _weights_with(w2_np, r, B, V, device="cuda"):
     z = lambda *s: torch.zeros(*s, dtype=torch.bfloat16, device=device)
     return xpress.Weights(w1=z(V, r), down_h=z(r, 64), down_g=z(r, 64), in_proj=z(r, 3 * r),
-                          mix_L=z(r, B, B), w_gate=z(64, r), w_up=z(64, r), w_down=z(r, 64),
+                          mix_L=z(B, B, r), w_gate=z(64, r), w_up=z(64, r), w_down=z(r, 64),
                           w2=upload.bf16_tensor(w2_np, device))
 
 
@@ -306,6 +306,41 @@ def test_topc_prepare_exact(C, V):
     assert np.array_equal(got, want)
     assert np.array_equal(base_c.float().cpu().numpy(), np.take_along_axis(base, want, axis=1))
     assert np.array_equal(w2c.float().cpu().numpy(), w2[want])
+
+
+@pytest.mark.parametrize("C,V", [(512, 8192), (64, 5003), (1024, 20000)])
+def test_topc_prepare_adversarial_rows(C, V):
+    """Rows that defeat a per-thread shortlist (sorted rows, the answer concentrated in the ids one
+    thread visits, very few distinct values) must still give the exact candidate sets."""
+    rng = np.random.default_rng(11)
+    N, B, r = 1, 8, 64
+    rows = N * (B - 1)
+    base = np.zeros((rows, V), dtype=np.float32)
+    base[0] = np.arange(V) / V * 100                      # ascending
+    base[1] = base[0][::-1]                               # descending
+    chunks = np.arange((V + 7) // 8)
+    ids7 = (8 * chunks[chunks % 256 == 7][:, None] + np.arange(8)[None, :]).reshape(-1)
+    ids7 = ids7[ids7 < V]
+    base[2, ids7] = 1.0 + np.arange(ids7.size) % 37       # best values all in one thread's ids
+    base[3] = rng.integers(0, 3, V)                       # three distinct values
+    base[4] = np.round(rng.standard_normal(V) * 2) / 2
+    base[4, rng.choice(V, 40, replace=False)] = 50.0      # a few large values
+    base[5] = -1.0                                        # all equal
+    base[6] = rng.standard_normal(V)
+    base = synth.bf16_round(base)
+    w2 = synth.bf16_round(rng.standard_normal((V, r)).astype(np.float32))
+    w = _weights_with(w2, r, B, V)
+    c = min(C, V)
+    cand = torch.empty(rows, c, dtype=torch.int64, device="cuda")
+    base_c = torch.empty(rows, c, dtype=torch.bfloat16, device="cuda")
+    w2c = torch.empty(rows, c, r, dtype=torch.bfloat16, device="cuda")
+    xpress.topc_prepare(w, upload.base_logits(base), N, C, cand, base_c, w2c)
+    torch.cuda.synchronize()
+    want = O.topc_select(base, C)
+    got = cand.cpu().numpy()
+    for i in range(rows):
+        assert np.array_equal(got[i], want[i]), f"row {i}"
+    assert np.array_equal(base_c.float().cpu().numpy(), np.take_along_axis(base, want, axis=1))
 
 
 def test_topc_readout_dyadic_exact_and_membership():
