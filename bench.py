@@ -8,9 +8,11 @@ step; the eager (kernel-by-kernel) rate is reported beside it, and both must giv
 
 Prints one JSON line. `value` is Jacobi passes per second of whole steps (per-step setup
 included). Also reported:
-  * `roofline`: the readout GEMM kernel (the dominant kernel), algorithmic bytes per launch
-    (w2 + base + lat) over its average duration measured with HIP events on the launch stream,
-    against the 8 TB/s HBM peak; its MFMA fraction of the 2.5 PFLOP/s bf16 peak is in `extra`;
+  * `roofline`: the readout kernel (the dominant kernel: the full-vocabulary MFMA readout, or the
+    gathered top-C readout when the workload has C > 0), algorithmic bytes per launch (w2 + base
+    + lat, or w2c + base_c + cand + lat) over its average duration measured with HIP events on
+    the launch stream, against the 8 TB/s HBM peak; its rate against the 2.5 PFLOP/s bf16 MFMA
+    peak is in `extra`;
   * `cpu_baseline`: the CPU oracle timed on this host on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -143,28 +145,40 @@ def main() -> int:
     part = torch.empty(ntiles, rows, 2, dtype=torch.int32, device=dev)
 
     def timed(fn, reps):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        # A spin kernel first, so the host has queued every launch before the GPU reaches them:
-        # each event pair then brackets the kernel alone, not the host's launch latency.
+        """Average time per launch of `reps` back-to-back launches between two HIP events on the
+        launch stream (torch's current stream, which the binding passes to the library). A spin
+        kernel first lets the host queue every launch before the GPU reaches them, so the
+        interval holds the kernels and the dispatch gaps between them, not host latency."""
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         if hasattr(torch.cuda, "_sleep"):
-            torch.cuda._sleep(50_000_000)
-        for a, b in evs:
-            a.record()
+            torch.cuda._sleep(10_000_000)
+        a.record()
+        for _ in range(reps):
             fn()
-            b.record()
+        b.record()
         torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3  # us
+        return a.elapsed_time(b) * 1e3 / reps  # us
 
     reps = args.kernel_reps
-    fn_readout = lambda: xpress.readout_partials(w, lat, base, part)
-    fn_reduce = lambda: xpress.argmax_reduce(part, blk2)
+    if wl.C > 0:
+        cand = torch.empty(rows, wl.C, dtype=torch.int64, device=dev)
+        base_c = torch.empty(rows, wl.C, dtype=torch.bfloat16, device=dev)
+        w2c = torch.empty(rows, wl.C, wl.r, dtype=torch.bfloat16, device=dev)
+        xpress.topc_prepare(w, base, wl.N, wl.C, cand, base_c, w2c)
+        fn_readout = lambda: xpress.readout_argmax_topc(lat, w2c, base_c, cand, blk2)
+        fn_reduce = None
+        readout_pass = fn_readout
+    else:
+        fn_readout = lambda: xpress.readout_partials(w, lat, base, part)
+        fn_reduce = lambda: xpress.argmax_reduce(part, blk2)
+        readout_pass = lambda: xpress.readout_argmax(w, lat, base, blk2, ws)
     fn_latent = lambda: xpress.latent_pass(w, blk2, am1, xh, lat, ws)
     for f in (fn_readout, fn_reduce, fn_latent):
-        f()
+        if f is not None:
+            f()
     torch.cuda.synchronize()
     readout_us = timed(fn_readout, reps)
-    reduce_us = timed(fn_reduce, reps)
+    reduce_us = timed(fn_reduce, reps) if fn_reduce is not None else 0.0
     latent_us = timed(fn_latent, reps)
 
     # The K-pass loop alone (per-step setup excluded), through the per-pass entry points.
@@ -173,7 +187,7 @@ def main() -> int:
     def loop():
         for _ in range(K):
             xpress.latent_pass(w, blk2, am1, xh, lat, ws)
-            xpress.readout_argmax(w, lat, base, blk2, ws)
+            readout_pass()
 
     loop()
     torch.cuda.synchronize()
@@ -187,11 +201,19 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    alg_bytes = wl.V * wl.r * 2 + rows * wl.V * 2 + rows * wl.r * 2
-    flops = 2.0 * rows * wl.V * wl.r
+    if wl.C > 0:
+        # gathered w2c rows + base_c + cand (int64) + lat, per launch
+        alg_bytes = rows * wl.C * (wl.r * 2 + 2 + 8) + rows * wl.r * 2
+        kname = "topc_readout_kernel"
+        kdesc = "topc_readout_kernel (gathered GEMV + base_c add + argmax into blk)"
+    else:
+        alg_bytes = wl.V * wl.r * 2 + rows * wl.V * 2 + rows * wl.r * 2
+        kname = "readout_partial_kernel"
+        kdesc = "readout_partial_kernel (bf16 MFMA readout + base add + running argmax)"
+    flops = 2.0 * rows * (wl.C if wl.C > 0 else wl.V) * wl.r
     achieved_gbs = alg_bytes / (readout_us * 1e-6) / 1e9
     mfma_tflops = flops / (readout_us * 1e-6) / 1e12
-    traffic = traffic_record("readout_partial_kernel", wl.name)
+    traffic = traffic_record(kname, wl.name)
 
     out = {
         "metric": METRIC,
@@ -209,7 +231,7 @@ def main() -> int:
         "config": {"workload": wl.name, "N": wl.N, "B": wl.B, "r": wl.r, "H": wl.H, "M": wl.M,
                    "V": wl.V, "topc": wl.C, "passes_per_step": K},
         "roofline": {
-            "kernel": "readout_partial_kernel (bf16 MFMA readout + base add + running argmax)",
+            "kernel": kdesc,
             "bound": "hbm",
             "achieved": round(achieved_gbs, 1),
             "peak": HBM_PEAK_GBS,
@@ -220,12 +242,12 @@ def main() -> int:
             "avg_launch_us": round(readout_us, 2),
         },
         "extra": {
-            "rows_x_V_scored_per_s": round(rows * wl.V * passes_per_s, 1),
+            "rows_x_scored_ids_per_s": round(rows * (wl.C if wl.C > 0 else wl.V) * passes_per_s, 1),
             "eager_ms_per_step": round(eager_ms, 4),
             "eager_passes_per_s": round(K / (eager_ms / 1e3), 2),
             "loop_only_passes_per_s": round(K / (loop_us * 1e-6), 1),
-            "readout_mfma_tflops": round(mfma_tflops, 1),
-            "readout_mfma_frac_of_bf16_peak": round(mfma_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "readout_tflops": round(mfma_tflops, 1),
+            "readout_frac_of_bf16_mfma_peak": round(mfma_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
             "argmax_reduce_us": round(reduce_us, 2),
             "latent_us": round(latent_us, 2),
             "pass_loop_us_per_pass": round(loop_us / K, 2),
@@ -253,17 +275,18 @@ def cpu_baseline(inp, K, budget_s):
     L = synth.bf16_round(O.fold_mixer(inp.raw_L).astype(np.float32))
     xh = O.hidden_cache(inp.h, inp.down_h, inp.down_g, inp.in_proj)
     blk = O.initial_block(inp.base, inp.anchor, wl.N, wl.B)
+    cand = O.topc_select(inp.base, wl.C) if wl.C > 0 else None
     passes = 0
     while passes < K:
-        blk, _, _, _ = O.jacobi(inp, L, xh, blk, K=1, stop_at_fixed_point=False)
+        blk, _, _, _ = O.jacobi(inp, L, xh, blk, K=1, stop_at_fixed_point=False, cand=cand)
         passes += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     return {"value": round(passes / dt, 4), "unit": "passes/s", "cores": O.max_threads(),
             "kind": "oracle",
-            "sample": f"{wl.name}: hidden cache + starting block + {passes} of {K} passes over all "
-                      f"{wl.rows} rows ({dt:.1f} s)"}
+            "sample": f"{wl.name}: hidden cache + starting block{' + top-C select' if wl.C else ''}"
+                      f" + {passes} of {K} passes over all {wl.rows} rows ({dt:.1f} s)"}
 
 
 if __name__ == "__main__":
