@@ -39,12 +39,26 @@ constexpr int kMaxRanges = 256;     // vocabulary ranges per row chunk (partials
 // against id 16*(l/32) + v: each lane owns 16 consecutive ids of its row (two 16-byte base chunks)
 // and visits them in increasing order.
 //
-// LDS stage layout (16-byte chunks): w2 A-row i, chunk c at i*RQ + (c ^ (i % RQ)); base row rr,
-// chunk c at 4*rr + (c ^ ((rr / 4) % 4)). Both XOR swizzles make the 16-lane phases of the
-// fragment reads hit 16 different bank groups. The copy engine writes lane j of a
+// LDS stage layout (16-byte chunks). w2: the tile is written by RQ/2 copy instructions of 64
+// chunks each (RPI = 64/RQ whole w2 rows per instruction), placed 65 chunks apart (one pad
+// chunk), and A-row i sits in instruction i % (RQ/2), sub-row i / (RQ/2). Lane l then reads
+// fragment s at a per-lane base plus the immediate 32*s bytes (no address arithmetic in the
+// loop), and at r = 256 the 16 lanes of a read phase hit 16 different bank groups. base: row rr,
+// chunk c at 4*rr + (c ^ ((rr / 4) % 4)) (XOR swizzle). The copy engine writes lane j of a
 // global_load_lds_dwordx4 to M0 + 16*j, so each copy instruction fills 64 consecutive chunks and
 // its lanes fetch whichever global chunks belong there.
 __device__ __forceinline__ int w2_row_id(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
+
+// Compile-time loop: f(Int<i>{}) for i = I .. N-1, each body instantiated with a constant index
+// (a plain unrolled loop is not guaranteed to unroll once its body grows, and a rolled loop
+// indexes register arrays dynamically).
+template <int V> struct Int { static constexpr int value = V; };
+template <int I, int N, class F> __device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(Int<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 // One 1 KiB copy: this lane's 16 bytes at gbase + off (a scalar base pointer and a per-lane
 // 32-bit byte offset) to LDS byte address lds_base + 16 * lane. Written as inline assembly so
@@ -64,14 +78,17 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
   if (pass_skipped(flags, pass)) return;
   constexpr int KS = R / 16;
   constexpr int RQ = R / 8;                     // 16-byte chunks per w2 / lat row
+  constexpr int RPI = 64 / RQ;                  // w2 rows per copy instruction
+  constexpr int NI = 32 / RPI;                  // copy instructions per w2 tile
+  constexpr int WP = 65;                        // chunks per w2 copy block (64 + pad)
   constexpr int CH = kNW * RW * 32;             // rows per row chunk
-  constexpr int WCH = 32 * RQ;                  // w2 chunks per stage
+  constexpr int WCH = NI * WP;                  // w2 chunks per stage
   constexpr int BCH = CH * 4;                   // base chunks per stage
   constexpr int SCH = WCH + BCH;                // chunks per stage
-  // copy instructions per wave per step; when the w2 tile has fewer than kNW * 64 chunks, the
-  // waves past it repeat the first ones (same bytes to the same place), so every wave issues the
-  // same number of copies and one vmcnt value fits all
-  constexpr int WI = (WCH / 64 + kNW - 1) / kNW;
+  // copy instructions per wave per step; when the w2 tile has fewer than kNW instructions, the
+  // waves past them repeat the first ones (same bytes to the same place), so every wave issues
+  // the same number of copies and one vmcnt value fits all
+  constexpr int WI = (NI + kNW - 1) / kNW;
   constexpr int BI = BCH / 64 / kNW;
   constexpr int DI = WI + BI;
   static_assert(BCH % (64 * kNW) == 0, "base stage must split evenly over the waves");
@@ -123,13 +140,13 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
   // Per-lane byte offsets of the copies, relative to the step's w2 tile and to the chunk's base
   // rows at the step's first id (loop-invariant; the step only moves the scalar base pointers).
   // In the last step of the vocabulary, ids past V are clamped instead (w2 row V-1, the padded
-  // row's last chunk).
+  // row's last chunk). Copy instruction ins, lane j of the w2 tile carries chunk j % RQ of A-row
+  // (j / RQ) * NI + ins.
   uint32_t offw[WI], offb[BI];
 #pragma unroll
   for (int q = 0; q < WI; ++q) {
-    const int ins = (wave + q * kNW) % (WCH / 64);  // copy instruction index in the w2 tile
-    const int p = ins * 64 + lane;                   // chunk position in the stage
-    const int i = p / RQ, c = (p % RQ) ^ (i % RQ);
+    const int ins = (wave + q * kNW) % NI;
+    const int i = (lane / RQ) * NI + ins, c = lane % RQ;
     offw[q] = (uint32_t)((w2_row_id(i) * R + 8 * c) * 2);
   }
 #pragma unroll
@@ -139,6 +156,14 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
     offb[q] = (uint32_t)(((int64_t)(min(row0 + rr, rows - 1) - row0) * ld + 8 * c) * 2);
   }
   const uint16_t* base_rc = base + (int64_t)row0 * ld;
+  // The lane id, recomputed where it is used: the clamped offsets of the vocabulary's last step
+  // are needed once per launch, so nothing of them may be hoisted into registers held across the
+  // loop.
+  auto opaque_lane_id = []() __attribute__((always_inline)) {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+  };
   // Issue the copies of step t into stage st.
   auto copy_step = [&](int t, int st) __attribute__((always_inline)) {
     const uint32_t sbase = lds0 + (uint32_t)st * (SCH * 16);
@@ -147,21 +172,21 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
     const bool tail = 32 * t + 32 > V;  // uniform
 #pragma unroll
     for (int q = 0; q < WI; ++q) {
-      const int ins = (wave + q * kNW) % (WCH / 64);
+      const int ins = (wave + q * kNW) % NI;
       uint32_t off = offw[q];
       if (tail) {
-        const int p = ins * 64 + lane;
-        const int i = p / RQ, c = (p % RQ) ^ (i % RQ);
+        const int ln = opaque_lane_id();
+        const int i = (ln / RQ) * NI + ins, c = ln % RQ;
         off = (uint32_t)(((min(32 * t + w2_row_id(i), V - 1) - 32 * t) * R + 8 * c) * 2);
       }
-      lds_copy16(gw, off, __builtin_amdgcn_readfirstlane(sbase + ins * 1024));
+      lds_copy16(gw, off, __builtin_amdgcn_readfirstlane(sbase + ins * WP * 16));
     }
 #pragma unroll
     for (int q = 0; q < BI; ++q) {
       const int ins = wave + q * kNW;
       uint32_t off = offb[q];
       if (tail) {
-        const int p = ins * 64 + lane;
+        const int p = ins * 64 + opaque_lane_id();
         const int rr = p >> 2, c = (p & 3) ^ ((rr >> 2) & 3);
         off = (uint32_t)(((int64_t)(min(row0 + rr, rows - 1) - row0) * ld +
                           8 * (min(4 * t + c, last_chunk) - 4 * t)) * 2);
@@ -170,18 +195,8 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
     }
   };
 
-  // The base tile enters the accumulators through the matrix core: two extra MFMAs per row tile
-  // with A = a 0/1 selection matrix (A-row i picks id w2_row_id(i)) and B = the row's base
-  // values, 8 consecutive ids per lane, which is a plain 16-byte chunk of the base row. The
-  // products are exact (x * 1, x * 0) and so is their sum, so the accumulator starts at exactly
-  // base[row, id]; no VALU conversion or add is left in the epilogue.
-  bf16x8 sel[2];
-#pragma unroll
-  for (int sg = 0; sg < 2; ++sg) {
-    const int e1 = w2_row_id(l32) - 16 * sg - 8 * half;  // the one k of this lane's A-row hit
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sel[sg][e] = (e == e1) ? (__bf16)1.0f : (__bf16)0.0f;
-  }
+  // this lane's A-fragment chunk of fragment 0 inside a stage (fragment s is 2*s chunks on)
+  const int a_off = (l32 % NI) * WP + (l32 / NI) * RQ + half;
 
   float bv[RW];
   int bi[RW];
@@ -191,74 +206,153 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
     bi[k] = 32 * t0;
   }
   // Step t of row tile k: the 16 logits of this lane's row (ids 32t + 16*half + e, e = 0..15)
-  // folded into the running winner. The step maximum comes from a tree of max operations; the
-  // lowest e holding it from a descent that prefers the lower half at every level. Steps rise
-  // with t, so a strict comparison keeps the lowest id among equal values.
-  auto epilogue = [&](int t, int k, const f32x16& acc) __attribute__((always_inline)) {
-    float lg[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) lg[e] = acc[e];
-    if (32 * t + 32 > V) {  // the last step of the vocabulary: ids >= V never win
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (32 * t + 16 * half + e >= V) lg[e] = -INFINITY;
-    }
-    float m2[8], m4[4], m8[2];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) m2[e] = fmaxf(lg[2 * e], lg[2 * e + 1]);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) m4[e] = fmaxf(m2[2 * e], m2[2 * e + 1]);
-    m8[0] = fmaxf(m4[0], m4[1]);
-    m8[1] = fmaxf(m4[2], m4[3]);
-    const float sv = fmaxf(m8[0], m8[1]);
-    const int s8 = m8[0] == sv ? 0 : 1;
-    const int s4 = 2 * s8 + ((s8 ? m4[2] : m4[0]) == sv ? 0 : 1);
-    const float a2 = s8 ? (s4 & 1 ? m2[6] : m2[4]) : (s4 & 1 ? m2[2] : m2[0]);
-    const int s2 = 2 * s4 + (a2 == sv ? 0 : 1);
-    float a1 = lg[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) a1 = s2 == e ? lg[2 * e] : a1;
-    const int se = 2 * s2 + (a1 == sv ? 0 : 1);
-    const bool gt = sv > bv[k];
-    bv[k] = gt ? sv : bv[k];
-    bi[k] = gt ? 32 * t + 16 * half + se : bi[k];
+  // folded into the running winner, in three phases. The step maximum comes from a tree of max
+  // operations; the lowest e holding it from a descent that takes the upper half at a level only
+  // when the lower one lacks the maximum, picking the next level's candidates by multiplexing on
+  // the bits found so far. Steps rise with t, so a strict comparison keeps the lowest id among
+  // equal values. Only the last step of a range can reach past V (checked when `last` is set).
+  struct Epi {
+    float m2[8], m4[4], m8[2], sv;  // phase 0 -> 1
+    float r1;                       // phase 1 -> 2: the candidate for the last bit
+    int se;                         // phase 1 -> 2: the upper three bits of e
   };
+  auto epi_phase = [&](int ph, int t, int k, f32x16& acc, Epi& ep, bool last)
+      __attribute__((always_inline)) {
+    if (ph == 0) {
+      if (last && 32 * t + 32 > V) {  // the last step of the vocabulary: ids >= V never win
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (32 * t + 16 * half + e >= V) acc[e] = -INFINITY;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ep.m2[e] = fmaxf(acc[2 * e], acc[2 * e + 1]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ep.m4[e] = fmaxf(ep.m2[2 * e], ep.m2[2 * e + 1]);
+      ep.m8[0] = fmaxf(ep.m4[0], ep.m4[1]);
+      ep.m8[1] = fmaxf(ep.m4[2], ep.m4[3]);
+      ep.sv = fmaxf(ep.m8[0], ep.m8[1]);
+    } else if (ph == 1) {
+      const bool c8 = ep.m8[0] != ep.sv;
+      const bool c4 = (c8 ? ep.m4[2] : ep.m4[0]) != ep.sv;
+      const float q2a = c8 ? ep.m2[4] : ep.m2[0], q2b = c8 ? ep.m2[6] : ep.m2[2];
+      const bool c2 = (c4 ? q2b : q2a) != ep.sv;
+      float lg[16];  // scalars: a select between two vector elements would become a dynamic index
+#pragma unroll
+      for (int e = 0; e < 16; ++e) lg[e] = acc[e];
+      float q1[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) q1[j] = c8 ? lg[8 + 2 * j] : lg[2 * j];
+      const float r1a = c4 ? q1[2] : q1[0], r1b = c4 ? q1[3] : q1[1];
+      ep.r1 = c2 ? r1b : r1a;
+      ep.se = (c8 ? 8 : 0) + (c4 ? 4 : 0) + (c2 ? 2 : 0);
+    } else {
+      ep.se += ep.r1 != ep.sv ? 1 : 0;
+      const bool gt = ep.sv > bv[k];
+      bv[k] = gt ? ep.sv : bv[k];
+      bi[k] = gt ? 32 * t + 16 * half + ep.se : bi[k];
+    }
+  };
+  auto epilogue = [&](int t, int k, f32x16& acc, bool last) __attribute__((always_inline)) {
+    Epi ep;
+#pragma unroll
+    for (int ph = 0; ph < 3; ++ph) epi_phase(ph, t, k, acc, ep, last);
+  };
+
+  // The MFMAs of the current stage into acc, with the epilogue of the previous step (tp, accp)
+  // when `with_prev` is set: its phases go between the MFMA groups in program order (phase ph of
+  // tile k after fragment group 1 + 3*k + ph), so they issue while the matrix core works instead
+  // of after it.
+  constexpr bool kSpread = 3 * RW + 1 <= KS;
+  int st = 0;
+  auto compute = [&](f32x16 (&acc)[RW], auto with_prev, int tp, f32x16 (&accp)[RW])
+      __attribute__((always_inline)) {
+    constexpr bool kPrev = decltype(with_prev)::value != 0;
+    const uint4* sp = s_stage[st];
+    Epi ep[RW];
+    // The accumulators start at the row's base logits: this lane's 16 ids (two 16-byte chunks of
+    // the base row) widened from bf16 to fp32 exactly (a shift or a mask per value).
+#pragma unroll
+    for (int k = 0; k < RW; ++k) {
+      const int rr = (wave * RW + k) * 32 + l32;
+      const int sw = (rr >> 2) & 3;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 c = sp[WCH + 4 * rr + ((2 * half + h) ^ sw)];
+        const uint32_t d[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[k][8 * h + 2 * j] = __uint_as_float(d[j] << 16);
+          acc[k][8 * h + 2 * j + 1] = __uint_as_float(d[j] & 0xFFFF0000u);
+        }
+      }
+    }
+    // A fragments are read two groups ahead of their MFMAs (three registers sets in rotation).
+    const uint4* sa = sp + a_off;
+    bf16x8 af[3];
+    af[0] = as_bf16x8(sa[0]);
+    if constexpr (KS > 1) af[1] = as_bf16x8(sa[2]);
+    static_for<0, KS>([&](auto sc) __attribute__((always_inline)) {
+      constexpr int s = decltype(sc)::value;
+      if constexpr (s + 2 < KS) af[(s + 2) % 3] = as_bf16x8(sa[2 * (s + 2)]);
+#pragma unroll
+      for (int k = 0; k < RW; ++k) acc[k] = mfma32x32x16(af[s % 3], bl[k][s], acc[k]);
+      if constexpr (kSpread && kPrev && s >= 1 && s <= 3 * RW) {
+        constexpr int g = s - 1;
+        epi_phase(g % 3, tp, g / 3, accp[g / 3], ep[g / 3], false);
+      }
+    });
+    if constexpr (!kSpread && kPrev) {
+#pragma unroll
+      for (int k = 0; k < RW; ++k) epilogue(tp, k, accp[k], false);
+    }
+    // The descent results are consumed here, at the end of the step, so the compiler computes
+    // them on every step rather than branching around them where the maximum does not rise (a
+    // branch would split the step into separate scheduling regions).
+    if constexpr (kSpread && kPrev) {
+#pragma unroll
+      for (int k = 0; k < RW; ++k) asm volatile("" ::"v"(ep[k].se));
+    }
+  };
+  constexpr int VW = (NS - 2) * DI;  // copies allowed in flight past step t
+  // Start step t: this wave's copies of step t are done (those of later steps may still run);
+  // after the barrier every wave's are, and every wave has finished reading step t-1's stage,
+  // which then receives the copies of step t+NS-1 (past the range end: the last step again, L2
+  // hits).
+  auto begin_step = [&](int t) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (VW & 15) | ((VW >> 4) << 14));  // vmcnt(VW)
+    __syncthreads();
+    copy_step(min(t + NS - 1, t1 - 1), st == 0 ? NS - 1 : st - 1);
+  };
+  auto next_stage = [&]() __attribute__((always_inline)) { st = st == NS - 1 ? 0 : st + 1; };
 
   // prologue: steps t0 .. t0+NS-2 in flight
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i) copy_step(min(t0 + i, t1 - 1), i);
-  constexpr int VW = (NS - 2) * DI;  // copies allowed in flight past step t
-  int st = 0;
-  for (int t = t0; t < t1; ++t) {
-    // this wave's copies of step t are done (those of later steps may still run); after the
-    // barrier every wave's are, and every wave has finished step t-1 (its stage is free)
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (VW & 15) | ((VW >> 4) << 14));  // vmcnt(VW)
-    __syncthreads();
-    // into the stage of step t-1; past the range end this refetches the last step (L2 hits)
-    copy_step(min(t + NS - 1, t1 - 1), st == 0 ? NS - 1 : st - 1);
+  // Software pipeline: step t's MFMAs carry step t-1's epilogue (VALU, from registers); two
+  // accumulator sets alternate. The last epilogue of the range runs on its own.
+  f32x16 accA[RW], accB[RW];
+  begin_step(t0);
+  if (active) compute(accA, Int<0>{}, 0, accB);
+  next_stage();
+  int t = t0 + 1;
+  for (; t + 1 < t1; t += 2) {
+    begin_step(t);
+    if (active) compute(accB, Int<1>{}, t - 1, accA);
+    next_stage();
+    begin_step(t + 1);
+    if (active) compute(accA, Int<1>{}, t, accB);
+    next_stage();
+  }
+  if (t < t1) {  // one step left: t = t1 - 1
+    begin_step(t);
     if (active) {
-      const uint4* sp = s_stage[st];
-      f32x16 acc[RW];
+      compute(accB, Int<1>{}, t - 1, accA);
 #pragma unroll
-      for (int k = 0; k < RW; ++k) {
-        const int rr = (wave * RW + k) * 32 + l32;
-        const int sw = (rr >> 2) & 3;
-        const bf16x8 b0 = as_bf16x8(sp[WCH + 4 * rr + ((2 * 0 + half) ^ sw)]);
-        const bf16x8 b1 = as_bf16x8(sp[WCH + 4 * rr + ((2 * 1 + half) ^ sw)]);
-        acc[k] = mfma32x32x16(sel[0], b0, f32x16{});
-        acc[k] = mfma32x32x16(sel[1], b1, acc[k]);
-      }
-      const uint4* sw = sp + l32 * RQ;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 a = as_bf16x8(sw[(2 * s + half) ^ (l32 % RQ)]);
-#pragma unroll
-        for (int k = 0; k < RW; ++k) acc[k] = mfma32x32x16(a, bl[k][s], acc[k]);
-      }
-#pragma unroll
-      for (int k = 0; k < RW; ++k) epilogue(t, k, acc[k]);
+      for (int k = 0; k < RW; ++k) epilogue(t, k, accB[k], true);
     }
-    st = st == NS - 1 ? 0 : st + 1;
+  } else if (active) {
+#pragma unroll
+    for (int k = 0; k < RW; ++k) epilogue(t - 1, k, accA[k], true);
   }
   // drain the trailing copies before the workgroup's LDS can be handed to another workgroup
   __builtin_amdgcn_s_waitcnt(0x0F70);
