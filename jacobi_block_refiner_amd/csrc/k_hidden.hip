@@ -8,7 +8,8 @@
 // That keeps both projections on exact bf16 operands: K1a runs one bf16 MFMA GEMM
 // hdg = h . [down_h; down_g]^T over all N*B slot rows (fp32 accumulate), split over K into
 // partial sums when there are few output tiles; K1b adds the partials in a fixed order, takes the
-// slot mean of the down_g half and applies in_proj's hidden half in fp32.
+// slot mean of the down_g half and applies in_proj's hidden half in fp32, one block of slots per
+// workgroup.
 #include "launch.hpp"
 #include "xpress_common.hpp"
 
@@ -23,20 +24,24 @@ constexpr int kLQ = kTK / 8 + 1;  // padded LDS row stride (uint4)
 
 // Split-K partial products: part[ks, m, j] = sum_{k in slice ks} h[m, k] * Wcat[j, k].
 // 4 waves as a 2 x 2 grid of 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16, layout as in the
-// readout kernel: D[row = 8*(v/4) + 4*(l/32) + v%4][col = l%32]). The next k chunk is loaded into
-// registers while the current one is multiplied out of LDS.
+// readout kernel: D[row = 8*(v/4) + 4*(l/32) + v%4][col = l%32]). Up to kDepth k chunks are loaded
+// into registers ahead of the one being multiplied out of LDS: the operands are first touches
+// from HBM, so the slice's loads must be in flight together rather than one chunk at a time.
+constexpr int kDepth = 8;
+
 __global__ __launch_bounds__(256) void hidden_gemm_kernel(const uint16_t* __restrict__ h,
                                                           const uint16_t* __restrict__ down_h,
                                                           const uint16_t* __restrict__ down_g,
                                                           int NB, int H, int r, int kslice,
                                                           float* __restrict__ part) {
-  __shared__ uint4 s_a[kTM * kLQ];
-  __shared__ uint4 s_b[kTN * kLQ];
+  __shared__ u32x4 s_a[kTM * kLQ];
+  __shared__ u32x4 s_b[kTN * kLQ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int m0 = blockIdx.x * kTM, n0 = blockIdx.y * kTN;
   const int ks = blockIdx.z;
   const int kbeg = ks * kslice, kend = min(H, kbeg + kslice);
+  const int nch = (kend - kbeg) / kTK;  // H and kslice are multiples of kTK
   const int l32 = lane & 31, half = lane >> 5;
   // this thread's two 16-byte chunks of each k chunk: rows rr0, rr0 + 32 at column cc
   const int rr0 = tid / (kTK / 8), cc = tid % (kTK / 8);
@@ -45,34 +50,60 @@ __global__ __launch_bounds__(256) void hidden_gemm_kernel(const uint16_t* __rest
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int rr = rr0 + 32 * q;
-    arow[q] = h + (int64_t)min(m0 + rr, NB - 1) * H;
+    arow[q] = h + (int64_t)min(m0 + rr, NB - 1) * H + kbeg;
     const int j = n0 + rr;  // output column = row of [down_h; down_g]
-    brow[q] = (j < r) ? down_h + (int64_t)j * H : down_g + (int64_t)(j - r) * H;
+    brow[q] = ((j < r) ? down_h + (int64_t)j * H : down_g + (int64_t)(j - r) * H) + kbeg;
   }
-  uint4 ra[2], rb[2];
-  auto load = [&](int k0) __attribute__((always_inline)) {
+  // native vectors, not HIP's uint4 struct: struct copies into the slots would keep them in memory
+  u32x4 ra[kDepth][2], rb[kDepth][2];
+  auto load = [&](auto slotc, int c) __attribute__((always_inline)) {
+    constexpr int slot = decltype(slotc)::value;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      ra[q] = reinterpret_cast<const uint4*>(arow[q] + k0)[cc];
-      rb[q] = reinterpret_cast<const uint4*>(brow[q] + k0)[cc];
+      ra[slot][q] = reinterpret_cast<const u32x4*>(arow[q] + c * kTK)[cc];
+      rb[slot][q] = reinterpret_cast<const u32x4*>(brow[q] + c * kTK)[cc];
+    }
+  };
+  auto stage = [&](auto slotc) __attribute__((always_inline)) {
+    constexpr int slot = decltype(slotc)::value;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      s_a[(rr0 + 32 * q) * kLQ + cc] = ra[slot][q];
+      s_b[(rr0 + 32 * q) * kLQ + cc] = rb[slot][q];
     }
   };
   f32x16 acc = {};
-  load(kbeg);
-  for (int k0 = kbeg; k0 < kend; k0 += kTK) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      s_a[(rr0 + 32 * q) * kLQ + cc] = ra[q];
-      s_b[(rr0 + 32 * q) * kLQ + cc] = rb[q];
-    }
-    __syncthreads();
-    if (k0 + kTK < kend) load(k0 + kTK);
+  auto multiply = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < kTK / 16; ++s) {
-      const bf16x8 a = as_bf16x8(s_a[(32 * wm + l32) * kLQ + 2 * s + half]);
-      const bf16x8 b = as_bf16x8(s_b[(32 * wn + l32) * kLQ + 2 * s + half]);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, s_a[(32 * wm + l32) * kLQ + 2 * s + half]);
+      const bf16x8 b = __builtin_bit_cast(bf16x8, s_b[(32 * wn + l32) * kLQ + 2 * s + half]);
       acc = mfma32x32x16(a, b, acc);
     }
+  };
+  // whole groups of kDepth chunks: every load unconditional (the last group's refills repeat its
+  // last chunk), so the slots stay in fixed registers
+  const int nfull = nch / kDepth * kDepth;
+  if (nfull > 0) {
+    static_for<0, kDepth>([&](auto dc) __attribute__((always_inline)) {
+      load(dc, decltype(dc)::value);
+    });
+    for (int c0 = 0; c0 < nfull; c0 += kDepth) {
+      static_for<0, kDepth>([&](auto dc) __attribute__((always_inline)) {
+        constexpr int d = decltype(dc)::value;
+        stage(dc);
+        __syncthreads();
+        load(dc, min(c0 + d + kDepth, nfull - 1));
+        multiply();
+        __syncthreads();
+      });
+    }
+  }
+  for (int c = nfull; c < nch; ++c) {  // the rest, one chunk at a time
+    load(Int<0>{}, c);
+    stage(Int<0>{});
+    __syncthreads();
+    multiply();
     __syncthreads();
   }
   const int col = n0 + 32 * wn + l32;
@@ -84,61 +115,73 @@ __global__ __launch_bounds__(256) void hidden_gemm_kernel(const uint16_t* __rest
   }
 }
 
-// Split-K reduction, once per element, in a fixed order: hdg[m, j] = sum_s part[s, m, j].
-__global__ __launch_bounds__(256) void hidden_reduce_kernel(const float4* __restrict__ part,
-                                                            int nsplit, int64_t n4,
-                                                            float4* __restrict__ hdg) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  // splits in ascending order (fixed summation order); 8 loads in flight at a time
-  float4 v = part[i];
-  int sp = 1;
-  for (; sp + 8 <= nsplit; sp += 8) {
-    float4 u[8];
+// One workgroup per (block n, 64 output channels), in fp32:
+//   hdg[n, b, j] = sum_s part[s, n*B + b, j]            (splits in ascending order)
+//   hg[k] = (1/B) sum_b hdg[n, b, r + k]                 (slots in ascending order)
+//   xh[n, b, c] = sum_k P[c, k] hdg[n, b, k] + sum_k P[c, r + k] hg[k]
+// The block's slots and its 64 rows of in_proj's hidden half are staged in LDS with coalesced
+// loads (many in flight); hd and hg are then read as broadcasts, the in_proj rows with a padded
+// pitch (no bank conflicts).
+template <int R>
+__global__ __launch_bounds__(256) void hidden_project_kernel(const float* __restrict__ part,
+                                                             int nsplit, int NB,
+                                                             const uint16_t* __restrict__ in_proj,
+                                                             int B, float* __restrict__ xh) {
+  constexpr int PQ = 2 * R / 8;     // 16-byte chunks of a staged in_proj row
+  constexpr int PP = PQ + 1;        // padded pitch
+  __shared__ float s_hdg[16][2 * R];
+  __shared__ float s_hg[R];
+  __shared__ float s_gp[64];
+  __shared__ uint4 s_p[64 * PP];
+  const int n = blockIdx.x, c0 = blockIdx.y * 64, tid = threadIdx.x;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) u[j] = part[(sp + j) * n4 + i];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      v.x += u[j].x;
-      v.y += u[j].y;
-      v.z += u[j].z;
-      v.w += u[j].w;
-    }
+  for (int i = 0; i < 64 * PQ / 256; ++i) {  // all of the thread's loads in flight together
+    const int q = tid + 256 * i, row = q / PQ, col = q % PQ;
+    s_p[row * PP + col] = reinterpret_cast<const uint4*>(in_proj + (int64_t)(c0 + row) * 3 * R)[col];
   }
-  for (; sp < nsplit; ++sp) {
-    const float4 u = part[sp * n4 + i];
+  const int64_t n4 = (int64_t)NB * 2 * R / 4;  // float4s per split
+  const float4* p4 = reinterpret_cast<const float4*>(part) + (int64_t)n * B * 2 * R / 4;
+  const int nq = B * 2 * R / 4;
+  auto add4 = [](float4& v, const float4& u) __attribute__((always_inline)) {
     v.x += u.x;
     v.y += u.y;
     v.z += u.z;
     v.w += u.w;
+  };
+  // two float4s per thread at a time, splits in ascending order, eight splits per batch of loads
+  for (int q0 = tid; q0 < nq; q0 += 512) {
+    const int q1 = min(q0 + 256, nq - 1);  // a repeat of the last element when past the end
+    float4 v0 = p4[q0], v1 = p4[q1];
+    int sp = 1;
+    for (; sp + 8 <= nsplit; sp += 8) {
+      float4 u0[8], u1[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        u0[j] = p4[(sp + j) * n4 + q0];
+        u1[j] = p4[(sp + j) * n4 + q1];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        add4(v0, u0[j]);
+        add4(v1, u1[j]);
+      }
+    }
+    for (; sp < nsplit; ++sp) {
+      add4(v0, p4[sp * n4 + q0]);
+      add4(v1, p4[sp * n4 + q1]);
+    }
+    reinterpret_cast<float4*>(&s_hdg[0][0])[q0] = v0;
+    if (q0 + 256 < nq) reinterpret_cast<float4*>(&s_hdg[0][0])[q0 + 256] = v1;
   }
-  hdg[i] = v;
-}
-
-// One workgroup per (block n, 64 output channels), in fp32:
-//   hg[k] = (1/B) sum_b hdg[n, b, r + k]
-//   xh[n, b, c] = sum_k P[c, k] hdg[n, b, k] + sum_k P[c, r + k] hg[k].
-// hd and hg sit in LDS (read as broadcasts); each thread streams its in_proj row from L2.
-template <int R>
-__global__ __launch_bounds__(256) void hidden_project_kernel(const float* __restrict__ hdg,
-                                                             const uint16_t* __restrict__ in_proj,
-                                                             int B, float* __restrict__ xh) {
-  __shared__ float s_hd[16][R];
-  __shared__ float s_hg[R];
-  __shared__ float s_gp[64];
-  const int n = blockIdx.x, c0 = blockIdx.y * 64, tid = threadIdx.x;
-  for (int q = tid; q < 16 * R; q += 256) {
-    const int b = q / R, k = q % R;
-    s_hd[b][k] = b < B ? hdg[((int64_t)n * B + b) * 2 * R + k] : 0.f;
-  }
+  __syncthreads();
   for (int k = tid; k < R; k += 256) {
     float sum = 0.f;
-    for (int b = 0; b < B; ++b) sum += hdg[((int64_t)n * B + b) * 2 * R + R + k];
+    for (int b = 0; b < B; ++b) sum += s_hdg[b][R + k];
     s_hg[k] = sum / (float)B;
   }
   __syncthreads();
   const int c = tid & 63, grp = tid >> 6;  // grp: slots 4*grp .. 4*grp+3
-  const uint4* prow = reinterpret_cast<const uint4*>(in_proj + (int64_t)(c0 + c) * 3 * R);
+  const uint4* prow = s_p + c * PP;
   if (grp == 0) {
     float g = 0.f;
     for (int kq = 0; kq < R / 8; ++kq) {
@@ -151,6 +194,7 @@ __global__ __launch_bounds__(256) void hidden_project_kernel(const float* __rest
     s_gp[c] = g;
   }
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const int b0 = min(4 * grp, 15);
   for (int kq = 0; kq < R / 8; ++kq) {
     const uint4 u = prow[kq];
     const float w8[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
@@ -158,7 +202,7 @@ __global__ __launch_bounds__(256) void hidden_project_kernel(const float* __rest
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] = fmaf(w8[e], s_hd[4 * grp + v][8 * kq + e], acc[v]);
+      for (int v = 0; v < 4; ++v) acc[v] = fmaf(w8[e], s_hdg[min(b0 + v, 15)][8 * kq + e], acc[v]);
   }
   __syncthreads();
 #pragma unroll
@@ -212,20 +256,16 @@ hipError_t launch_hidden_project(const float* part, int H, const uint16_t* in_pr
                                  int r, float* xh, hipStream_t s) {
   const int NB = N * B;
   const int ns = hidden_splits(NB, H, r);
-  float* hdg = const_cast<float*>(part) + (size_t)ns * NB * 2 * r;
-  const int64_t n4 = (int64_t)NB * 2 * r / 4;
-  hipLaunchKernelGGL(hidden_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
-                     reinterpret_cast<const float4*>(part), ns, n4, reinterpret_cast<float4*>(hdg));
   dim3 grid(N, r / 64);
   switch (r) {
     case 64:
-      hipLaunchKernelGGL(hidden_project_kernel<64>, grid, dim3(256), 0, s, hdg, in_proj, B, xh);
+      hipLaunchKernelGGL(hidden_project_kernel<64>, grid, dim3(256), 0, s, part, ns, NB, in_proj, B, xh);
       break;
     case 128:
-      hipLaunchKernelGGL(hidden_project_kernel<128>, grid, dim3(256), 0, s, hdg, in_proj, B, xh);
+      hipLaunchKernelGGL(hidden_project_kernel<128>, grid, dim3(256), 0, s, part, ns, NB, in_proj, B, xh);
       break;
     case 256:
-      hipLaunchKernelGGL(hidden_project_kernel<256>, grid, dim3(256), 0, s, hdg, in_proj, B, xh);
+      hipLaunchKernelGGL(hidden_project_kernel<256>, grid, dim3(256), 0, s, part, ns, NB, in_proj, B, xh);
       break;
     default: return hipErrorInvalidValue;
   }

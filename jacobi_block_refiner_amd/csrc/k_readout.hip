@@ -49,17 +49,6 @@ constexpr int kMaxRanges = 256;     // vocabulary ranges per row chunk (partials
 // its lanes fetch whichever global chunks belong there.
 __device__ __forceinline__ int w2_row_id(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
 
-// Compile-time loop: f(Int<i>{}) for i = I .. N-1, each body instantiated with a constant index
-// (a plain unrolled loop is not guaranteed to unroll once its body grows, and a rolled loop
-// indexes register arrays dynamically).
-template <int V> struct Int { static constexpr int value = V; };
-template <int I, int N, class F> __device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(Int<I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
 // One 1 KiB copy: this lane's 16 bytes at gbase + off (a scalar base pointer and a per-lane
 // 32-bit byte offset) to LDS byte address lds_base + 16 * lane. Written as inline assembly so
 // the compiler's wait-count bookkeeping stays out of it (the kernel waits for the copies itself,

@@ -29,6 +29,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // (value, index) arg-max combine: larger value wins; equal values keep the lower index.
 // -0.0 and +0.0 compare equal, so they tie and the lower index wins.
+// Compile-time loop: f(Int<i>{}) for i = I .. N-1, each body instantiated with a constant index
+// (a plain unrolled loop is not guaranteed to unroll once its body grows, and a rolled loop
+// indexes register arrays dynamically).
+template <int V> struct Int { static constexpr int value = V; };
+template <int I, int N, class F> __device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(Int<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {
   const bool take = (ov > v) | ((ov == v) & (oi < i));  // bitwise: no branches
   v = take ? ov : v;
