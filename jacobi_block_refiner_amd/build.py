@@ -21,9 +21,9 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-# Per-source extra flags. The readout's running maxima never see a NaN (non-finite inputs are
-# outside the contract), so its fmaxf needs no quieting of the MFMA outputs first.
-EXTRA = {"k_readout.hip": ["-fno-honor-nans"]}
+# Per-source extra flags. The readout's running maxima and the top-C selection's comparisons never
+# see a NaN (non-finite inputs are outside the contract), so fmaxf needs no quieting first.
+EXTRA = {"k_readout.hip": ["-fno-honor-nans"], "k_topc.hip": ["-fno-honor-nans"]}
 
 
 def sources() -> list[Path]:

@@ -184,26 +184,29 @@ constexpr int kBuf = 2048;
 constexpr int kEq = 512;
 __device__ __forceinline__ uint32_t radix_kth(const uint32_t* keys, int n, int k, uint32_t* s_hist,
                                               uint32_t* s_par, uint32_t* above_out) {
-  // keys: 17-bit (key + 1, 0 = empty); returns the k-th largest non-empty key and sets
-  // *above_out = number of keys strictly above it. Whole workgroup.
+  // keys: 17-bit (key + 1, 0 = empty); returns the k-th largest non-empty key (as key + 1) and
+  // sets *above_out = number of keys strictly above it. Whole workgroup (256 threads). Two
+  // histogram levels over the 16-bit key (high byte, then low byte inside the boundary bin); the
+  // boundary bin is found by a parallel scan over the bins in descending order: thread t owns bin
+  // 255 - t, and the bin whose [count above, count above + own count) holds k - 1 is the one.
   const int tid = threadIdx.x;
+  __shared__ int s_tmp[4];
   s_hist[tid] = 0;
-  if (tid < 256) s_hist[256 + tid] = 0;
   __syncthreads();
   for (int j = tid; j < n; j += 256) {
     const uint32_t k1 = keys[j];
-    if (k1) atomicAdd(&s_hist[k1 >> 8], 1u);  // 0x10000 >> 8 = 256: bin 256 only for key 0xffff+1
+    if (k1) atomicAdd(&s_hist[(k1 - 1) >> 8], 1u);
   }
   __syncthreads();
-  if (tid == 0) {
-    uint32_t acc = 0;
-    int hb = 0;
-    for (int b = 256; b >= 0; --b) {
-      if (acc + s_hist[b] >= (uint32_t)k) { hb = b; break; }
-      acc += s_hist[b];
+  int total;
+  {
+    const int bin = 255 - tid;
+    const int cnt = (int)s_hist[bin];
+    const int above = block_exclusive_scan(cnt, s_tmp, total);
+    if (above < k && k <= above + cnt) {
+      s_par[0] = (uint32_t)bin;
+      s_par[1] = (uint32_t)above;
     }
-    s_par[0] = (uint32_t)hb;
-    s_par[1] = acc;
   }
   __syncthreads();
   const uint32_t h1 = s_par[0], a1 = s_par[1];
@@ -211,19 +214,18 @@ __device__ __forceinline__ uint32_t radix_kth(const uint32_t* keys, int n, int k
   __syncthreads();
   for (int j = tid; j < n; j += 256) {
     const uint32_t k1 = keys[j];
-    if (k1 && (k1 >> 8) == h1) atomicAdd(&s_hist[k1 & 0xffu], 1u);
+    if (k1 && ((k1 - 1) >> 8) == h1) atomicAdd(&s_hist[(k1 - 1) & 0xffu], 1u);
   }
   __syncthreads();
-  if (tid == 0) {
-    const uint32_t rem = (uint32_t)k - a1;
-    uint32_t acc = 0;
-    int lb = 0;
-    for (int b = 255; b >= 0; --b) {
-      if (acc + s_hist[b] >= rem) { lb = b; break; }
-      acc += s_hist[b];
+  {
+    const int rem = k - (int)a1;
+    const int bin = 255 - tid;
+    const int cnt = (int)s_hist[bin];
+    const int above = block_exclusive_scan(cnt, s_tmp, total);
+    if (above < rem && rem <= above + cnt) {
+      s_par[2] = ((h1 << 8) | (uint32_t)bin) + 1;
+      s_par[3] = a1 + (uint32_t)above;
     }
-    s_par[2] = (h1 << 8) | (uint32_t)lb;
-    s_par[3] = a1 + acc;
   }
   __syncthreads();
   const uint32_t t = s_par[2];
@@ -232,18 +234,17 @@ __device__ __forceinline__ uint32_t radix_kth(const uint32_t* keys, int n, int k
   return t;
 }
 
-__global__ __launch_bounds__(256) void topc_select_kernel(const uint16_t* __restrict__ base,
-                                                          int64_t ld, int64_t V, int c,
-                                                          int64_t* __restrict__ cand,
-                                                          uint16_t* __restrict__ base_c) {
+__device__ __forceinline__ void topc_select_row(const uint16_t* __restrict__ base, int64_t ld,
+                                                int64_t V, int c, int64_t* __restrict__ cand,
+                                                uint16_t* __restrict__ base_c) {
   __shared__ uint32_t s_hist[512];
   __shared__ int s_tmp[4];
   __shared__ uint32_t s_par[4];
   __shared__ uint32_t s_key[kBuf];  // key + 1 (0: empty)
   __shared__ int s_id[kBuf];
   __shared__ int s_eq[kEq];         // ids of the boundary ties
-  __shared__ int s_sel[1024];       // ids of the winners
-  __shared__ int s_cnt[2];
+  __shared__ __align__(16) int s_sel[1024];  // ids of the winners
+  __shared__ int s_cnt[4];
   const int p = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const uint16_t* row = base + (int64_t)p * ld;
   int64_t* out_id = cand + (int64_t)p * c;
@@ -253,29 +254,66 @@ __global__ __launch_bounds__(256) void topc_select_kernel(const uint16_t* __rest
     select_row_exact(row, V, c, out_id, out_b, s_hist, s_tmp, s_par);
     return;
   }
+  // The two passes over the row load kLB chunks per thread before using any of them, so enough
+  // bytes are in flight to stream the row (one chunk at a time is latency-bound). Rows are padded
+  // to the stride, so the last chunk is read whole. The passes compare values as fp32 (a bf16
+  // widens exactly; the order of the finite values is the key order, -0.0 equal to +0.0), and ids
+  // >= V, or chunks past the row, read as -inf, below every finite value.
+  constexpr int kLB = 8;
+  const uint4* row4 = reinterpret_cast<const uint4*>(row);
+  auto load_batch = [&](int64_t q0, uint4 (&raw)[kLB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kLB; ++u) {
+      const int64_t q = q0 + 256 * u;
+      raw[u] = q < nchunk ? row4[q] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto widen = [&](int64_t q, const uint4& raw, float (&x)[8]) __attribute__((always_inline)) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(w[e] << 16);
+      x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+    if (q * 8 + 8 > V) {  // the row's last chunk, or past it
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (q * 8 + e >= V) x[e] = -INFINITY;
+    }
+  };
+  // key + 1 of a finite fp32 that holds a bf16 value
+  auto key1_of = [](float v) __attribute__((always_inline)) {
+    return order_key(__float_as_uint(v) >> 16) + 1;
+  };
   // 1. group maxima: thread tid visits chunks tid + 256 i; groups of gv visits (<= 8 groups)
   const int nv_max = (int)((nchunk + 255) / 256);
   const int gv = (nv_max + 7) / 8;
   {
-    uint32_t gm = 0;
+    float gm = -INFINITY;
     int g = 0, inside = 0;
-    for (int64_t q = tid; q < nchunk; q += 256) {
-      uint32_t key[8];
-      uint16_t bits[8];
-      load8_keys(row, q * 8, V, key, bits);
+    for (int64_t q0 = tid; q0 < nchunk; q0 += 256 * kLB) {
+      uint4 raw[kLB];
+      load_batch(q0, raw);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) gm = max(gm, key[e] <= 0xffffu ? key[e] + 1 : 0u);
-      if (++inside == gv) {
-        s_key[tid * 8 + g] = gm;
-        ++g;
-        inside = 0;
-        gm = 0;
+      for (int u = 0; u < kLB; ++u) {
+        const int64_t q = q0 + 256 * u;
+        if (q < nchunk) {
+          float x[8];
+          widen(q, raw[u], x);
+          gm = fmaxf(fmaxf(fmaxf(gm, x[0]), fmaxf(x[1], x[2])),
+                     fmaxf(fmaxf(x[3], x[4]), fmaxf(fmaxf(x[5], x[6]), x[7])));
+          if (++inside == gv) {
+            s_key[tid * 8 + g] = gm > -INFINITY ? key1_of(gm) : 0u;
+            ++g;
+            inside = 0;
+            gm = -INFINITY;
+          }
+        }
       }
     }
-    if (inside) s_key[tid * 8 + g++] = gm;
+    if (inside) s_key[tid * 8 + g++] = gm > -INFINITY ? key1_of(gm) : 0u;
     for (; g < 8; ++g) s_key[tid * 8 + g] = 0;
   }
-  if (tid == 0) s_cnt[0] = 0;
   __syncthreads();
   // 2. t0: the c-th largest group maximum (every group maximum is non-empty if its group had an
   // id below V; with fewer than c of them t0 is the smallest key, 1)
@@ -285,52 +323,69 @@ __global__ __launch_bounds__(256) void topc_select_kernel(const uint16_t* __rest
   (void)block_exclusive_scan(ngm, s_tmp, ngm_total);
   uint32_t above;
   const uint32_t t0 = ngm_total >= c ? radix_kth(s_key, kBuf, c, s_hist, s_par, &above) : 1u;
-  // 3. every element with key >= t0 into the buffer (wave-aggregated appends; lane 0 has the
-  // wave's lowest chunk, so it is active whenever any lane of its wave is)
-  for (int64_t q = tid; q < nchunk; q += 256) {
-    uint32_t key[8];
-    uint16_t bits[8];
-    load8_keys(row, q * 8, V, key, bits);
+  // the smallest fp32 value with key >= t0 - 1 (any finite value when t0 <= 1: the key's bf16
+  // bits, inverse of order_key, would not be a finite value then)
+  float v0 = -3.4028235e38f;
+  if (t0 > 1) {
+    const uint32_t k = t0 - 1;
+    const uint32_t bits = (k & 0x8000u) ? (k & 0x7fffu) : (~k & 0xffffu);
+    v0 = fmaxf(__uint_as_float(bits << 16), -3.4028235e38f);
+  }
+  for (int j = tid; j < kBuf; j += 256) s_key[j] = 0;
+  __syncthreads();
+  // 3. every element with value >= v0 into the buffer. Each wave appends to its own quarter of
+  // it (kBuf / 4 slots) with a wave-uniform running count: the compare's lane mask is the ballot,
+  // so no atomics; unused slots stay empty (key 0). A quarter that would overflow sends the row to
+  // the exact path.
+  constexpr int kSeg = kBuf / 4;
+  const int wave = tid >> 6;
+  int wcnt = 0;  // wave-uniform
+  for (int64_t q0 = tid; q0 < nchunk; q0 += 256 * kLB) {
+    uint4 raw[kLB];
+    load_batch(q0, raw);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const bool hit = key[e] <= 0xffffu && key[e] + 1 >= t0;
-      const uint64_t m = __ballot(hit);
-      if (m) {
-        int basei = 0;
-        if (lane == 0) basei = atomicAdd(&s_cnt[0], __popcll(m));
-        basei = __shfl(basei, 0);
-        const int pos = basei + __popcll(m & ((1ull << lane) - 1));
-        if (hit && pos < kBuf) {
-          s_key[pos] = key[e] + 1;
-          s_id[pos] = (int)(q * 8 + e);
+    for (int u = 0; u < kLB; ++u) {
+      const int64_t q = q0 + 256 * u;
+      float x[8];
+      widen(q, raw[u], x);  // past the row: -inf, no hit
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool hit = x[e] >= v0;
+        const uint64_t m = __ballot(hit);
+        if (m) {
+          const int pos = wcnt + __popcll(m & ((1ull << lane) - 1));
+          if (hit && pos < kSeg) {
+            s_key[wave * kSeg + pos] = key1_of(x[e]);
+            s_id[wave * kSeg + pos] = (int)(q * 8 + e);
+          }
+          wcnt += __popcll(m);
         }
       }
     }
   }
+  if (lane == 0) s_cnt[wave] = wcnt;
   __syncthreads();
-  const int nbuf = s_cnt[0];
-  if (nbuf > kBuf) {  // uniform
+  const int wmax = max(max(s_cnt[0], s_cnt[1]), max(s_cnt[2], s_cnt[3]));
+  if (wmax > kSeg) {  // uniform
     select_row_exact(row, V, c, out_id, out_b, s_hist, s_tmp, s_par);
     return;
   }
-  for (int j = nbuf + tid; j < kBuf; j += 256) s_key[j] = 0;
-  __syncthreads();
   // 4. exact selection on the buffer: threshold T (c-th largest), every key above it, and the
   // need_eq lowest ids among the keys equal to it (the boundary ties, compacted first)
   const uint32_t T = radix_kth(s_key, kBuf, c, s_hist, s_par, &above);
   const int need_eq = c - (int)above;
   int n_eq = 0;
-  for (int j = tid; j < nbuf; j += 256) n_eq += s_key[j] == T;
+  for (int j = tid; j < kBuf; j += 256) n_eq += s_key[j] == T;
   int eq_total;
   int epos = block_exclusive_scan(n_eq, s_tmp, eq_total);
-  for (int j = tid; j < nbuf; j += 256)
+  for (int j = tid; j < kBuf; j += 256)
     if (s_key[j] == T) {
       if (epos < kEq) s_eq[epos] = s_id[j];
       ++epos;
     }
   __syncthreads();
   int n_sel = 0;
-  for (int j = tid; j < nbuf; j += 256) {
+  for (int j = tid; j < kBuf; j += 256) {
     const uint32_t k1 = s_key[j];
     bool sel = k1 > T;
     if (k1 == T) {
@@ -339,7 +394,7 @@ __global__ __launch_bounds__(256) void topc_select_kernel(const uint16_t* __rest
       if (eq_total <= kEq) {
         for (int i2 = 0; i2 < eq_total; ++i2) lower += s_eq[i2] < id;
       } else {
-        for (int i2 = 0; i2 < nbuf; ++i2) lower += s_key[i2] == T && s_id[i2] < id;
+        for (int i2 = 0; i2 < kBuf; ++i2) lower += s_key[i2] == T && s_id[i2] < id;
       }
       sel = lower < need_eq;
     }
@@ -347,7 +402,7 @@ __global__ __launch_bounds__(256) void topc_select_kernel(const uint16_t* __rest
   }
   int sel_total;
   int spos = block_exclusive_scan(n_sel, s_tmp, sel_total);
-  for (int j = tid; j < nbuf; j += 256) {
+  for (int j = tid; j < kBuf; j += 256) {
     const uint32_t k1 = s_key[j];
     bool sel = k1 > T;
     if (k1 == T) {
@@ -356,20 +411,81 @@ __global__ __launch_bounds__(256) void topc_select_kernel(const uint16_t* __rest
       if (eq_total <= kEq) {
         for (int i2 = 0; i2 < eq_total; ++i2) lower += s_eq[i2] < id;
       } else {
-        for (int i2 = 0; i2 < nbuf; ++i2) lower += s_key[i2] == T && s_id[i2] < id;
+        for (int i2 = 0; i2 < kBuf; ++i2) lower += s_key[i2] == T && s_id[i2] < id;
       }
       sel = lower < need_eq;
     }
     if (sel) s_sel[spos++] = s_id[j];
   }
   __syncthreads();
-  // 5. each winner at its rank by id (ascending id order)
+  // 5. the winners in ascending id order: a bitonic sort of s_sel in LDS, padded to a power of
+  // two with INT_MAX (the winners' ids are distinct)
+  int P = 1;
+  while (P < c) P <<= 1;
+  for (int j = c + tid; j < P; j += 256) s_sel[j] = INT_MAX;
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < P; i += 256) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const int a = s_sel[i], b = s_sel[ixj];
+          if ((a > b) == ((i & k) == 0)) {
+            s_sel[i] = b;
+            s_sel[ixj] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
   for (int k = tid; k < c; k += 256) {
     const int id = s_sel[k];
-    int rank = 0;
-    for (int i2 = 0; i2 < c; ++i2) rank += s_sel[i2] < id;
-    out_id[rank] = id;
-    out_b[rank] = row[id];
+    out_id[k] = id;
+    out_b[k] = row[id];
+  }
+}
+
+// One workgroup per draft row: the row's candidate set; with blk given, also the row's starting
+// token (vLLM API page "vllm.model_executor.models.qwen3_xpress", jacobi_refine_greedy: the
+// argmax of the base logits, lowest id on ties), which is the best of the candidates under the
+// same order, written into blk[n, 1 + p % (B - 1)] (and the anchor into slot 0): the starting
+// block without a separate pass over base.
+__global__ __launch_bounds__(256) void topc_select_kernel(const uint16_t* __restrict__ base,
+                                                          int64_t ld, int64_t V, int c,
+                                                          int64_t* __restrict__ cand,
+                                                          uint16_t* __restrict__ base_c,
+                                                          const int64_t* __restrict__ anchor,
+                                                          int64_t* __restrict__ blk, int B) {
+  topc_select_row(base, ld, V, c, cand, base_c);
+  if (!blk) return;
+  // the block's first row also stores the anchor in slot 0
+  if (blockIdx.x % (B - 1) == 0 && threadIdx.x == 0)
+    blk[(int64_t)(blockIdx.x / (B - 1)) * B] = anchor[blockIdx.x / (B - 1)];
+  __shared__ float s_bv[4];
+  __shared__ int s_bi[4];
+  __threadfence_block();
+  __syncthreads();  // the row's candidates and values are written (by this workgroup)
+  const int p = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t* ids = cand + (int64_t)p * c;
+  const uint16_t* vals = base_c + (int64_t)p * c;
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+  for (int k = tid; k < c; k += 256) argmax_merge(bv, bi, __uint_as_float((uint32_t)vals[k] << 16), (int)ids[k]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    argmax_merge(bv, bi, ov, oi);
+  }
+  if (lane == 0) {
+    s_bv[wave] = bv;
+    s_bi[wave] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+#pragma unroll
+    for (int w = 1; w < 4; ++w) argmax_merge(bv, bi, s_bv[w], s_bi[w]);
+    blk[(int64_t)(p / (B - 1)) * B + 1 + p % (B - 1)] = bi;
   }
 }
 
@@ -467,8 +583,10 @@ __global__ __launch_bounds__(256) void topc_readout_kernel(
 }  // namespace
 
 hipError_t launch_topc_select(const uint16_t* base, int64_t ld, int rows, int64_t V, int c,
-                              int64_t* cand, uint16_t* base_c, hipStream_t s) {
-  hipLaunchKernelGGL(topc_select_kernel, dim3(rows), dim3(256), 0, s, base, ld, V, c, cand, base_c);
+                              int64_t* cand, uint16_t* base_c, const int64_t* anchor,
+                              int64_t* blk, int B, hipStream_t s) {
+  hipLaunchKernelGGL(topc_select_kernel, dim3(rows), dim3(256), 0, s, base, ld, V, c, cand, base_c,
+                     anchor, blk, B);
   return hipGetLastError();
 }
 

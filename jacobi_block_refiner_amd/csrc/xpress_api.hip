@@ -304,7 +304,9 @@ xpress_status xpress_topc_prepare(const xpress_weights* w, const xpress_bf16* ba
   const int c = (int)(C < w->V ? C : w->V);
   const int rows = N * (w->B - 1);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  XP_TRY(xpress::launch_topc_select(base, base_ld, rows, w->V, c, cand, base_c, s), "top-C select");
+  XP_TRY(xpress::launch_topc_select(base, base_ld, rows, w->V, c, cand, base_c, nullptr, nullptr, 0,
+                                    s),
+         "top-C select");
   XP_TRY(xpress::launch_topc_gather(cand, w->w2, rows, c, w->r, w2c, s), "top-C gather");
   return XPRESS_OK;
 }
@@ -358,16 +360,21 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
   void* lscr = at<char>(ws, L.lscr);
   XP_TRY(xpress::launch_hidden_gemm(h, w->down_h, w->down_g, N * B, w->H, r, hdg, s), "hidden gemm");
   XP_TRY(xpress::launch_hidden_project(hdg, w->H, w->in_proj, N, B, r, xh, s), "hidden project");
-  if (flags & XPRESS_INIT_FROM_BASE)
-    XP_TRY(xpress::launch_initial_block(base, base_ld, anchor, N, B, V, blk, s), "initial block");
-  else
-    XP_TRY(xpress::launch_set_anchor(anchor, N, B, blk, s), "set anchor");
   const int c = C > 0 ? (int)(C < V ? C : V) : 0;
+  const bool init = (flags & XPRESS_INIT_FROM_BASE) != 0;
+  // the starting block: with candidates, the selection writes it (the best candidate is the
+  // row's argmax; the anchor too)
+  if (init && c == 0)
+    XP_TRY(xpress::launch_initial_block(base, base_ld, anchor, N, B, V, blk, s), "initial block");
+  else if (!init)
+    XP_TRY(xpress::launch_set_anchor(anchor, N, B, blk, s), "set anchor");
   int64_t* cand = at<int64_t>(ws, L.cand);
   xpress_bf16* base_c = at<xpress_bf16>(ws, L.base_c);
   xpress_bf16* w2c = at<xpress_bf16>(ws, L.w2c);
   if (c > 0) {
-    XP_TRY(xpress::launch_topc_select(base, base_ld, rows, V, c, cand, base_c, s), "top-C select");
+    XP_TRY(xpress::launch_topc_select(base, base_ld, rows, V, c, cand, base_c, anchor,
+                                      init ? blk : nullptr, B, s),
+           "top-C select");
     XP_TRY(xpress::launch_topc_gather(cand, w->w2, rows, c, r, w2c, s), "top-C gather");
   }
   const bool stop = (flags & XPRESS_STOP_AT_FIXED_POINT) != 0;
