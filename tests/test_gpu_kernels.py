@@ -102,6 +102,25 @@ def test_readout_argmax_dyadic_exact(r, V, N):
     assert int(changed.item()) == int(not np.array_equal(draft_rows(blk0), best))
 
 
+@pytest.mark.parametrize("V", [1, 7, 31, 33])
+def test_readout_argmax_small_vocabulary(V):
+    """A vocabulary of fewer ids than one 32-id step (or just past it): the single partial step's
+    ids past V must never win; dyadic values, so the argmax is exact (ties included)."""
+    N, B, r = 2, 16, 64
+    rows = N * (B - 1)
+    rng = np.random.default_rng(11 + V)
+    lat = _dyadic(rng, (rows, r), -4, 4, 16)
+    w2 = _dyadic(rng, (V, r), -4, 4, 16)
+    base = _dyadic(rng, (rows, V), -8, 8, 4)
+    blk = torch.zeros(N, B, dtype=torch.int64, device="cuda")
+    log(f"readout small vocabulary V={V}")
+    xpress.readout_argmax(_weights_with(w2, r, B, V), upload.bf16_tensor(lat),
+                          upload.base_logits(base), blk, xpress.alloc_workspace(N, B, r, V, 0, 1))
+    torch.cuda.synchronize()
+    best, _, _ = O.readout_argmax(lat, w2, base)
+    assert np.array_equal(draft_rows(blk.cpu().numpy()), best)
+
+
 def test_readout_zero_head_is_argmax_of_base():
     N, B, r, V = 4, 16, 256, 4099
     lat, w2, base = _readout_case(4, N, B, r, V, zero_head=True)
@@ -290,7 +309,7 @@ def test_step_fixed_k_runs_every_pass_and_is_deterministic():
 # ----------------------------------------------------------------------------------------------
 # top-C
 
-@pytest.mark.parametrize("C,V", [(64, 5003), (512, 8192), (700, 700), (1, 3000)])
+@pytest.mark.parametrize("C,V", [(64, 5003), (512, 8192), (700, 700), (1, 3000), (5, 7), (40, 33)])
 def test_topc_prepare_exact(C, V):
     rng = np.random.default_rng(6)
     N, B, r = 3, 16, 64
