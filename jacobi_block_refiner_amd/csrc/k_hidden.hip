@@ -218,7 +218,7 @@ __global__ __launch_bounds__(256) void hidden_project_kernel(const float* __rest
 int hidden_chunks_per_split(int NB, int H, int r) {
   const int tiles = ((NB + kTM - 1) / kTM) * ((2 * r) / kTN);
   const int kchunks = H / kTK;
-  int s = (512 + tiles - 1) / tiles;  // aim for >= 512 workgroups
+  int s = (256 + tiles - 1) / tiles;  // aim for >= 256 workgroups (one per CU)
   if (s > kchunks) s = kchunks;
   if (s < 1) s = 1;
   return (kchunks + s - 1) / s;
@@ -238,7 +238,7 @@ size_t hidden_scratch_bytes(int NB, int H, int r) {
 // number of splits, whatever H is).
 size_t hidden_scratch_bytes_any_h(int NB, int r) {
   const int tiles = ((NB + kTM - 1) / kTM) * ((2 * r) / kTN);
-  const int smax = (512 + tiles - 1) / tiles;
+  const int smax = (256 + tiles - 1) / tiles;
   return ((size_t)smax + 1) * NB * 2 * r * sizeof(float);
 }
 

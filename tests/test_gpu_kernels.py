@@ -148,8 +148,8 @@ def test_readout_changed_flag_stays_clear_at_a_fixed_point():
     assert int(changed.item()) == 0 and np.array_equal(blk.cpu().numpy(), blk0)
 
 
-# the last two run the GEMM's deep path (every slice's chunks loaded together): 8 chunks per
-# slice, and 10 (8 + a remainder of 2) with a ragged last row tile (528 slot rows)
+# the last two run the GEMM's deep path (a slice's chunks loaded 8 at a time): 16 chunks per
+# slice, and 20 (16 + a remainder of 4) with a ragged last row tile (528 slot rows)
 @pytest.mark.parametrize("H,r,N,B", [(256, 64, 3, 4), (4096, 256, 3, 16), (320, 128, 2, 7),
                                      (4096, 256, 32, 16), (5120, 256, 33, 16)])
 def test_hidden_cache_parity(H, r, N, B):
