@@ -11,6 +11,7 @@
 // slot mean of the down_g half and applies in_proj's hidden half in fp32, one block of slots per
 // workgroup.
 #include "launch.hpp"
+#include "block_start.hpp"
 #include "xpress_common.hpp"
 
 namespace xpress {
@@ -29,17 +30,17 @@ constexpr int kLQ = kTK / 8 + 1;  // padded LDS row stride (uint4)
 // from HBM, so the slice's loads must be in flight together rather than one chunk at a time.
 constexpr int kDepth = 8;
 
-__global__ __launch_bounds__(256) void hidden_gemm_kernel(const uint16_t* __restrict__ h,
-                                                          const uint16_t* __restrict__ down_h,
-                                                          const uint16_t* __restrict__ down_g,
-                                                          int NB, int H, int r, int kslice,
-                                                          float* __restrict__ part) {
+__device__ __forceinline__ void hidden_gemm_tile(const uint16_t* __restrict__ h,
+                                                 const uint16_t* __restrict__ down_h,
+                                                 const uint16_t* __restrict__ down_g, int NB,
+                                                 int H, int r, int kslice,
+                                                 float* __restrict__ part, int bx, int by,
+                                                 int ks) {
   __shared__ u32x4 s_a[kTM * kLQ];
   __shared__ u32x4 s_b[kTN * kLQ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-  const int m0 = blockIdx.x * kTM, n0 = blockIdx.y * kTN;
-  const int ks = blockIdx.z;
+  const int m0 = bx * kTM, n0 = by * kTN;
   const int kbeg = ks * kslice, kend = min(H, kbeg + kslice);
   const int nch = (kend - kbeg) / kTK;  // H and kslice are multiples of kTK
   const int l32 = lane & 31, half = lane >> 5;
@@ -113,6 +114,29 @@ __global__ __launch_bounds__(256) void hidden_gemm_kernel(const uint16_t* __rest
     const int row = m0 + 32 * wm + 8 * (v / 4) + 4 * half + (v % 4);
     if (row < NB) out[(int64_t)row * (2 * r) + col] = acc[v];
   }
+}
+
+__global__ __launch_bounds__(256) void hidden_gemm_kernel(const uint16_t* __restrict__ h,
+                                                          const uint16_t* __restrict__ down_h,
+                                                          const uint16_t* __restrict__ down_g,
+                                                          int NB, int H, int r, int kslice,
+                                                          float* __restrict__ part) {
+  hidden_gemm_tile(h, down_h, down_g, NB, H, r, kslice, part, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// The start of a step in one launch: workgroups [0, g1) are the hidden GEMM's tiles (mt x nt
+// tiles per split, split-major), the rest the starting block's rows. The two are independent; the
+// GEMM is latency-bound and the starting block bandwidth-bound, so they overlap well.
+__global__ __launch_bounds__(256) void step_start_kernel(
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ down_h,
+    const uint16_t* __restrict__ down_g, int NB, int H, int r, int kslice,
+    float* __restrict__ part, int g1, int mt, int nt, const uint16_t* __restrict__ base,
+    int64_t ld, const int64_t* __restrict__ anchor, int B, int64_t V, int64_t* __restrict__ blk) {
+  const int i = blockIdx.x;
+  if (i < g1)
+    hidden_gemm_tile(h, down_h, down_g, NB, H, r, kslice, part, i % mt, (i / mt) % nt, i / (mt * nt));
+  else
+    initial_block_row(base, ld, anchor, B, V, blk, i - g1);
 }
 
 // One workgroup per (block n, 64 output channels), in fp32:
@@ -249,6 +273,20 @@ hipError_t launch_hidden_gemm(const uint16_t* h, const uint16_t* down_h, const u
   dim3 grid((NB + kTM - 1) / kTM, (2 * r) / kTN, ns);
   hipLaunchKernelGGL(hidden_gemm_kernel, grid, dim3(256), 0, s, h, down_h, down_g, NB, H, r,
                      kslice, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_start(const uint16_t* h, const uint16_t* down_h, const uint16_t* down_g,
+                             int NB, int H, int r, float* part, const uint16_t* base, int64_t ld,
+                             const int64_t* anchor, int N, int B, int64_t V, int64_t* blk,
+                             hipStream_t s) {
+  const int ns = hidden_splits(NB, H, r);
+  const int kslice = hidden_chunks_per_split(NB, H, r) * kTK;
+  const int mt = (NB + kTM - 1) / kTM, nt = (2 * r) / kTN;
+  const int g1 = mt * nt * ns;
+  hipLaunchKernelGGL(step_start_kernel, dim3((unsigned)(g1 + N * (B - 1))), dim3(256), 0, s, h,
+                     down_h, down_g, NB, H, r, kslice, part, g1, mt, nt, base, ld, anchor, B, V,
+                     blk);
   return hipGetLastError();
 }
 

@@ -21,6 +21,11 @@ hipError_t launch_hidden_gemm(const uint16_t* h, const uint16_t* down_h, const u
 // K1b: reduce the partials (fixed order), then
 // xh[n, b] = in_proj[:, :r] . hdg[n, b, :r] + in_proj[:, r:2r] . mean_b hdg[n, b, r:]; `part` is
 // the scratch of launch_hidden_gemm (hidden_scratch_bytes long).
+// K1a + K2 in one launch (independent): the hidden GEMM's tiles and the starting block's rows.
+hipError_t launch_step_start(const uint16_t* h, const uint16_t* down_h, const uint16_t* down_g,
+                             int NB, int H, int r, float* part, const uint16_t* base, int64_t ld,
+                             const int64_t* anchor, int N, int B, int64_t V, int64_t* blk,
+                             hipStream_t s);
 hipError_t launch_hidden_project(const float* part, int H, const uint16_t* in_proj, int N, int B,
                                  int r, float* xh, hipStream_t s);
 // K2: blk[n, 0] = anchor[n]; blk[n, b] = argmax_v base[n*(B-1)+b-1, v].

@@ -358,16 +358,18 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
   float* xh = at<float>(ws, L.xh);
   xpress_bf16* lat = at<xpress_bf16>(ws, L.lat);
   void* lscr = at<char>(ws, L.lscr);
-  XP_TRY(xpress::launch_hidden_gemm(h, w->down_h, w->down_g, N * B, w->H, r, hdg, s), "hidden gemm");
-  XP_TRY(xpress::launch_hidden_project(hdg, w->H, w->in_proj, N, B, r, xh, s), "hidden project");
   const int c = C > 0 ? (int)(C < V ? C : V) : 0;
   const bool init = (flags & XPRESS_INIT_FROM_BASE) != 0;
   // the starting block: with candidates, the selection writes it (the best candidate is the
-  // row's argmax; the anchor too)
+  // row's argmax; the anchor too); without, one launch computes it beside the hidden GEMM
   if (init && c == 0)
-    XP_TRY(xpress::launch_initial_block(base, base_ld, anchor, N, B, V, blk, s), "initial block");
-  else if (!init)
-    XP_TRY(xpress::launch_set_anchor(anchor, N, B, blk, s), "set anchor");
+    XP_TRY(xpress::launch_step_start(h, w->down_h, w->down_g, N * B, w->H, r, hdg, base, base_ld,
+                                     anchor, N, B, V, blk, s),
+           "hidden gemm + starting block");
+  else
+    XP_TRY(xpress::launch_hidden_gemm(h, w->down_h, w->down_g, N * B, w->H, r, hdg, s), "hidden gemm");
+  XP_TRY(xpress::launch_hidden_project(hdg, w->H, w->in_proj, N, B, r, xh, s), "hidden project");
+  if (!init) XP_TRY(xpress::launch_set_anchor(anchor, N, B, blk, s), "set anchor");
   int64_t* cand = at<int64_t>(ws, L.cand);
   xpress_bf16* base_c = at<xpress_bf16>(ws, L.base_c);
   xpress_bf16* w2c = at<xpress_bf16>(ws, L.w2c);
