@@ -156,7 +156,11 @@ xpress_status xpress_argmax_reduce(const uint32_t* part, int32_t ntiles, int32_t
  * cand[p] = the c = min(C, V) ids with the largest base[p, :] under the order (value descending,
  * id ascending), stored in ascending id order; base_c[p, k] = base[p, cand[p, k]];
  * w2c[p, k, :] = w2[cand[p, k], :].
- * cand: [N*(B-1), c] int64; base_c: [N*(B-1), c] bf16; w2c: [N*(B-1), c, r] bf16 (written). */
+ * cand: [N*(B-1), c] int64; base_c: [N*(B-1), c] bf16; w2c: [N*(B-1), c, r] bf16 (written).
+ * ws (optional, may be NULL): device scratch; when it is 16-byte aligned and holds at least
+ * N*(B-1) * 8*ceil(ceil(V/8)/8) * 2 bytes, the selection keeps per-chunk maxima there and its
+ * second pass over base reads only the chunks that can hold an answer (same result, less
+ * traffic); otherwise it reads base twice. xpress_jacobi_step's workspace includes this. */
 xpress_status xpress_topc_prepare(const xpress_weights* w, const xpress_bf16* base,
                                   int64_t base_ld, int32_t N, int32_t C, int64_t* cand,
                                   xpress_bf16* base_c, xpress_bf16* w2c, void* ws,

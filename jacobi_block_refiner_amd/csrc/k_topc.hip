@@ -236,7 +236,8 @@ __device__ __forceinline__ uint32_t radix_kth(const uint32_t* keys, int n, int k
 
 __device__ __forceinline__ void topc_select_row(const uint16_t* __restrict__ base, int64_t ld,
                                                 int64_t V, int c, int64_t* __restrict__ cand,
-                                                uint16_t* __restrict__ base_c) {
+                                                uint16_t* __restrict__ base_c,
+                                                uint16_t* __restrict__ cmax) {
   __shared__ uint32_t s_hist[512];
   __shared__ int s_tmp[4];
   __shared__ uint32_t s_par[4];
@@ -245,6 +246,8 @@ __device__ __forceinline__ void topc_select_row(const uint16_t* __restrict__ bas
   __shared__ int s_eq[kEq];         // ids of the boundary ties
   __shared__ __align__(16) int s_sel[1024];  // ids of the winners
   __shared__ int s_cnt[4];
+  constexpr int kHC = 1024;         // chunk-list capacity per wave
+  __shared__ int s_hc[4][kHC];      // chunks whose maximum can hold an answer, per wave
   const int p = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const uint16_t* row = base + (int64_t)p * ld;
   int64_t* out_id = cand + (int64_t)p * c;
@@ -285,6 +288,10 @@ __device__ __forceinline__ void topc_select_row(const uint16_t* __restrict__ bas
   auto key1_of = [](float v) __attribute__((always_inline)) {
     return order_key(__float_as_uint(v) >> 16) + 1;
   };
+  // chunk maxima (bf16 bits), written by pass 1 when a buffer is given, read back by pass 3 so
+  // that it re-reads only the chunks that can hold an answer
+  const int64_t nchunk8 = (nchunk + 7) / 8 * 8;
+  uint16_t* cmax_row = cmax ? cmax + (int64_t)blockIdx.x * nchunk8 : nullptr;
   // 1. group maxima: thread tid visits chunks tid + 256 i; groups of gv visits (<= 8 groups)
   const int nv_max = (int)((nchunk + 255) / 256);
   const int gv = (nv_max + 7) / 8;
@@ -300,8 +307,10 @@ __device__ __forceinline__ void topc_select_row(const uint16_t* __restrict__ bas
         if (q < nchunk) {
           float x[8];
           widen(q, raw[u], x);
-          gm = fmaxf(fmaxf(fmaxf(gm, x[0]), fmaxf(x[1], x[2])),
-                     fmaxf(fmaxf(x[3], x[4]), fmaxf(fmaxf(x[5], x[6]), x[7])));
+          const float cm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                 fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+          if (cmax_row) cmax_row[q] = (uint16_t)(__float_as_uint(cm) >> 16);  // -inf: 0xff80
+          gm = fmaxf(gm, cm);
           if (++inside == gv) {
             s_key[tid * 8 + g] = gm > -INFINITY ? key1_of(gm) : 0u;
             ++g;
@@ -313,7 +322,10 @@ __device__ __forceinline__ void topc_select_row(const uint16_t* __restrict__ bas
     }
     if (inside) s_key[tid * 8 + g++] = gm > -INFINITY ? key1_of(gm) : 0u;
     for (; g < 8; ++g) s_key[tid * 8 + g] = 0;
+    if (cmax_row)  // the padding up to a multiple of 8 chunk maxima: -inf
+      for (int64_t q = nchunk + tid; q < nchunk8; q += 256) cmax_row[q] = 0xff80u;
   }
+  __threadfence_block();
   __syncthreads();
   // 2. t0: the c-th largest group maximum (every group maximum is non-empty if its group had an
   // id below V; with fewer than c of them t0 is the smallest key, 1)
@@ -340,6 +352,66 @@ __device__ __forceinline__ void topc_select_row(const uint16_t* __restrict__ bas
   constexpr int kSeg = kBuf / 4;
   const int wave = tid >> 6;
   int wcnt = 0;  // wave-uniform
+  // With chunk maxima: (3a) each wave lists the chunks whose maximum is >= v0 (8 maxima per
+  // 16-byte read), then (3b) reads only those chunks, one per lane, and appends their elements
+  // >= v0 as below. A list that would overflow sends the row to the full pass instead.
+  bool full_pass = cmax_row == nullptr;
+  if (!full_pass) {
+    int hc = 0;  // wave-uniform (lane 0, which runs every iteration any lane runs, holds it)
+    const uint4* cm4 = reinterpret_cast<const uint4*>(cmax_row);
+    const int64_t n8 = nchunk8 / 8;
+    for (int64_t g0 = tid; g0 < n8; g0 += 256 * kLB) {
+      uint4 m8[kLB];
+#pragma unroll
+      for (int u = 0; u < kLB; ++u) {
+        const int64_t g = g0 + 256 * u;
+        m8[u] = g < n8 ? cm4[g] : make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
+      }
+#pragma unroll
+      for (int u = 0; u < kLB; ++u) {
+        const int64_t g = g0 + 256 * u;
+        const uint32_t w[4] = {m8[u].x, m8[u].y, m8[u].z, m8[u].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t b = (e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16);
+          const bool hit = __uint_as_float(b) >= v0;
+          const uint64_t m = __ballot(hit);
+          if (m) {
+            const int pos = hc + __popcll(m & ((1ull << lane) - 1));
+            if (hit && pos < kHC) s_hc[wave][pos] = (int)(g * 8 + e);
+            hc += __popcll(m);
+          }
+        }
+      }
+    }
+    if (lane == 0) s_cnt[wave] = hc;
+    __syncthreads();
+    hc = s_cnt[wave];  // every lane: the wave's count
+    full_pass = max(max(s_cnt[0], s_cnt[1]), max(s_cnt[2], s_cnt[3])) > kHC;  // uniform
+    if (!full_pass) {
+      for (int i0 = 0; i0 < hc; i0 += 64) {  // wave-uniform bound
+        const bool has = i0 + lane < hc;
+        const int64_t q = has ? s_hc[wave][i0 + lane] : nchunk;  // past the row: all -inf
+        float x[8];
+        widen(q, has ? row4[q] : make_uint4(0, 0, 0, 0), x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool hit = x[e] >= v0;
+          const uint64_t m = __ballot(hit);
+          if (m) {
+            const int pos = wcnt + __popcll(m & ((1ull << lane) - 1));
+            if (hit && pos < kSeg) {
+              s_key[wave * kSeg + pos] = key1_of(x[e]);
+              s_id[wave * kSeg + pos] = (int)(q * 8 + e);
+            }
+            wcnt += __popcll(m);
+          }
+        }
+      }
+    }
+    __syncthreads();  // s_cnt is reused below
+  }
+  if (full_pass)
   for (int64_t q0 = tid; q0 < nchunk; q0 += 256 * kLB) {
     uint4 raw[kLB];
     load_batch(q0, raw);
@@ -455,8 +527,9 @@ __global__ __launch_bounds__(256) void topc_select_kernel(const uint16_t* __rest
                                                           int64_t* __restrict__ cand,
                                                           uint16_t* __restrict__ base_c,
                                                           const int64_t* __restrict__ anchor,
-                                                          int64_t* __restrict__ blk, int B) {
-  topc_select_row(base, ld, V, c, cand, base_c);
+                                                          int64_t* __restrict__ blk, int B,
+                                                          uint16_t* __restrict__ cmax) {
+  topc_select_row(base, ld, V, c, cand, base_c, cmax);
   if (!blk) return;
   // the block's first row also stores the anchor in slot 0
   if (blockIdx.x % (B - 1) == 0 && threadIdx.x == 0)
@@ -584,10 +657,15 @@ __global__ __launch_bounds__(256) void topc_readout_kernel(
 
 hipError_t launch_topc_select(const uint16_t* base, int64_t ld, int rows, int64_t V, int c,
                               int64_t* cand, uint16_t* base_c, const int64_t* anchor,
-                              int64_t* blk, int B, hipStream_t s) {
+                              int64_t* blk, int B, uint16_t* cmax, hipStream_t s) {
   hipLaunchKernelGGL(topc_select_kernel, dim3(rows), dim3(256), 0, s, base, ld, V, c, cand, base_c,
-                     anchor, blk, B);
+                     anchor, blk, B, cmax);
   return hipGetLastError();
+}
+
+size_t topc_select_scratch_bytes(int rows, int64_t V) {
+  const int64_t nchunk8 = ((V + 7) / 8 + 7) / 8 * 8;
+  return (size_t)rows * (size_t)nchunk8 * 2;
 }
 
 hipError_t launch_topc_gather(const int64_t* cand, const uint16_t* w2, int rows, int c, int r,

@@ -51,9 +51,12 @@ hipError_t launch_argmax_reduce(const uint2* part, int ntiles, int rows, int B, 
 // K3: top-C candidate selection (+ base_c) and the w2 gather. With blk non-null the selection
 // also writes the starting block: each row's best candidate into blk[n, 1 + p % (B-1)] and the
 // anchor into blk[n, 0].
+// cmax (nullable, 16-byte aligned, topc_select_scratch_bytes long): per-chunk maxima that let
+// the selection's second pass re-read only the chunks that can hold an answer.
 hipError_t launch_topc_select(const uint16_t* base, int64_t ld, int rows, int64_t V, int c,
                               int64_t* cand, uint16_t* base_c, const int64_t* anchor, int64_t* blk,
-                              int B, hipStream_t s);
+                              int B, uint16_t* cmax, hipStream_t s);
+size_t topc_select_scratch_bytes(int rows, int64_t V);
 hipError_t launch_topc_gather(const int64_t* cand, const uint16_t* w2, int rows, int c, int r,
                               uint16_t* w2c, hipStream_t s);
 // K7: top-C gathered GEMV + argmax + candidate -> vocabulary id -> blk.

@@ -100,7 +100,7 @@ xpress_status check_base(const xpress_bf16* base, int64_t ld, int64_t V) {
 // Workspace regions of a call with N blocks.
 struct Layout {
   size_t hdg = 0, xh = 0, lat = 0, lscr = 0, part = 0, flags = 0, cand = 0, base_c = 0, w2c = 0,
-         total = 0;
+         cmax = 0, total = 0;
 };
 
 
@@ -124,6 +124,7 @@ Layout step_layout(int N, int B, int r, int H, int64_t V, int C, int K) {
   L.cand = take(rows * c * sizeof(int64_t));
   L.base_c = take(rows * c * 2);
   L.w2c = take(rows * c * r * 2);
+  L.cmax = take(C > 0 ? xpress::topc_select_scratch_bytes((int)rows, V) : 0);
   L.total = off;
   return L;
 }
@@ -289,8 +290,6 @@ xpress_status xpress_topc_prepare(const xpress_weights* w, const xpress_bf16* ba
                                   int64_t base_ld, int32_t N, int32_t C, int64_t* cand,
                                   xpress_bf16* base_c, xpress_bf16* w2c, void* ws,
                                   size_t ws_bytes, xpress_stream stream) {
-  (void)ws;
-  (void)ws_bytes;
   xpress_status st = check_weights(w, false, false, true);
   if (st != XPRESS_OK) return st;
   if (N < 0) return fail(XPRESS_ERR_ARG, "N=%d < 0", N);
@@ -304,8 +303,11 @@ xpress_status xpress_topc_prepare(const xpress_weights* w, const xpress_bf16* ba
   const int c = (int)(C < w->V ? C : w->V);
   const int rows = N * (w->B - 1);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // the workspace, when it is large enough (and aligned), holds the selection's chunk maxima
+  const bool ws_ok = ws != nullptr && (reinterpret_cast<uintptr_t>(ws) & 15) == 0 &&
+                     ws_bytes >= xpress::topc_select_scratch_bytes(rows, w->V);
   XP_TRY(xpress::launch_topc_select(base, base_ld, rows, w->V, c, cand, base_c, nullptr, nullptr, 0,
-                                    s),
+                                    ws_ok ? static_cast<uint16_t*>(ws) : nullptr, s),
          "top-C select");
   XP_TRY(xpress::launch_topc_gather(cand, w->w2, rows, c, w->r, w2c, s), "top-C gather");
   return XPRESS_OK;
@@ -375,7 +377,7 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
   xpress_bf16* w2c = at<xpress_bf16>(ws, L.w2c);
   if (c > 0) {
     XP_TRY(xpress::launch_topc_select(base, base_ld, rows, V, c, cand, base_c, anchor,
-                                      init ? blk : nullptr, B, s),
+                                      init ? blk : nullptr, B, at<uint16_t>(ws, L.cmax), s),
            "top-C select");
     XP_TRY(xpress::launch_topc_gather(cand, w->w2, rows, c, r, w2c, s), "top-C gather");
   }

@@ -309,8 +309,16 @@ def test_step_fixed_k_runs_every_pass_and_is_deterministic():
 # ----------------------------------------------------------------------------------------------
 # top-C
 
+def _select_scratch(rows, V):
+    """Scratch for the selection's chunk maxima (rows x 8-aligned chunk count, 2 bytes each): with
+    it, the second pass re-reads only the chunks that can hold an answer."""
+    nchunk8 = ((V + 7) // 8 + 7) // 8 * 8
+    return torch.empty(rows * nchunk8 * 2, dtype=torch.uint8, device="cuda")
+
+
+@pytest.mark.parametrize("chunk_maxima", [False, True])
 @pytest.mark.parametrize("C,V", [(64, 5003), (512, 8192), (700, 700), (1, 3000), (5, 7), (40, 33)])
-def test_topc_prepare_exact(C, V):
+def test_topc_prepare_exact(C, V, chunk_maxima):
     rng = np.random.default_rng(6)
     N, B, r = 3, 16, 64
     rows = N * (B - 1)
@@ -323,7 +331,8 @@ def test_topc_prepare_exact(C, V):
     cand = torch.empty(rows, c, dtype=torch.int64, device="cuda")
     base_c = torch.empty(rows, c, dtype=torch.bfloat16, device="cuda")
     w2c = torch.empty(rows, c, r, dtype=torch.bfloat16, device="cuda")
-    xpress.topc_prepare(w, upload.base_logits(base), N, C, cand, base_c, w2c)
+    ws = _select_scratch(rows, V) if chunk_maxima else None
+    xpress.topc_prepare(w, upload.base_logits(base), N, C, cand, base_c, w2c, ws)
     torch.cuda.synchronize()
     want = O.topc_select(base, C)
     got = cand.cpu().numpy()
@@ -332,8 +341,9 @@ def test_topc_prepare_exact(C, V):
     assert np.array_equal(w2c.float().cpu().numpy(), w2[want])
 
 
+@pytest.mark.parametrize("chunk_maxima", [False, True])
 @pytest.mark.parametrize("C,V", [(512, 8192), (64, 5003), (1024, 20000)])
-def test_topc_prepare_adversarial_rows(C, V):
+def test_topc_prepare_adversarial_rows(C, V, chunk_maxima):
     """Rows that defeat a per-thread shortlist (sorted rows, the answer concentrated in the ids one
     thread visits, very few distinct values) must still give the exact candidate sets."""
     rng = np.random.default_rng(11)
@@ -358,7 +368,8 @@ def test_topc_prepare_adversarial_rows(C, V):
     cand = torch.empty(rows, c, dtype=torch.int64, device="cuda")
     base_c = torch.empty(rows, c, dtype=torch.bfloat16, device="cuda")
     w2c = torch.empty(rows, c, r, dtype=torch.bfloat16, device="cuda")
-    xpress.topc_prepare(w, upload.base_logits(base), N, C, cand, base_c, w2c)
+    ws = _select_scratch(rows, V) if chunk_maxima else None
+    xpress.topc_prepare(w, upload.base_logits(base), N, C, cand, base_c, w2c, ws)
     torch.cuda.synchronize()
     want = O.topc_select(base, C)
     got = cand.cpu().numpy()
