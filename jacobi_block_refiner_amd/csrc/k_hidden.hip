@@ -22,6 +22,7 @@ constexpr int kTM = 64;  // rows (slots) per workgroup
 constexpr int kTN = 64;  // output columns per workgroup
 constexpr int kTK = 64;  // k chunk
 constexpr int kLQ = kTK / 8 + 1;  // padded LDS row stride (uint4)
+constexpr int kMaxSplits = 8;     // split-K slices at most
 
 // Split-K partial products: part[ks, m, j] = sum_{k in slice ks} h[m, k] * Wcat[j, k].
 // 4 waves as a 2 x 2 grid of 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16, layout as in the
@@ -242,7 +243,14 @@ __global__ __launch_bounds__(256) void hidden_project_kernel(const float* __rest
 int hidden_chunks_per_split(int NB, int H, int r) {
   const int tiles = ((NB + kTM - 1) / kTM) * ((2 * r) / kTN);
   const int kchunks = H / kTK;
-  int s = (256 + tiles - 1) / tiles;  // aim for >= 256 workgroups (one per CU)
+  // aim for >= 256 workgroups (one per CU), but at most kMaxSplits slices: every slice is one
+  // more partial for the projection to read back (with few slot rows the GEMM is latency-bound
+  // whatever the split)
+  int s = (256 + tiles - 1) / tiles;
+  if (s > kMaxSplits) s = kMaxSplits;
+  // few slot rows: the projection's few workgroups each read every slice back, so fewer slices
+  const int srow = max(2, (NB + kTM - 1) / kTM);
+  if (s > srow) s = srow;
   if (s > kchunks) s = kchunks;
   if (s < 1) s = 1;
   return (kchunks + s - 1) / s;
@@ -262,7 +270,7 @@ size_t hidden_scratch_bytes(int NB, int H, int r) {
 // number of splits, whatever H is).
 size_t hidden_scratch_bytes_any_h(int NB, int r) {
   const int tiles = ((NB + kTM - 1) / kTM) * ((2 * r) / kTN);
-  const int smax = (256 + tiles - 1) / tiles;
+  const int smax = min((256 + tiles - 1) / tiles, kMaxSplits);
   return ((size_t)smax + 1) * NB * 2 * r * sizeof(float);
 }
 
