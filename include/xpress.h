@@ -77,6 +77,14 @@ typedef struct {
   const xpress_bf16* w_up;    /* [M, r]                                                        */
   const xpress_bf16* w_down;  /* [r, M]                                                        */
   const xpress_bf16* w2;      /* [V, r]   readout                                              */
+  const float* w1p;           /* [V, r]   OPTIONAL (NULL: not used), fp32: the embedding table with
+                                          in_proj's embedding block applied,
+                                          w1p[v, c] = sum_k in_proj[c, 2r+k] * w1[v, k]
+                                          (xpress_fold_embedding). When given, the latent stage
+                                          gathers its rows instead of projecting w1's rows every
+                                          pass and runs as two launches instead of three;
+                                          results agree with the NULL path within fp32
+                                          rounding                                              */
 } xpress_weights;
 
 /* Flags of xpress_jacobi_step. */
@@ -99,6 +107,14 @@ xpress_status xpress_workspace_size(int32_t n_max, int32_t B, int32_t r, int64_t
  * alias raw). */
 xpress_status xpress_fold_mixer(const xpress_bf16* raw, int32_t r, int32_t B, xpress_bf16* mix_L,
                                 xpress_stream stream);
+
+/* Projected embedding table (the embedding block of in_proj that qwen3_xpress page,
+ * jacobi_refine_greedy, applies to the gathered token embeddings every pass, applied here once
+ * to every row of w1): w1p[v, c] = sum_k in_proj[c, 2r + k] * w1[v, k] for v < V, c < r, with
+ * bf16 operands and fp32 accumulation. Reads w->w1, w->in_proj, w->r, w->V (w->w1p is ignored).
+ * w1p: [V, r] fp32 (written, caller-owned, 16-byte aligned; 4*V*r bytes). Pass it as
+ * xpress_weights.w1p afterwards; recompute it whenever w1 or in_proj change. */
+xpress_status xpress_fold_embedding(const xpress_weights* w, float* w1p, xpress_stream stream);
 
 /* Hidden cache (qwen3_xpress page, hidden_cache, and the hidden half of in_proj that
  * jacobi_refine_greedy applies once per step):

@@ -32,12 +32,61 @@ namespace xpress {
 
 namespace {
 
+// The token each of the 16 slots of block n reads (slot 0: am1[n], slot b: blk[n, b-1]; -1 for
+// slots past B) into tok (LDS). With `part` (inside a step, pass >= 1) the block first finishes
+// the previous pass: the partial winners of its readout rows (range-major, `ntiles` <= 256
+// ranges) are reduced to the block's new tokens -- the work of the argmax-reduce kernel for these
+// rows, without its launch. Every workgroup of the block reduces them (the same result); the one
+// with `writer` set writes them into blk and raises flags[pass-1] on a change. Called by all 256
+// threads; the caller synchronises before reading tok.
+__device__ __forceinline__ void block_tokens(const uint2* __restrict__ part, int ntiles, int rows,
+                                             int64_t* __restrict__ blk,
+                                             const int64_t* __restrict__ am1, int n, int B,
+                                             bool writer, int32_t* __restrict__ flags, int pass,
+                                             int64_t* tok) {
+  const int tid = threadIdx.x;
+  if (part) {
+    // all 16 loads per thread are issued before the first merge (clamped repeats change nothing)
+    const int rb = tid >> 4, j = tid & 15;  // readout row rb of the block, range slice j
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    const uint2* pr = part + (int64_t)n * (B - 1) + min(rb, B - 2);
+    uint2 q[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) q[k] = pr[(int64_t)min(j + 16 * k, ntiles - 1) * rows];
+    if (rb < B - 1) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) argmax_merge(bv, bi, __uint_as_float(q[k].x), (int)q[k].y);
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) {  // the 16 slices are 16 consecutive lanes
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      argmax_merge(bv, bi, ov, oi);
+    }
+    if (j == 0 && rb < B - 1) {
+      const int64_t nv = (int64_t)bi;
+      if (writer) {
+        int64_t* slot = blk + (int64_t)n * B + 1 + rb;
+        if (*slot != nv) {
+          *slot = nv;
+          if (flags) __hip_atomic_store(flags + pass - 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      if (rb + 2 < B) tok[rb + 2] = nv;  // slot b reads blk[b-1]
+    }
+    if (tid == 0) {
+      tok[0] = am1[n];
+      tok[1] = blk[(int64_t)n * B];
+    }
+    if (tid >= B && tid < 16) tok[tid] = -1;
+  } else if (tid < 16) {
+    tok[tid] = tid == 0 ? am1[n] : (tid < B ? blk[(int64_t)n * B + tid - 1] : -1);
+  }
+}
+
 // Steps 1-3 for one block and 64 channels (blockIdx.y); 4 waves. With `part` given (inside a
-// step), the block first finishes the previous pass: the partial winners of its readout rows
-// (range-major, `ntiles` <= 256 ranges) are reduced to the block's new tokens -- the work of the
-// argmax-reduce kernel for these rows, without its launch. Every channel slice of the block
-// reduces them (the same result); slice 0 writes them into blk and raises flags[pass-1] on a
-// change.
+// step), the block first finishes the previous pass (block_tokens); slice 0 writes blk.
 template <int R>
 __global__ __launch_bounds__(256) void latent_mix_kernel(
     const uint2* __restrict__ part, int ntiles, int rows, int64_t* __restrict__ blk,
@@ -66,44 +115,7 @@ __global__ __launch_bounds__(256) void latent_mix_kernel(
       }
   }
 
-  // step 0 (fused only): new tokens of the block; all 16 loads per thread are issued before the
-  // first merge (clamped repeats change nothing)
-  if (part) {
-    const int rb = tid >> 4, j = tid & 15;  // readout row rb of the block, range slice j
-    float bv = -INFINITY;
-    int bi = INT_MAX;
-    const uint2* pr = part + (int64_t)n * (B - 1) + min(rb, B - 2);
-    uint2 q[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) q[k] = pr[(int64_t)min(j + 16 * k, ntiles - 1) * rows];
-    if (rb < B - 1) {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) argmax_merge(bv, bi, __uint_as_float(q[k].x), (int)q[k].y);
-    }
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) {  // the 16 slices are 16 consecutive lanes
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      argmax_merge(bv, bi, ov, oi);
-    }
-    if (j == 0 && rb < B - 1) {
-      const int64_t nv = (int64_t)bi;
-      if (blockIdx.y == 0) {
-        int64_t* slot = blk + (int64_t)n * B + 1 + rb;
-        if (*slot != nv) {
-          *slot = nv;
-          if (flags) __hip_atomic_store(flags + pass - 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-      if (rb + 2 < B) s_tok[rb + 2] = nv;  // slot b reads blk[b-1]
-    }
-    if (tid == 0) {
-      s_tok[0] = am1[n];
-      s_tok[1] = blk[(int64_t)n * B];
-    }
-  } else if (tid < 16) {
-    s_tok[tid] = tid == 0 ? am1[n] : (tid < B ? blk[(int64_t)n * B + tid - 1] : -1);
-  }
+  block_tokens(part, ntiles, rows, blk, am1, n, B, blockIdx.y == 0, flags, pass, s_tok);
   __syncthreads();
 
   // steps 1-2: x[slot, c] = xh[slot, c] + sum_k P_e[c, k] w1[tok(slot), k]; wave w computes the
@@ -255,6 +267,232 @@ __global__ __launch_bounds__(256) void latent_down_kernel(
     }
 }
 
+
+// Embedding table with the embedding block of in_proj applied (done once per weight set; the
+// pass then gathers rows instead of projecting them):
+//   w1p[v, c] = sum_k in_proj[c, 2r + k] * w1[v, k]    (fp32)
+// Each wave computes 64 vocabulary rows (four 16-row MFMA tiles sharing every in_proj fragment)
+// for all r channels.
+template <int R>
+__global__ __launch_bounds__(256) void fold_embedding_kernel(const uint16_t* __restrict__ w1,
+                                                             const uint16_t* __restrict__ in_proj,
+                                                             int64_t V, float* __restrict__ w1p) {
+  constexpr int KS = R / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, q4 = lane >> 4;
+  const int64_t v0 = ((int64_t)blockIdx.x * 4 + wave) * 64;
+  if (v0 >= V) return;  // wave-uniform; the kernel has no barrier
+  bf16x8 a[4][KS];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int64_t row = min(v0 + 16 * t + l16, V - 1);
+    const uint4* src = reinterpret_cast<const uint4*>(w1 + row * R);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) a[t][s] = as_bf16x8(src[4 * s + q4]);
+  }
+  for (int ct = 0; ct < R / 16; ++ct) {
+    const int c = ct * 16 + l16;
+    const uint4* prow = reinterpret_cast<const uint4*>(in_proj + (int64_t)c * 3 * R + 2 * R);
+    bf16x8 b[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) b[s] = as_bf16x8(prow[4 * s + q4]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) acc = mfma16x16x32(a[t][s], b[s], acc);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t row = v0 + 16 * t + 4 * q4 + v;
+        if (row < V) w1p[row * R + c] = acc[v];
+      }
+    }
+  }
+}
+
+// The latent stage from the projected embedding table w1p, in two launches. Workgroup (n, g)
+// of latent_share_kernel takes block n and the 64 SwiGLU units g*64 .. g*64+63 (G = M/64
+// workgroups per block):
+//   0. the block's tokens (block_tokens; inside a step this finishes the previous pass);
+//   1. x[b, c] = xh[b, c] + w1p[tok(b), c]            thread c < r, all 16 slots in registers;
+//   2. u[b, c] = sum_{j<=b} L[b, j, c] x[j, c]          same thread, taps in registers;
+//   3. a = w_gate[units] . u, e = w_up[units] . u,  s = silu(a) * e   (16x16x32 MFMAs);
+//   4. share_g = w_down[:, units] . s (+ u for g = 0), written to dpart for slots 1..B-1.
+// latent_sum_kernel then adds the G shares of each slot in slice order into lat (bf16): a fixed
+// summation order, and the kernel boundary orders the shares' stores before their loads.
+// Every workgroup of a block computes the same u (same inputs, same arithmetic).
+template <int R>
+__global__ __launch_bounds__(256) void latent_share_kernel(
+    const uint2* __restrict__ part, int ntiles, int rows, int64_t* __restrict__ blk,
+    const int64_t* __restrict__ am1, const float* __restrict__ xh, const float* __restrict__ w1p,
+    const uint16_t* __restrict__ mix_L, const uint16_t* __restrict__ w_gate,
+    const uint16_t* __restrict__ w_up, const uint16_t* __restrict__ w_down, int B, int M,
+    int64_t V, float* __restrict__ dpart, int32_t* __restrict__ flags, int pass) {
+  // inside a step: runs when the previous pass ran; on its own: when this pass runs
+  if (part ? pass_skipped(flags, pass - 1) : pass_skipped(flags, pass)) return;
+  constexpr int KS = R / 32;  // k steps of the gate/up products
+  constexpr int DT = R / 64;  // 16-channel output tiles of the down product per wave
+  constexpr int UP = R + 8;   // bf16 row pitch of s_u (one 16-byte pad per row)
+  constexpr int SP = 64 + 8;  // bf16 row pitch of s_s
+  __shared__ int64_t s_tok[16];
+  __shared__ float s_u32[16][R];
+  __shared__ __align__(16) uint16_t s_u[16][UP];
+  __shared__ __align__(16) uint16_t s_s[16][SP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
+  const int n = blockIdx.x, g = blockIdx.y, G = gridDim.y;
+  const bool chan = tid < R;  // thread tid owns channel tid in steps 1-2
+  const int c = min(tid, R - 1);
+
+  // Loads that do not depend on the tokens go first: the slice's gate/up rows, xh and the taps.
+  const int m = g * 64 + wave * 16 + l16;
+  bf16x8 gB[KS], uB[KS];
+  {
+    const uint4* grow = reinterpret_cast<const uint4*>(w_gate + (int64_t)m * R);
+    const uint4* urow = reinterpret_cast<const uint4*>(w_up + (int64_t)m * R);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      gB[s] = as_bf16x8(grow[4 * s + q4]);
+      uB[s] = as_bf16x8(urow[4 * s + q4]);
+    }
+  }
+  // Every load below is unconditional, at an index clamped into range, and a select drops what
+  // is not wanted: a load under a condition becomes a branch with its own wait, one memory
+  // round trip at a time.
+  float x[16];
+#pragma unroll
+  for (int b = 0; b < 16; ++b) x[b] = xh[((int64_t)n * B + min(b, B - 1)) * R + c];
+  // taps L[b, j, c] for j <= b (mix_L is [B, B, r], channel innermost: one coalesced 2-byte load
+  // across the wave per tap); slots b >= B are zeroed after the mixer
+  uint16_t tap[136];
+#pragma unroll
+  for (int b = 0, k = 0; b < 16; ++b)
+#pragma unroll
+    for (int j = 0; j <= b; ++j, ++k)
+      tap[k] = mix_L[((int64_t)min(b, B - 1) * B + min(j, B - 1)) * R + c];
+
+  block_tokens(part, ntiles, rows, blk, am1, n, B, g == 0, flags, pass, s_tok);
+  __syncthreads();
+
+  // steps 1-2
+  {
+    float e[16];
+    bool ok[16];
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      const int64_t t = s_tok[b];
+      ok[b] = b < B && t >= 0 && t < V;  // slots past B and ids outside [0, V): zero
+      e[b] = w1p[(ok[b] ? t : 0) * R + c];
+    }
+    // all 16 rows in flight before the first is used (otherwise each load sinks into the branch
+    // on b < B next to its use)
+    asm volatile("" : "+v"(e[0]), "+v"(e[1]), "+v"(e[2]), "+v"(e[3]), "+v"(e[4]), "+v"(e[5]),
+                 "+v"(e[6]), "+v"(e[7]), "+v"(e[8]), "+v"(e[9]), "+v"(e[10]), "+v"(e[11]),
+                 "+v"(e[12]), "+v"(e[13]), "+v"(e[14]), "+v"(e[15]));
+#pragma unroll
+    for (int b = 0; b < 16; ++b) x[b] = b < B ? x[b] + (ok[b] ? e[b] : 0.f) : 0.f;
+    float u[16];
+#pragma unroll
+    for (int b = 0, k = 0; b < 16; ++b) {
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j <= b; ++j, ++k) acc = fmaf(bf16_to_f32(tap[k]), x[j], acc);
+      u[b] = b < B ? acc : 0.f;
+    }
+    if (chan) {
+#pragma unroll
+      for (int b = 0; b < 16; ++b) {
+        s_u32[b][c] = u[b];
+        s_u[b][c] = f32_to_bf16(u[b]);
+      }
+    }
+  }
+  // the slice's w_down columns, needed after the gate products
+  bf16x8 dB[DT][2];
+#pragma unroll
+  for (int it = 0; it < DT; ++it) {
+    const int i = (wave * DT + it) * 16 + l16;
+    const uint4* drow = reinterpret_cast<const uint4*>(w_down + (int64_t)i * M + g * 64);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) dB[it][ks] = as_bf16x8(drow[4 * ks + q4]);
+  }
+  __syncthreads();
+
+  // step 3: units g*64 + 16*wave .. +15 for the 16 slot rows
+  {
+    f32x4 ag = {0, 0, 0, 0}, au = {0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&s_u[l16][32 * s + 8 * q4]));
+      ag = mfma16x16x32(a, gB[s], ag);
+      au = mfma16x16x32(a, uB[s], au);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float z = ag[v];
+      const float sg = z / (1.f + __expf(-z));
+      s_s[4 * q4 + v][16 * wave + l16] = f32_to_bf16(sg * au[v]);
+    }
+  }
+  __syncthreads();
+
+  // step 4: this slice's share of w_down . s for channels (wave*DT + it)*16 + l16; slice 0's
+  // share carries the residual u
+  {
+    bf16x8 a[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      a[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&s_s[l16][32 * ks + 8 * q4]));
+    float* dp = dpart + ((int64_t)n * G + g) * 16 * R;
+#pragma unroll
+    for (int it = 0; it < DT; ++it) {
+      f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) acc = mfma16x16x32(a[ks], dB[it][ks], acc);
+      const int i = (wave * DT + it) * 16 + l16;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int b = 4 * q4 + v;
+        if (b >= 1 && b < B) dp[b * R + i] = g == 0 ? s_u32[b][i] + acc[v] : acc[v];
+      }
+    }
+  }
+}
+
+// lat[n, b-1, c] = sum_g dpart[n, g, b, c] in slice order, for slots 1..B-1. Workgroup (n, y)
+// takes 256/(r/4) consecutive slots, one thread per 4 channels of a slot.
+template <int R>
+__global__ __launch_bounds__(256) void latent_sum_kernel(const float* __restrict__ dpart, int B,
+                                                         int G, uint16_t* __restrict__ lat,
+                                                         const int32_t* __restrict__ flags,
+                                                         int pass, int prev) {
+  if (prev ? pass_skipped(flags, pass - 1) : pass_skipped(flags, pass)) return;
+  constexpr int QR = R / 4;
+  constexpr int RPW = 256 / QR;
+  const int n = blockIdx.x, tid = threadIdx.x;
+  const int b = 1 + blockIdx.y * RPW + tid / QR, q = tid % QR;
+  if (b >= B) return;
+  const float4* dp4 = reinterpret_cast<const float4*>(dpart + (int64_t)n * G * 16 * R);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int g0 = 0; g0 < G; g0 += 8) {
+    // eight shares in flight at once (indexes past G clamped, their values dropped)
+    float4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = dp4[((int64_t)min(g0 + k, G - 1) * 16 + b) * QR + q];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const bool on = g0 + k < G;
+      acc.x += on ? v[k].x : 0.f;
+      acc.y += on ? v[k].y : 0.f;
+      acc.z += on ? v[k].z : 0.f;
+      acc.w += on ? v[k].w : 0.f;
+    }
+  }
+  uint2 o;
+  o.x = pack_bf16x2(acc.x, acc.y);
+  o.y = pack_bf16x2(acc.z, acc.w);
+  *reinterpret_cast<uint2*>(lat + ((int64_t)n * (B - 1) + b - 1) * R + 4 * q) = o;
+}
+
 template <int R>
 hipError_t launch_r(const uint2* part, int ntiles, int64_t* blk, const int64_t* am1,
                     const float* xh, const uint16_t* w1, const uint16_t* in_proj,
@@ -284,7 +522,53 @@ hipError_t launch_r(const uint2* part, int ntiles, int64_t* blk, const int64_t* 
   return hipGetLastError();
 }
 
+template <int R>
+hipError_t launch_fused_r(const uint2* part, int ntiles, int64_t* blk, const int64_t* am1,
+                          const float* xh, const float* w1p, const uint16_t* mix_L,
+                          const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                          int N, int B, int M, int64_t V, uint16_t* lat, float* dpart,
+                          int32_t* flags, int pass, hipStream_t s) {
+  const int G = M / 64;
+  hipLaunchKernelGGL(latent_share_kernel<R>, dim3(N, G), dim3(256), 0, s, part, ntiles,
+                     N * (B - 1), blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, B, M, V, dpart,
+                     flags, pass);
+  constexpr int RPW = 256 / (R / 4);
+  hipLaunchKernelGGL(latent_sum_kernel<R>, dim3(N, (B - 1 + RPW - 1) / RPW), dim3(256), 0, s,
+                     dpart, B, G, lat, flags, pass, part != nullptr ? 1 : 0);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+size_t latent_fused_scratch_bytes(int N, int r, int M) {
+  return (size_t)N * (M / 64) * 16 * r * sizeof(float);
+}
+
+hipError_t launch_latent_fused(const uint2* part, int ntiles, int64_t* blk, const int64_t* am1,
+                               const float* xh, const float* w1p, const uint16_t* mix_L,
+                               const uint16_t* w_gate, const uint16_t* w_up,
+                               const uint16_t* w_down, int N, int B, int r, int M, int64_t V,
+                               uint16_t* lat, float* dpart, int32_t* flags, int pass,
+                               hipStream_t s) {
+  switch (r) {
+    case 64: return launch_fused_r<64>(part, ntiles, blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, dpart, flags, pass, s);
+    case 128: return launch_fused_r<128>(part, ntiles, blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, dpart, flags, pass, s);
+    case 256: return launch_fused_r<256>(part, ntiles, blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, dpart, flags, pass, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_fold_embedding(const uint16_t* w1, const uint16_t* in_proj, int r, int64_t V,
+                                 float* w1p, hipStream_t s) {
+  const dim3 grid((unsigned)((V + 255) / 256));
+  switch (r) {
+    case 64: hipLaunchKernelGGL(fold_embedding_kernel<64>, grid, dim3(256), 0, s, w1, in_proj, V, w1p); break;
+    case 128: hipLaunchKernelGGL(fold_embedding_kernel<128>, grid, dim3(256), 0, s, w1, in_proj, V, w1p); break;
+    case 256: hipLaunchKernelGGL(fold_embedding_kernel<256>, grid, dim3(256), 0, s, w1, in_proj, V, w1p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 size_t latent_scratch_bytes(int N, int r, int M) {
   const size_t nrows = (size_t)N * 16;

@@ -41,6 +41,19 @@ hipError_t launch_latent(const uint2* part, int ntiles, int64_t* blk, const int6
                          const uint16_t* mix_L, const uint16_t* w_gate, const uint16_t* w_up,
                          const uint16_t* w_down, int N, int B, int r, int M, int64_t V,
                          uint16_t* lat, void* scratch, int32_t* flags, int pass, hipStream_t s);
+// K4 from the projected embedding table w1p (launch_fold_embedding), two launches: the
+// per-(block, 64-unit slice) shares of the latent, then their sum into lat. dpart: [N, M/64, 16,
+// r] fp32 shares (latent_fused_scratch_bytes). part / blk / flags as in launch_latent.
+size_t latent_fused_scratch_bytes(int N, int r, int M);
+hipError_t launch_latent_fused(const uint2* part, int ntiles, int64_t* blk, const int64_t* am1,
+                               const float* xh, const float* w1p, const uint16_t* mix_L,
+                               const uint16_t* w_gate, const uint16_t* w_up,
+                               const uint16_t* w_down, int N, int B, int r, int M, int64_t V,
+                               uint16_t* lat, float* dpart, int32_t* flags, int pass,
+                               hipStream_t s);
+// w1p[v, c] = sum_k in_proj[c, 2r + k] * w1[v, k], fp32 [V, r].
+hipError_t launch_fold_embedding(const uint16_t* w1, const uint16_t* in_proj, int r, int64_t V,
+                                 float* w1p, hipStream_t s);
 // K5: per (vocab tile, row) partial argmax of base + lat . w2^T; part: [rows, ntiles].
 hipError_t launch_readout_partial(const uint16_t* lat, const uint16_t* w2, const uint16_t* base,
                                   int64_t ld, int rows, int64_t V, int r, uint2* part,

@@ -85,6 +85,8 @@ xpress_status check_weights(const xpress_weights* w, bool need_hidden, bool need
     XP_PTR(w->w_gate);
     XP_PTR(w->w_up);
     XP_PTR(w->w_down);
+    if (w->w1p != nullptr && !aligned16(w->w1p))
+      return fail(XPRESS_ERR_ARG, "w->w1p is not 16-byte aligned");
   }
   if (need_w2) XP_PTR(w->w2);
   return XPRESS_OK;
@@ -103,6 +105,14 @@ struct Layout {
          cmax = 0, total = 0;
 };
 
+// Scratch of the latent stage: the larger of the three-kernel path's and the projected-table
+// path's (shares of the latent per 64-unit slice).
+size_t latent_bytes(int N, int r, int M) {
+  const size_t a = xpress::latent_scratch_bytes(N, r, M);
+  const size_t b = xpress::latent_fused_scratch_bytes(N, r, M);
+  return a > b ? a : b;
+}
+
 
 Layout step_layout(int N, int B, int r, int H, int64_t V, int C, int K) {
   Layout L;
@@ -118,7 +128,7 @@ Layout step_layout(int N, int B, int r, int H, int64_t V, int C, int K) {
   L.hdg = take(xpress::hidden_scratch_bytes_any_h(N * B, r));
   L.xh = take((size_t)N * B * r * sizeof(float));
   L.lat = take(rows * r * 2);
-  L.lscr = take(xpress::latent_scratch_bytes(N, r, kMaxM));
+  L.lscr = take(latent_bytes(N, r, kMaxM));
   L.part = take(C > 0 ? 0 : rows * (size_t)xpress::readout_tiles(V) * sizeof(uint2));
   L.flags = take((size_t)(K + 1) * sizeof(int32_t));
   L.cand = take(rows * c * sizeof(int64_t));
@@ -158,6 +168,19 @@ xpress_status xpress_fold_mixer(const xpress_bf16* raw, int32_t r, int32_t B, xp
   if (raw == mix_L) return fail(XPRESS_ERR_ARG, "mix_L must not alias raw");
   XP_TRY(xpress::launch_fold_mixer(raw, r, B, mix_L, reinterpret_cast<hipStream_t>(stream)),
          "fold mixer");
+  return XPRESS_OK;
+}
+
+xpress_status xpress_fold_embedding(const xpress_weights* w, float* w1p, xpress_stream stream) {
+  if (w == nullptr) return fail(XPRESS_ERR_ARG, "weights struct is NULL");
+  xpress_status st = check_dims(2, w->r, w->V);
+  if (st != XPRESS_OK) return st;
+  XP_PTR(w->w1);
+  XP_PTR(w->in_proj);
+  XP_PTR(w1p);
+  XP_TRY(xpress::launch_fold_embedding(w->w1, w->in_proj, w->r, w->V, w1p,
+                                       reinterpret_cast<hipStream_t>(stream)),
+         "fold embedding");
   return XPRESS_OK;
 }
 
@@ -209,12 +232,23 @@ xpress_status xpress_latent_pass(const xpress_weights* w, const int64_t* blk, co
   XP_PTR(xh);
   XP_PTR(lat);
   XP_PTR(ws);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (w->w1p != nullptr) {
+    const size_t need = xpress::latent_fused_scratch_bytes(N, w->r, w->M);
+    if (ws_bytes < need)
+      return fail(XPRESS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed for N=%d", ws_bytes, need, N);
+    XP_TRY(xpress::launch_latent_fused(nullptr, 0, const_cast<int64_t*>(blk), am1, xh, w->w1p,
+                                       w->mix_L, w->w_gate, w->w_up, w->w_down, N, w->B, w->r,
+                                       w->M, w->V, lat, static_cast<float*>(ws), nullptr, 0, s),
+           "latent");
+    return XPRESS_OK;
+  }
   const size_t need = xpress::latent_scratch_bytes(N, w->r, w->M);
   if (ws_bytes < need)
     return fail(XPRESS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed for N=%d", ws_bytes, need, N);
   XP_TRY(xpress::launch_latent(nullptr, 0, const_cast<int64_t*>(blk), am1, xh, w->w1, w->in_proj,
                                w->mix_L, w->w_gate, w->w_up, w->w_down, N, w->B, w->r, w->M, w->V,
-                               lat, ws, nullptr, 0, reinterpret_cast<hipStream_t>(stream)),
+                               lat, ws, nullptr, 0, s),
          "latent");
   return XPRESS_OK;
 }
@@ -382,6 +416,7 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
     XP_TRY(xpress::launch_topc_gather(cand, w->w2, rows, c, r, w2c, s), "top-C gather");
   }
   const bool stop = (flags & XPRESS_STOP_AT_FIXED_POINT) != 0;
+  const bool fused = w->w1p != nullptr;
   int32_t* pf = stop ? at<int32_t>(ws, L.flags) : nullptr;
   if (stop) XP_TRY(xpress::launch_flags_reset(pf, K + 1, s), "flags reset");
   uint2* part = at<uint2>(ws, L.part);
@@ -390,10 +425,16 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
   // block finishes its own rows); only the last pass's reduce is a launch of its own.
   for (int p = 0; p < K; ++p) {
     const uint2* prev = (c == 0 && p > 0) ? part : nullptr;
-    XP_TRY(xpress::launch_latent(prev, ntiles, blk, am1, xh, w->w1, w->in_proj, w->mix_L,
-                                 w->w_gate, w->w_up, w->w_down, N, B, r, w->M, V, lat, lscr, pf,
-                                 p, s),
-           "latent");
+    if (fused)
+      XP_TRY(xpress::launch_latent_fused(prev, ntiles, blk, am1, xh, w->w1p, w->mix_L, w->w_gate,
+                                         w->w_up, w->w_down, N, B, r, w->M, V, lat,
+                                         static_cast<float*>(lscr), pf, p, s),
+             "latent");
+    else
+      XP_TRY(xpress::launch_latent(prev, ntiles, blk, am1, xh, w->w1, w->in_proj, w->mix_L,
+                                   w->w_gate, w->w_up, w->w_down, N, B, r, w->M, V, lat, lscr, pf,
+                                   p, s),
+             "latent");
     if (c > 0) {
       XP_TRY(xpress::launch_topc_readout(lat, w2c, base_c, cand, rows, B, r, c, blk, nullptr, pf, p, s),
              "top-C readout");

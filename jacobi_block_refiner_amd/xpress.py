@@ -35,6 +35,7 @@ class _Weights(ctypes.Structure):
         ("w1", ctypes.c_void_p), ("down_h", ctypes.c_void_p), ("down_g", ctypes.c_void_p),
         ("in_proj", ctypes.c_void_p), ("mix_L", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
         ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+        ("w1p", ctypes.c_void_p),
     ]
 
 
@@ -60,6 +61,7 @@ def lib() -> ctypes.CDLL:
         sig = {
             "xpress_workspace_size": [i32, i32, i32, i64, i32, i32, ctypes.POINTER(sz)],
             "xpress_fold_mixer": [P, i32, i32, P, P],
+            "xpress_fold_embedding": [W, P, P],
             "xpress_hidden_cache": [W, P, i32, P, P, sz, P],
             "xpress_initial_block": [P, i64, P, i32, i32, i64, P, P],
             "xpress_latent_pass": [W, P, P, P, i32, P, P, sz, P],
@@ -124,6 +126,8 @@ class Weights:
     w_up: torch.Tensor
     w_down: torch.Tensor
     w2: torch.Tensor
+    # optional fp32 [V, r] projected embedding table (fold_embedding); None: not used
+    w1p: torch.Tensor | None = None
 
     @property
     def dims(self):
@@ -139,6 +143,13 @@ class Weights:
             if not t.is_contiguous():
                 raise ValueError(f"{k} must be contiguous")
             setattr(s, k, t.data_ptr())
+        if self.w1p is not None:
+            t = self.w1p
+            if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+                raise TypeError("w1p must be a contiguous CUDA float32 tensor")
+            if tuple(t.shape) != (d["V"], d["r"]):
+                raise ValueError(f"w1p shape {tuple(t.shape)} != (V, r) = ({d['V']}, {d['r']})")
+            s.w1p = t.data_ptr()
         return s
 
 
@@ -159,6 +170,17 @@ def fold_mixer(raw: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tens
     r, B, _ = raw.shape
     out = torch.empty(B, B, r, dtype=raw.dtype, device=raw.device) if out is None else out
     _check(lib().xpress_fold_mixer(_ptr(raw), r, B, _ptr(out), _stream()))
+    return out
+
+
+def fold_embedding(w: Weights, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Projected embedding table w1p [V, r] fp32: in_proj's embedding block applied to every row
+    of w1 (set it as ``w.w1p`` to run the latent stage as two launches instead of three)."""
+    d = w.dims
+    s = w.struct()
+    out = (torch.empty(d["V"], d["r"], dtype=torch.float32, device=w.w1.device)
+           if out is None else out)
+    _check(lib().xpress_fold_embedding(ctypes.byref(s), _ptr(out), _stream()))
     return out
 
 

@@ -172,24 +172,61 @@ def _latent_case(wl_id, N, seed=0, **over):
     return inp, xh
 
 
+def _dev(inp, path):
+    """Device inputs; path "table": the latent gathers the projected embedding table (two
+    launches); "project": it projects the gathered w1 rows itself (three launches)."""
+    d = Dev(inp)
+    if path == "project":
+        d.w.w1p = None
+    else:
+        assert d.w.w1p is not None
+    return d
+
+
+@pytest.mark.parametrize("r,V", [(64, 1000), (128, 4096), (256, 8195)])
+def test_fold_embedding_matches_oracle_projection(r, V):
+    """w1p[v] = P_e . w1[v]: the oracle's latent with an identity mixer and a zero hidden cache
+    returns exactly that projection as its mixer output u, for the ids the slots read."""
+    wl = replace(synth.WORKLOADS[1], N=4, B=16, r=r, V=V, M=64)
+    inp = synth.make_inputs(wl, seed=5).rounded_bf16()
+    d = Dev(inp)
+    got_all = d.w.w1p.cpu().numpy().astype(np.float64)
+    assert got_all.shape == (V, r)
+    rng = np.random.default_rng(7)
+    ids = np.concatenate([[0, V - 1, V // 2], rng.integers(0, V, size=4 * 16 - 3)])
+    blk = ids[: 4 * 16].reshape(4, 16)
+    am1 = rng.integers(0, V, size=4)
+    L = np.broadcast_to(np.eye(16), (r, 16, 16)).copy()
+    _, u = O.latent(replace(inp, am1=am1), L, np.zeros((4, 16, r)), blk, am1, return_u=True)
+    prev = np.concatenate([am1[:, None], blk[:, :-1]], axis=1)  # ids read by the 16 slots
+    got = got_all[prev.reshape(-1)]
+    err = lat_rel_err(got, u.reshape(-1, r))
+    log(f"fold embedding r={r} V={V}: row-relative error {err:.2e}")
+    assert err < 1e-5
+
+
+@pytest.mark.parametrize("path", ["table", "project"])
 @pytest.mark.parametrize("wl_id,N,over", [(1, 3, {}), (3, 3, {"V": 4096}),
                                          (1, 2, {"B": 7, "M": 256, "r": 128}),
-                                         (3, 2, {"V": 2048, "M": 1024})])
-def test_latent_parity(wl_id, N, over):
+                                         (3, 2, {"V": 2048, "M": 1024}),
+                                         (1, 37, {"B": 16, "r": 256, "M": 512, "V": 3000}),
+                                         (1, 5, {"B": 2, "r": 64, "M": 64, "V": 700})])
+def test_latent_parity(wl_id, N, over, path):
     inp, xh = _latent_case(wl_id, N, **over)
-    d = Dev(inp)
+    d = _dev(inp, path)
     lat = torch.empty(N, inp.wl.B - 1, inp.wl.r, dtype=torch.bfloat16, device="cuda")
     xpress.latent_pass(d.w, upload.tokens(inp.blk), d.am1, torch.from_numpy(xh).cuda(), lat, d.ws())
     torch.cuda.synchronize()
     want = O.latent(inp, oracle_mixer(inp), xh.astype(np.float64), inp.blk, inp.am1)
     err = lat_rel_err(lat_to_f64(lat), want)
-    log(f"latent wl{wl_id} {over}: row-relative error {err:.2e}")
+    log(f"latent {path} wl{wl_id} N={N} {over}: row-relative error {err:.2e}")
     assert err < LAT_RTOL
 
 
-def test_latent_causality_bit_invariance():
+@pytest.mark.parametrize("path", ["table", "project"])
+def test_latent_causality_bit_invariance(path):
     inp, xh = _latent_case(3, 3, V=4096)
-    d = Dev(inp)
+    d = _dev(inp, path)
     xh_t = torch.from_numpy(xh).cuda()
     B = inp.wl.B
     lat0 = torch.empty(3, B - 1, inp.wl.r, dtype=torch.bfloat16, device="cuda")
@@ -207,16 +244,34 @@ def test_latent_causality_bit_invariance():
         assert not np.array_equal(a[:, b:], c[:, b:])
 
 
-def test_latent_repeat_is_bit_identical():
+@pytest.mark.parametrize("path", ["table", "project"])
+def test_latent_repeat_is_bit_identical(path):
     inp, xh = _latent_case(3, 4, V=4096)
-    d = Dev(inp)
+    d = _dev(inp, path)
     xh_t = torch.from_numpy(xh).cuda()
     outs = []
+    ws = d.ws()
     for _ in range(3):
         lat = torch.empty(4, inp.wl.B - 1, inp.wl.r, dtype=torch.bfloat16, device="cuda")
-        xpress.latent_pass(d.w, upload.tokens(inp.blk), d.am1, xh_t, lat, d.ws())
+        xpress.latent_pass(d.w, upload.tokens(inp.blk), d.am1, xh_t, lat, ws)
         outs.append(lat.view(torch.int16).cpu().numpy())
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+def test_latent_paths_agree():
+    """The two-launch latent (projected table) and the three-kernel one differ only by fp32
+    rounding of the embedding projection; their bf16 latents agree within a few bf16 ulps."""
+    inp, xh = _latent_case(3, 8, V=4096)
+    outs = []
+    for path in ("table", "project"):
+        d = _dev(inp, path)
+        lat = torch.empty(8, inp.wl.B - 1, inp.wl.r, dtype=torch.bfloat16, device="cuda")
+        xpress.latent_pass(d.w, upload.tokens(inp.blk), d.am1, torch.from_numpy(xh).cuda(), lat,
+                           d.ws())
+        outs.append(lat_to_f64(lat))
+    err = lat_rel_err(outs[0], outs[1])
+    log(f"latent paths: row-relative difference {err:.2e}")
+    assert err < 1e-2
 
 
 # ----------------------------------------------------------------------------------------------
@@ -248,9 +303,10 @@ def test_one_pass_teacher_forced(variant):
     assert bad == 0
 
 
+@pytest.mark.parametrize("path", ["table", "project"])
 @pytest.mark.parametrize("variant", ["tiny", "strong"])
 @pytest.mark.parametrize("init", [True, False])
-def test_step_to_fixed_point_matches_oracle(variant, init):
+def test_step_to_fixed_point_matches_oracle(variant, init, path):
     if variant == "tiny":
         inp = synth.make_inputs(1).rounded_bf16()
     else:
@@ -258,7 +314,7 @@ def test_step_to_fixed_point_matches_oracle(variant, init):
     wl = inp.wl
     B = inp.raw_L.shape[1]
     N = inp.blk.shape[0]
-    d = Dev(inp)
+    d = _dev(inp, path)
     blk = upload.tokens(inp.blk)
     passes = torch.zeros(1, dtype=torch.int32, device="cuda")
     flags = xpress.STOP_AT_FIXED_POINT | (xpress.INIT_FROM_BASE if init else 0)
@@ -272,7 +328,7 @@ def test_step_to_fixed_point_matches_oracle(variant, init):
     want, n_pass, _, hg = O.jacobi(inp, L, xh, start, K=K, stop_at_fixed_point=True,
                                    history=True)
     got = blk.cpu().numpy()
-    log(f"step {variant} init={init}: passes gpu {int(passes.item())} oracle {n_pass}, "
+    log(f"step {path} {variant} init={init}: passes gpu {int(passes.item())} oracle {n_pass}, "
         f"min gap {hg.min():.3g}")
     bad, exempt = end_to_end_ok(got, want, hg)
     assert bad == 0
