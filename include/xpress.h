@@ -80,11 +80,12 @@ typedef struct {
   const float* w1p;           /* [V, r]   OPTIONAL (NULL: not used), fp32: the embedding table with
                                           in_proj's embedding block applied,
                                           w1p[v, c] = sum_k in_proj[c, 2r+k] * w1[v, k]
-                                          (xpress_fold_embedding). When given, the latent stage
-                                          gathers its rows instead of projecting w1's rows every
-                                          pass and runs as two launches instead of three;
-                                          results agree with the NULL path within fp32
-                                          rounding                                              */
+                                          (xpress_fold_embedding). When given and N <= 127,
+                                          the latent stage gathers its rows instead of
+                                          projecting w1's rows every pass and runs as two
+                                          launches instead of three (from 128 blocks on the
+                                          three-kernel path is faster and is used); results
+                                          agree with the NULL path within fp32 rounding        */
 } xpress_weights;
 
 /* Flags of xpress_jacobi_step. */

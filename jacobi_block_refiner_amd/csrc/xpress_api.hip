@@ -99,6 +99,14 @@ xpress_status check_base(const xpress_bf16* base, int64_t ld, int64_t V) {
   return XPRESS_OK;
 }
 
+// Whether the latent stage runs from the projected embedding table (share + sum kernels). From
+// 128 blocks on the three-kernel path is faster (46 against 50 us per pass at 256 blocks: the
+// shares of the down product, G fp32 copies of lat, then cost more traffic than the projection
+// they replace) and is taken even when the table is given; the results agree within fp32
+// rounding either way.
+constexpr int kTableMaxN = 127;
+bool use_table(const xpress_weights* w, int N) { return w->w1p != nullptr && N <= kTableMaxN; }
+
 // Workspace regions of a call with N blocks.
 struct Layout {
   size_t hdg = 0, xh = 0, lat = 0, lscr = 0, part = 0, flags = 0, cand = 0, base_c = 0, w2c = 0,
@@ -233,7 +241,7 @@ xpress_status xpress_latent_pass(const xpress_weights* w, const int64_t* blk, co
   XP_PTR(lat);
   XP_PTR(ws);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (w->w1p != nullptr) {
+  if (use_table(w, N)) {
     const size_t need = xpress::latent_fused_scratch_bytes(N, w->r, w->M);
     if (ws_bytes < need)
       return fail(XPRESS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed for N=%d", ws_bytes, need, N);
@@ -416,7 +424,7 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
     XP_TRY(xpress::launch_topc_gather(cand, w->w2, rows, c, r, w2c, s), "top-C gather");
   }
   const bool stop = (flags & XPRESS_STOP_AT_FIXED_POINT) != 0;
-  const bool fused = w->w1p != nullptr;
+  const bool fused = use_table(w, N);
   int32_t* pf = stop ? at<int32_t>(ws, L.flags) : nullptr;
   if (stop) XP_TRY(xpress::launch_flags_reset(pf, K + 1, s), "flags reset");
   uint2* part = at<uint2>(ws, L.part);
