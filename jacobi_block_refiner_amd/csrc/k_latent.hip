@@ -527,11 +527,12 @@ hipError_t launch_fused_r(const uint2* part, int ntiles, int64_t* blk, const int
                           const float* xh, const float* w1p, const uint16_t* mix_L,
                           const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                           int N, int B, int M, int64_t V, uint16_t* lat, float* dpart,
-                          int32_t* flags, int pass, hipStream_t s) {
+                          int32_t* flags, int pass, hipStream_t s, bool with_sum) {
   const int G = M / 64;
   hipLaunchKernelGGL(latent_share_kernel<R>, dim3(N, G), dim3(256), 0, s, part, ntiles,
                      N * (B - 1), blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, B, M, V, dpart,
                      flags, pass);
+  if (!with_sum) return hipGetLastError();
   constexpr int RPW = 256 / (R / 4);
   hipLaunchKernelGGL(latent_sum_kernel<R>, dim3(N, (B - 1 + RPW - 1) / RPW), dim3(256), 0, s,
                      dpart, B, G, lat, flags, pass, part != nullptr ? 1 : 0);
@@ -549,11 +550,11 @@ hipError_t launch_latent_fused(const uint2* part, int ntiles, int64_t* blk, cons
                                const uint16_t* w_gate, const uint16_t* w_up,
                                const uint16_t* w_down, int N, int B, int r, int M, int64_t V,
                                uint16_t* lat, float* dpart, int32_t* flags, int pass,
-                               hipStream_t s) {
+                               hipStream_t s, bool with_sum) {
   switch (r) {
-    case 64: return launch_fused_r<64>(part, ntiles, blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, dpart, flags, pass, s);
-    case 128: return launch_fused_r<128>(part, ntiles, blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, dpart, flags, pass, s);
-    case 256: return launch_fused_r<256>(part, ntiles, blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, dpart, flags, pass, s);
+    case 64: return launch_fused_r<64>(part, ntiles, blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, dpart, flags, pass, s, with_sum);
+    case 128: return launch_fused_r<128>(part, ntiles, blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, dpart, flags, pass, s, with_sum);
+    case 256: return launch_fused_r<256>(part, ntiles, blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, dpart, flags, pass, s, with_sum);
     default: return hipErrorInvalidValue;
   }
 }

@@ -582,9 +582,10 @@ __global__ __launch_bounds__(256) void topc_gather_kernel(const int64_t* __restr
 // vocabulary id -- and translated to its id once at the end.
 template <int R>
 __global__ __launch_bounds__(256) void topc_readout_kernel(
-    const uint16_t* __restrict__ lat, const uint16_t* __restrict__ w2c,
-    const uint16_t* __restrict__ base_c, const int64_t* __restrict__ cand, int B, int c,
-    int64_t* __restrict__ blk, int32_t* changed, int32_t* flags, int pass) {
+    const uint16_t* __restrict__ lat, const float* __restrict__ shares, int nsh,
+    const uint16_t* __restrict__ w2c, const uint16_t* __restrict__ base_c,
+    const int64_t* __restrict__ cand, int B, int c, int64_t* __restrict__ blk, int32_t* changed,
+    int32_t* flags, int pass) {
   if (pass_skipped(flags, pass)) return;
   constexpr int G = R / 8;        // lanes per candidate
   constexpr int CPW = 64 / G;     // candidates per wave per load
@@ -596,7 +597,33 @@ __global__ __launch_bounds__(256) void topc_readout_kernel(
   const int q = lane % G, sub = lane / G;
   const uint16_t* bc = base_c + (int64_t)p * c;
   float lv[8];
-  {
+  if (shares) {
+    // The latent row from the nsh slice shares of the latent kernels ([N, nsh, 16, r] fp32, the
+    // residual in share 0), summed in slice order and rounded to bf16 exactly as the sum kernel
+    // forms lat (the values are the same bits).
+    const int n = p / (B - 1), b = 1 + p % (B - 1);
+    const float4* sp = reinterpret_cast<const float4*>(shares + ((int64_t)n * nsh * 16 + b) * R) + 2 * q;
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int g0 = 0; g0 < nsh; g0 += 8) {
+      float4 v[8][2];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int64_t off = (int64_t)min(g0 + k, nsh - 1) * 16 * (R / 4);
+        v[k][0] = sp[off];
+        v[k][1] = sp[off + 1];
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const bool on = g0 + k < nsh;
+        a[0] += on ? v[k][0].x : 0.f; a[1] += on ? v[k][0].y : 0.f;
+        a[2] += on ? v[k][0].z : 0.f; a[3] += on ? v[k][0].w : 0.f;
+        a[4] += on ? v[k][1].x : 0.f; a[5] += on ? v[k][1].y : 0.f;
+        a[6] += on ? v[k][1].z : 0.f; a[7] += on ? v[k][1].w : 0.f;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lv[e] = bf16_to_f32(f32_to_bf16(a[e]));
+  } else {
     const uint4 u = reinterpret_cast<const uint4*>(lat + (int64_t)p * R)[q];
     lv[0] = bf16_lo(u.x); lv[1] = bf16_hi(u.x); lv[2] = bf16_lo(u.y); lv[3] = bf16_hi(u.y);
     lv[4] = bf16_lo(u.z); lv[5] = bf16_hi(u.z); lv[6] = bf16_lo(u.w); lv[7] = bf16_hi(u.w);
@@ -678,21 +705,22 @@ hipError_t launch_topc_gather(const int64_t* cand, const uint16_t* w2, int rows,
   return hipGetLastError();
 }
 
-hipError_t launch_topc_readout(const uint16_t* lat, const uint16_t* w2c, const uint16_t* base_c,
-                               const int64_t* cand, int rows, int B, int r, int c, int64_t* blk,
-                               int32_t* changed, int32_t* flags, int pass, hipStream_t s) {
+hipError_t launch_topc_readout(const uint16_t* lat, const float* shares, int nsh,
+                               const uint16_t* w2c, const uint16_t* base_c, const int64_t* cand,
+                               int rows, int B, int r, int c, int64_t* blk, int32_t* changed,
+                               int32_t* flags, int pass, hipStream_t s) {
   switch (r) {
     case 64:
-      hipLaunchKernelGGL(topc_readout_kernel<64>, dim3(rows), dim3(256), 0, s, lat, w2c, base_c,
-                         cand, B, c, blk, changed, flags, pass);
+      hipLaunchKernelGGL(topc_readout_kernel<64>, dim3(rows), dim3(256), 0, s, lat, shares, nsh,
+                         w2c, base_c, cand, B, c, blk, changed, flags, pass);
       break;
     case 128:
-      hipLaunchKernelGGL(topc_readout_kernel<128>, dim3(rows), dim3(256), 0, s, lat, w2c, base_c,
-                         cand, B, c, blk, changed, flags, pass);
+      hipLaunchKernelGGL(topc_readout_kernel<128>, dim3(rows), dim3(256), 0, s, lat, shares, nsh,
+                         w2c, base_c, cand, B, c, blk, changed, flags, pass);
       break;
     case 256:
-      hipLaunchKernelGGL(topc_readout_kernel<256>, dim3(rows), dim3(256), 0, s, lat, w2c, base_c,
-                         cand, B, c, blk, changed, flags, pass);
+      hipLaunchKernelGGL(topc_readout_kernel<256>, dim3(rows), dim3(256), 0, s, lat, shares, nsh,
+                         w2c, base_c, cand, B, c, blk, changed, flags, pass);
       break;
     default: return hipErrorInvalidValue;
   }

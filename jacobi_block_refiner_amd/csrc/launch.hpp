@@ -42,7 +42,8 @@ hipError_t launch_latent(const uint2* part, int ntiles, int64_t* blk, const int6
                          const uint16_t* w_down, int N, int B, int r, int M, int64_t V,
                          uint16_t* lat, void* scratch, int32_t* flags, int pass, hipStream_t s);
 // K4 from the projected embedding table w1p (launch_fold_embedding), two launches: the
-// per-(block, 64-unit slice) shares of the latent, then their sum into lat. dpart: [N, M/64, 16,
+// per-(block, 64-unit slice) shares of the latent, then their sum into lat (skipped with
+// with_sum = false, for a consumer that sums the shares itself). dpart: [N, M/64, 16,
 // r] fp32 shares (latent_fused_scratch_bytes). part / blk / flags as in launch_latent.
 size_t latent_fused_scratch_bytes(int N, int r, int M);
 hipError_t launch_latent_fused(const uint2* part, int ntiles, int64_t* blk, const int64_t* am1,
@@ -50,7 +51,7 @@ hipError_t launch_latent_fused(const uint2* part, int ntiles, int64_t* blk, cons
                                const uint16_t* w_gate, const uint16_t* w_up,
                                const uint16_t* w_down, int N, int B, int r, int M, int64_t V,
                                uint16_t* lat, float* dpart, int32_t* flags, int pass,
-                               hipStream_t s);
+                               hipStream_t s, bool with_sum = true);
 // w1p[v, c] = sum_k in_proj[c, 2r + k] * w1[v, k], fp32 [V, r].
 hipError_t launch_fold_embedding(const uint16_t* w1, const uint16_t* in_proj, int r, int64_t V,
                                  float* w1p, hipStream_t s);
@@ -72,10 +73,13 @@ hipError_t launch_topc_select(const uint16_t* base, int64_t ld, int rows, int64_
 size_t topc_select_scratch_bytes(int rows, int64_t V);
 hipError_t launch_topc_gather(const int64_t* cand, const uint16_t* w2, int rows, int c, int r,
                               uint16_t* w2c, hipStream_t s);
-// K7: top-C gathered GEMV + argmax + candidate -> vocabulary id -> blk.
-hipError_t launch_topc_readout(const uint16_t* lat, const uint16_t* w2c, const uint16_t* base_c,
-                               const int64_t* cand, int rows, int B, int r, int c, int64_t* blk,
-                               int32_t* changed, int32_t* pass_flags, int pass, hipStream_t s);
+// K7: top-C gathered GEMV + argmax + candidate -> vocabulary id -> blk. The latent rows come
+// from lat (bf16), or, with shares != nullptr, from the nsh slice shares the latent share kernel
+// leaves ([N, nsh, 16, r] fp32), summed as the latent sum kernel would (same bits).
+hipError_t launch_topc_readout(const uint16_t* lat, const float* shares, int nsh,
+                               const uint16_t* w2c, const uint16_t* base_c, const int64_t* cand,
+                               int rows, int B, int r, int c, int64_t* blk, int32_t* changed,
+                               int32_t* pass_flags, int pass, hipStream_t s);
 // mix_L = bf16(raw * tril + I), per channel.
 hipError_t launch_fold_mixer(const uint16_t* raw, int r, int B, uint16_t* mix_L, hipStream_t s);
 // blk[n, 0] = anchor[n] (the step without the argmax start).

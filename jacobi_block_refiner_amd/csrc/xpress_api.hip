@@ -367,8 +367,8 @@ xpress_status xpress_readout_argmax_topc(const xpress_bf16* lat, const xpress_bf
   XP_PTR(w2c);
   if (base_c == nullptr || cand == nullptr || blk == nullptr)
     return fail(XPRESS_ERR_ARG, "base_c, cand or blk is NULL");
-  XP_TRY(xpress::launch_topc_readout(lat, w2c, base_c, cand, N * (B - 1), B, r, c, blk, changed,
-                                     nullptr, 0, reinterpret_cast<hipStream_t>(stream)),
+  XP_TRY(xpress::launch_topc_readout(lat, nullptr, 0, w2c, base_c, cand, N * (B - 1), B, r, c, blk,
+                                     changed, nullptr, 0, reinterpret_cast<hipStream_t>(stream)),
          "top-C readout");
   return XPRESS_OK;
 }
@@ -433,10 +433,11 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
   // block finishes its own rows); only the last pass's reduce is a launch of its own.
   for (int p = 0; p < K; ++p) {
     const uint2* prev = (c == 0 && p > 0) ? part : nullptr;
+    // with candidates, the top-C readout sums the table path's latent shares itself
     if (fused)
       XP_TRY(xpress::launch_latent_fused(prev, ntiles, blk, am1, xh, w->w1p, w->mix_L, w->w_gate,
                                          w->w_up, w->w_down, N, B, r, w->M, V, lat,
-                                         static_cast<float*>(lscr), pf, p, s),
+                                         static_cast<float*>(lscr), pf, p, s, c == 0),
              "latent");
     else
       XP_TRY(xpress::launch_latent(prev, ntiles, blk, am1, xh, w->w1, w->in_proj, w->mix_L,
@@ -444,7 +445,9 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
                                    p, s),
              "latent");
     if (c > 0) {
-      XP_TRY(xpress::launch_topc_readout(lat, w2c, base_c, cand, rows, B, r, c, blk, nullptr, pf, p, s),
+      XP_TRY(xpress::launch_topc_readout(lat, fused ? static_cast<const float*>(lscr) : nullptr,
+                                         w->M / 64, w2c, base_c, cand, rows, B, r, c, blk,
+                                         nullptr, pf, p, s),
              "top-C readout");
     } else {
       XP_TRY(xpress::launch_readout_partial(lat, w->w2, base, base_ld, rows, V, r, part, pf, p, s),

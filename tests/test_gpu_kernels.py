@@ -482,12 +482,14 @@ def test_topc_step_limits(C):
     assert end_to_end_ok(got, want, hg)[0] == 0
 
 
-def test_topc_step_matches_oracle():
+@pytest.mark.parametrize("path", ["table", "project"])
+def test_topc_step_matches_oracle(path):
+    """With the projected table the top-C readout sums the latent shares itself (no lat)."""
     inp = strong(synth.make_inputs(replace(synth.WORKLOADS[1], B=8), N=6, seed=6))
     N, B = inp.blk.shape
     wl = inp.wl
     C = 48
-    d = Dev(inp)
+    d = _dev(inp, path)
     blk = upload.tokens(inp.blk)
     passes = torch.zeros(1, dtype=torch.int32, device="cuda")
     xpress.jacobi_step(d.w, d.h, d.base, d.anchor, d.am1, blk, K=2 * B, C=C,
