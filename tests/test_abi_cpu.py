@@ -78,3 +78,25 @@ def test_small_workspace_and_bad_stride_are_rejected():
     st = L.xpress_readout_argmax(ctypes.byref(w), misaligned, fake, 151936, 4, fake, None, fake,
                                  1 << 30, None)
     assert st == xpress.ERR_ARG and b"aligned" in L.xpress_last_error()
+
+
+def test_fold_embedding_and_table_arguments_are_checked():
+    L = xpress.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    w = xpress._Weights(B=16, r=256, H=4096, M=512, V=151936, w1=fake, down_h=fake,
+                        down_g=fake, in_proj=fake, mix_L=fake, w_gate=fake, w_up=fake,
+                        w_down=fake, w2=fake)
+    assert L.xpress_fold_embedding(None, fake, None) == xpress.ERR_ARG
+    assert L.xpress_fold_embedding(ctypes.byref(w), None, None) == xpress.ERR_ARG
+    assert L.xpress_fold_embedding(ctypes.byref(w), ctypes.c_void_p((1 << 20) + 4),
+                                   None) == xpress.ERR_ARG
+    bad = xpress._Weights(B=16, r=96, H=4096, M=512, V=151936, w1=fake, in_proj=fake)
+    assert L.xpress_fold_embedding(ctypes.byref(bad), fake, None) == xpress.ERR_ARG
+    # a misaligned projected table is rejected before anything is enqueued
+    w.w1p = (1 << 20) + 8
+    st = L.xpress_latent_pass(ctypes.byref(w), fake, fake, fake, 4, fake, fake, 1 << 30, None)
+    assert st == xpress.ERR_ARG and b"w1p" in L.xpress_last_error()
+    # with the table, the latent scratch holds the M/64 slice shares of every block
+    w.w1p = 1 << 20
+    st = L.xpress_latent_pass(ctypes.byref(w), fake, fake, fake, 4, fake, fake, 1024, None)
+    assert st == xpress.ERR_WORKSPACE
