@@ -59,7 +59,7 @@ __device__ __forceinline__ void lds_copy16(const void* gbase, uint32_t off, uint
                :: "s"(lds_base), "v"(off), "s"(gbase) : "memory");
 }
 
-template <int R, int kNW, int RW, int NS>
+template <int R, int kNW, int RW, int NS, int TR>
 __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
     const uint16_t* __restrict__ lat, const uint16_t* __restrict__ w2,
     const uint16_t* __restrict__ base, int64_t ld, int rows, int V, int nvr, int n_rc,
@@ -70,7 +70,8 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
   constexpr int RPI = 64 / RQ;                  // w2 rows per copy instruction
   constexpr int NI = 32 / RPI;                  // copy instructions per w2 tile
   constexpr int WP = 65;                        // chunks per w2 copy block (64 + pad)
-  constexpr int CH = kNW * RW * 32;             // rows per row chunk
+  static_assert(TR >= 1 && TR <= kNW * RW, "row tiles per chunk");
+  constexpr int CH = TR * 32;                   // rows per row chunk (waves past TR/RW only copy)
   constexpr int WCH = NI * WP;                  // w2 chunks per stage
   constexpr int BCH = CH * 4;                   // base chunks per stage
   constexpr int SCH = WCH + BCH;                // chunks per stage
@@ -78,9 +79,10 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
   // waves past them repeat the first ones (same bytes to the same place), so every wave issues
   // the same number of copies and one vmcnt value fits all
   constexpr int WI = (NI + kNW - 1) / kNW;
-  constexpr int BI = BCH / 64 / kNW;
+  // base copy instructions per stage, and per wave (as for w2, waves past them repeat the first)
+  constexpr int NBI = BCH / 64;
+  constexpr int BI = (NBI + kNW - 1) / kNW;
   constexpr int DI = WI + BI;
-  static_assert(BCH % (64 * kNW) == 0, "base stage must split evenly over the waves");
 
   __shared__ uint4 s_stage[NS][SCH];
 
@@ -123,7 +125,8 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
   // These loads complete here, so no wait for them lands inside the loop (where it would also
   // wait for the stage copies in flight).
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  const bool active = row0 + wave * RW * 32 < rows;  // wave-uniform: the wave has real rows
+  // wave-uniform: the wave holds row tiles of this chunk and some of them are real rows
+  const bool active = wave * RW < TR && row0 + wave * RW * 32 < rows;
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)&s_stage[0][0];
   // Per-lane byte offsets of the copies, relative to the step's w2 tile and to the chunk's base
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
   }
 #pragma unroll
   for (int q = 0; q < BI; ++q) {
-    const int p = (wave + q * kNW) * 64 + lane;      // base chunk position
+    const int p = ((wave + q * kNW) % NBI) * 64 + lane;  // base chunk position
     const int rr = p >> 2, c = (p & 3) ^ ((rr >> 2) & 3);
     offb[q] = (uint32_t)(((int64_t)(min(row0 + rr, rows - 1) - row0) * ld + 8 * c) * 2);
   }
@@ -172,7 +175,7 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
     }
 #pragma unroll
     for (int q = 0; q < BI; ++q) {
-      const int ins = wave + q * kNW;
+      const int ins = (wave + q * kNW) % NBI;
       uint32_t off = offb[q];
       if (tail) {
         const int p = ins * 64 + opaque_lane_id();
@@ -357,7 +360,8 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
     const int row = row0 + (wave * RW + k) * 32 + l32;
     // range-major partials: the 32 lanes store 256 contiguous bytes (scattered 8-byte stores
     // into row-major partials cost a partial-line write-back per row at the end of the kernel)
-    if (half == 0 && row < rows) part[(int64_t)vr * rows + row] = make_uint2(__float_as_uint(v), (unsigned)i);
+    if (half == 0 && wave * RW < TR && row < rows)
+      part[(int64_t)vr * rows + row] = make_uint2(__float_as_uint(v), (unsigned)i);
   }
 }
 
@@ -409,29 +413,33 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const uint2* __restr
   }
 }
 
-template <int R, int NW, int RW, int NS>
+template <int R, int NW, int RW, int NS, int TR>
 hipError_t launch_partial_t(const uint16_t* lat, const uint16_t* w2, const uint16_t* base,
                             int64_t ld, int rows, int64_t V, uint2* part, const int32_t* flags,
                             int pass, hipStream_t s) {
   const int nvr = readout_tiles(V);
-  constexpr int CH = NW * RW * 32;
+  constexpr int CH = TR * 32;
   const int n_rc = (rows + CH - 1) / CH;
-  hipLaunchKernelGGL((readout_partial_kernel<R, NW, RW, NS>), dim3((unsigned)(nvr * n_rc)), dim3(64 * NW),
+  hipLaunchKernelGGL((readout_partial_kernel<R, NW, RW, NS, TR>), dim3((unsigned)(nvr * n_rc)), dim3(64 * NW),
                      0, s, lat, w2, base, ld, rows, (int)V, nvr, n_rc, part, flags, pass);
   return hipGetLastError();
 }
 
-// Row chunk shape: up to 256 rows, 8 waves of one 32-row tile each; more rows, 8 waves of two
-// 32-row tiles each (512 rows per chunk), so each w2 fragment read from LDS feeds two MFMAs.
-// (Four waves of four tiles, or sixteen of one, measured slower at 480 rows.)
-template <int NW, int RW, int NS>
+// Row chunk shape: up to 32 rows (a single request), one 32-row tile held by wave 0 while all 8
+// waves issue copies, with a base stage of those 32 rows only (a 256-row stage copies the last row
+// over and over: 16.2 against 15.2 us at 15 rows; deeper rings, possible with the small stage,
+// measured slower: 15.7 us with 4 stages, 17.8 with 8, as the steps in flight outgrow the L2);
+// up to 256 rows, 8 waves of one 32-row tile each; more rows, 8 waves of two 32-row tiles each
+// (512 rows per chunk), so each w2 fragment read from LDS feeds two MFMAs. (Four waves of four
+// tiles, or sixteen of one, measured slower at 480 rows.)
+template <int NW, int RW, int NS, int TR = NW * RW>
 hipError_t launch_partial_shape(const uint16_t* lat, const uint16_t* w2, const uint16_t* base,
                                 int64_t ld, int rows, int64_t V, int r, uint2* part,
                                 const int32_t* flags, int pass, hipStream_t s) {
   switch (r) {
-    case 64: return launch_partial_t<64, NW, RW, NS>(lat, w2, base, ld, rows, V, part, flags, pass, s);
-    case 128: return launch_partial_t<128, NW, RW, NS>(lat, w2, base, ld, rows, V, part, flags, pass, s);
-    case 256: return launch_partial_t<256, NW, RW, NS>(lat, w2, base, ld, rows, V, part, flags, pass, s);
+    case 64: return launch_partial_t<64, NW, RW, NS, TR>(lat, w2, base, ld, rows, V, part, flags, pass, s);
+    case 128: return launch_partial_t<128, NW, RW, NS, TR>(lat, w2, base, ld, rows, V, part, flags, pass, s);
+    case 256: return launch_partial_t<256, NW, RW, NS, TR>(lat, w2, base, ld, rows, V, part, flags, pass, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -446,6 +454,7 @@ int readout_tiles(int64_t V) {
 hipError_t launch_readout_partial(const uint16_t* lat, const uint16_t* w2, const uint16_t* base,
                                   int64_t ld, int rows, int64_t V, int r, uint2* part,
                                   const int32_t* flags, int pass, hipStream_t s) {
+  if (rows <= 32) return launch_partial_shape<8, 1, 3, 1>(lat, w2, base, ld, rows, V, r, part, flags, pass, s);
   if (rows <= 256) return launch_partial_shape<8, 1, 3>(lat, w2, base, ld, rows, V, r, part, flags, pass, s);
   return launch_partial_shape<8, 2, 3>(lat, w2, base, ld, rows, V, r, part, flags, pass, s);
 }

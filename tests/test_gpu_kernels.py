@@ -77,8 +77,11 @@ def test_initial_block_exact(V):
     assert np.array_equal(blk.cpu().numpy(), want)
 
 
-# N = 20 and 35 (300 and 525 rows) take the wide row-chunk shape; 525 rows span two row chunks
+# N = 1 and 2 (15 and 30 rows) take the one-tile shape (the long vocabularies give ranges of
+# several steps, so the ring wraps); N = 20 and 35 (300 and 525 rows)
+# take the wide row-chunk shape; 525 rows span two row chunks
 @pytest.mark.parametrize("r,V,N", [(64, 5003, 3), (256, 5003, 5), (256, 8192, 3), (128, 700, 2),
+                                   (256, 151936, 1), (128, 60001, 2), (64, 40000, 1),
                                    (256, 5003, 20), (256, 8192, 35), (128, 3001, 35)])
 def test_readout_argmax_dyadic_exact(r, V, N):
     """Every fp32 partial sum is exact, so the GPU must match the oracle on every row, ties
