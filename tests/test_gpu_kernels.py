@@ -485,10 +485,11 @@ def test_topc_step_limits(C):
     assert end_to_end_ok(got, want, hg)[0] == 0
 
 
-@pytest.mark.parametrize("path", ["table", "project"])
-def test_topc_step_matches_oracle(path):
-    """With the projected table the top-C readout sums the latent shares itself (no lat)."""
-    inp = strong(synth.make_inputs(replace(synth.WORKLOADS[1], B=8), N=6, seed=6))
+@pytest.mark.parametrize("path,M", [("table", 128), ("project", 128), ("table", 1024)])
+def test_topc_step_matches_oracle(path, M):
+    """With the projected table the top-C readout sums the latent shares itself (no lat); at
+    M = 1024 there are 16 slice shares, two rounds of eight."""
+    inp = strong(synth.make_inputs(replace(synth.WORKLOADS[1], B=8, M=M), N=6, seed=6))
     N, B = inp.blk.shape
     wl = inp.wl
     C = 48
