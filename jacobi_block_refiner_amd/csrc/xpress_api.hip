@@ -107,19 +107,20 @@ xpress_status check_base(const xpress_bf16* base, int64_t ld, int64_t V) {
 constexpr int kTableMaxN = 127;
 bool use_table(const xpress_weights* w, int N) { return w->w1p != nullptr && N <= kTableMaxN; }
 
+// Scratch of the latent stage: the three-kernel path's, or the larger projected-table path's
+// (slice shares) when N is small enough for that path to run.
+size_t latent_bytes(int N, int r, int M) {
+  const size_t a = xpress::latent_scratch_bytes(N, r, M);
+  const size_t b = N <= kTableMaxN ? xpress::latent_fused_scratch_bytes(N, r, M) : 0;
+  return a > b ? a : b;
+}
+
 // Workspace regions of a call with N blocks.
 struct Layout {
   size_t hdg = 0, xh = 0, lat = 0, lscr = 0, part = 0, flags = 0, cand = 0, base_c = 0, w2c = 0,
          cmax = 0, total = 0;
 };
 
-// Scratch of the latent stage: the larger of the three-kernel path's and the projected-table
-// path's (shares of the latent per 64-unit slice).
-size_t latent_bytes(int N, int r, int M) {
-  const size_t a = xpress::latent_scratch_bytes(N, r, M);
-  const size_t b = xpress::latent_fused_scratch_bytes(N, r, M);
-  return a > b ? a : b;
-}
 
 
 Layout step_layout(int N, int B, int r, int H, int64_t V, int C, int K) {
@@ -164,7 +165,14 @@ xpress_status xpress_workspace_size(int32_t n_max, int32_t B, int32_t r, int64_t
   if (n_max < 0 || C < 0 || k_max < 0) return fail(XPRESS_ERR_ARG, "negative n_max, C or k_max");
   xpress_status st = check_dims(B, r, V);
   if (st != XPRESS_OK) return st;
-  *bytes = step_layout(n_max, B, r, kMaxH, V, C, k_max).total;
+  // every region grows with N, except the latent scratch, which the table path enlarges up to
+  // kTableMaxN blocks: the largest layout of any N <= n_max is at n_max or at kTableMaxN
+  size_t t = step_layout(n_max, B, r, kMaxH, V, C, k_max).total;
+  if (n_max > kTableMaxN) {
+    const size_t u = step_layout(kTableMaxN, B, r, kMaxH, V, C, k_max).total;
+    t = u > t ? u : t;
+  }
+  *bytes = t;
   return XPRESS_OK;
 }
 
