@@ -12,6 +12,7 @@
 // (high byte histogram, then low byte histogram inside the boundary bin), followed by one ordered
 // compaction pass that keeps every id above the threshold key and the lowest-id ties at it.
 #include "launch.hpp"
+#include "hidden_tile.hpp"
 #include "xpress_common.hpp"
 
 #include <limits.h>
@@ -234,8 +235,9 @@ __device__ __forceinline__ uint32_t radix_kth(const uint32_t* keys, int n, int k
   return t;
 }
 
-__device__ __forceinline__ void topc_select_row(const uint16_t* __restrict__ base, int64_t ld,
-                                                int64_t V, int c, int64_t* __restrict__ cand,
+__device__ __forceinline__ void topc_select_row(int p, const uint16_t* __restrict__ base,
+                                                int64_t ld, int64_t V, int c,
+                                                int64_t* __restrict__ cand,
                                                 uint16_t* __restrict__ base_c,
                                                 uint16_t* __restrict__ cmax) {
   __shared__ uint32_t s_hist[512];
@@ -248,7 +250,7 @@ __device__ __forceinline__ void topc_select_row(const uint16_t* __restrict__ bas
   __shared__ int s_cnt[4];
   constexpr int kHC = 1024;         // chunk-list capacity per wave
   __shared__ int s_hc[4][kHC];      // chunks whose maximum can hold an answer, per wave
-  const int p = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
   const uint16_t* row = base + (int64_t)p * ld;
   int64_t* out_id = cand + (int64_t)p * c;
   uint16_t* out_b = base_c + (int64_t)p * c;
@@ -291,7 +293,7 @@ __device__ __forceinline__ void topc_select_row(const uint16_t* __restrict__ bas
   // chunk maxima (bf16 bits), written by pass 1 when a buffer is given, read back by pass 3 so
   // that it re-reads only the chunks that can hold an answer
   const int64_t nchunk8 = (nchunk + 7) / 8 * 8;
-  uint16_t* cmax_row = cmax ? cmax + (int64_t)blockIdx.x * nchunk8 : nullptr;
+  uint16_t* cmax_row = cmax ? cmax + (int64_t)p * nchunk8 : nullptr;
   // 1. group maxima: thread tid visits chunks tid + 256 i; groups of gv visits (<= 8 groups)
   const int nv_max = (int)((nchunk + 255) / 256);
   const int gv = (nv_max + 7) / 8;
@@ -517,28 +519,27 @@ __device__ __forceinline__ void topc_select_row(const uint16_t* __restrict__ bas
   }
 }
 
-// One workgroup per draft row: the row's candidate set; with blk given, also the row's starting
+// Draft row p, by one workgroup: the row's candidate set; with blk given, also the row's starting
 // token (vLLM API page "vllm.model_executor.models.qwen3_xpress", jacobi_refine_greedy: the
 // argmax of the base logits, lowest id on ties), which is the best of the candidates under the
 // same order, written into blk[n, 1 + p % (B - 1)] (and the anchor into slot 0): the starting
 // block without a separate pass over base.
-__global__ __launch_bounds__(256) void topc_select_kernel(const uint16_t* __restrict__ base,
-                                                          int64_t ld, int64_t V, int c,
-                                                          int64_t* __restrict__ cand,
-                                                          uint16_t* __restrict__ base_c,
-                                                          const int64_t* __restrict__ anchor,
-                                                          int64_t* __restrict__ blk, int B,
-                                                          uint16_t* __restrict__ cmax) {
-  topc_select_row(base, ld, V, c, cand, base_c, cmax);
+__device__ __forceinline__ void topc_select_block(int p, const uint16_t* __restrict__ base,
+                                                  int64_t ld, int64_t V, int c,
+                                                  int64_t* __restrict__ cand,
+                                                  uint16_t* __restrict__ base_c,
+                                                  const int64_t* __restrict__ anchor,
+                                                  int64_t* __restrict__ blk, int B,
+                                                  uint16_t* __restrict__ cmax) {
+  topc_select_row(p, base, ld, V, c, cand, base_c, cmax);
   if (!blk) return;
   // the block's first row also stores the anchor in slot 0
-  if (blockIdx.x % (B - 1) == 0 && threadIdx.x == 0)
-    blk[(int64_t)(blockIdx.x / (B - 1)) * B] = anchor[blockIdx.x / (B - 1)];
+  if (p % (B - 1) == 0 && threadIdx.x == 0) blk[(int64_t)(p / (B - 1)) * B] = anchor[p / (B - 1)];
   __shared__ float s_bv[4];
   __shared__ int s_bi[4];
   __threadfence_block();
   __syncthreads();  // the row's candidates and values are written (by this workgroup)
-  const int p = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t* ids = cand + (int64_t)p * c;
   const uint16_t* vals = base_c + (int64_t)p * c;
   float bv = -INFINITY;
@@ -560,6 +561,33 @@ __global__ __launch_bounds__(256) void topc_select_kernel(const uint16_t* __rest
     for (int w = 1; w < 4; ++w) argmax_merge(bv, bi, s_bv[w], s_bi[w]);
     blk[(int64_t)(p / (B - 1)) * B + 1 + p % (B - 1)] = bi;
   }
+}
+
+__global__ __launch_bounds__(256) void topc_select_kernel(const uint16_t* __restrict__ base,
+                                                          int64_t ld, int64_t V, int c,
+                                                          int64_t* __restrict__ cand,
+                                                          uint16_t* __restrict__ base_c,
+                                                          const int64_t* __restrict__ anchor,
+                                                          int64_t* __restrict__ blk, int B,
+                                                          uint16_t* __restrict__ cmax) {
+  topc_select_block(blockIdx.x, base, ld, V, c, cand, base_c, anchor, blk, B, cmax);
+}
+
+// The start of a top-C step in one launch: workgroups [0, g1) are the hidden GEMM's tiles (mt x
+// nt tiles per split, split-major), the rest the draft rows' selection. The two are independent;
+// the GEMM is latency-bound and hides behind the selection.
+__global__ __launch_bounds__(256) void topc_start_kernel(
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ down_h,
+    const uint16_t* __restrict__ down_g, int NB, int H, int r, int kslice,
+    float* __restrict__ part, int g1, int mt, int nt, const uint16_t* __restrict__ base,
+    int64_t ld, int64_t V, int c, int64_t* __restrict__ cand, uint16_t* __restrict__ base_c,
+    const int64_t* __restrict__ anchor, int64_t* __restrict__ blk, int B,
+    uint16_t* __restrict__ cmax) {
+  const int i = blockIdx.x;
+  if (i < g1)
+    hidden_gemm_tile(h, down_h, down_g, NB, H, r, kslice, part, i % mt, (i / mt) % nt, i / (mt * nt));
+  else
+    topc_select_block(i - g1, base, ld, V, c, cand, base_c, anchor, blk, B, cmax);
 }
 
 __global__ __launch_bounds__(256) void topc_gather_kernel(const int64_t* __restrict__ cand,
@@ -686,6 +714,21 @@ hipError_t launch_topc_select(const uint16_t* base, int64_t ld, int rows, int64_
                               int64_t* cand, uint16_t* base_c, const int64_t* anchor,
                               int64_t* blk, int B, uint16_t* cmax, hipStream_t s) {
   hipLaunchKernelGGL(topc_select_kernel, dim3(rows), dim3(256), 0, s, base, ld, V, c, cand, base_c,
+                     anchor, blk, B, cmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_topc_start(const uint16_t* h, const uint16_t* down_h, const uint16_t* down_g,
+                             int NB, int H, int r, float* part, const uint16_t* base, int64_t ld,
+                             int rows, int64_t V, int c, int64_t* cand, uint16_t* base_c,
+                             const int64_t* anchor, int64_t* blk, int B, uint16_t* cmax,
+                             hipStream_t s) {
+  const int ns = hidden_splits(NB, H, r);
+  const int kslice = hidden_chunks_per_split(NB, H, r) * kTK;
+  const int mt = (NB + kTM - 1) / kTM, nt = (2 * r) / kTN;
+  const int g1 = mt * nt * ns;
+  hipLaunchKernelGGL(topc_start_kernel, dim3((unsigned)(g1 + rows)), dim3(256), 0, s, h, down_h,
+                     down_g, NB, H, r, kslice, part, g1, mt, nt, base, ld, V, c, cand, base_c,
                      anchor, blk, B, cmax);
   return hipGetLastError();
 }

@@ -14,6 +14,7 @@ int readout_tiles(int64_t V);
 // K1a: split-K partials of hdg[m, j] = sum_k h[m, k] * Wcat[j, k], Wcat = [down_h; down_g],
 // m < NB = N*B, j < 2r; scratch [hidden_splits, NB, 2r] fp32.
 int hidden_splits(int NB, int H, int r);
+int hidden_chunks_per_split(int NB, int H, int r);
 size_t hidden_scratch_bytes(int NB, int H, int r);
 size_t hidden_scratch_bytes_any_h(int NB, int r);
 hipError_t launch_hidden_gemm(const uint16_t* h, const uint16_t* down_h, const uint16_t* down_g,
@@ -71,6 +72,14 @@ hipError_t launch_topc_select(const uint16_t* base, int64_t ld, int rows, int64_
                               int64_t* cand, uint16_t* base_c, const int64_t* anchor, int64_t* blk,
                               int B, uint16_t* cmax, hipStream_t s);
 size_t topc_select_scratch_bytes(int rows, int64_t V);
+// K1a + K3's selection in one launch (independent): the hidden GEMM's tiles (into part, as
+// launch_hidden_gemm) and every draft row's selection (as launch_topc_select, with blk and
+// anchor nullable alike).
+hipError_t launch_topc_start(const uint16_t* h, const uint16_t* down_h, const uint16_t* down_g,
+                             int NB, int H, int r, float* part, const uint16_t* base, int64_t ld,
+                             int rows, int64_t V, int c, int64_t* cand, uint16_t* base_c,
+                             const int64_t* anchor, int64_t* blk, int B, uint16_t* cmax,
+                             hipStream_t s);
 hipError_t launch_topc_gather(const int64_t* cand, const uint16_t* w2, int rows, int c, int r,
                               uint16_t* w2c, hipStream_t s);
 // K7: top-C gathered GEMV + argmax + candidate -> vocabulary id -> blk. The latent rows come

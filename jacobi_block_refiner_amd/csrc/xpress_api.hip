@@ -414,7 +414,15 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
   const bool init = (flags & XPRESS_INIT_FROM_BASE) != 0;
   // the starting block: with candidates, the selection writes it (the best candidate is the
   // row's argmax; the anchor too); without, one launch computes it beside the hidden GEMM
-  if (init && c == 0)
+  int64_t* cand = at<int64_t>(ws, L.cand);
+  xpress_bf16* base_c = at<xpress_bf16>(ws, L.base_c);
+  xpress_bf16* w2c = at<xpress_bf16>(ws, L.w2c);
+  if (c > 0)  // the hidden GEMM beside the selection (which also writes the starting block)
+    XP_TRY(xpress::launch_topc_start(h, w->down_h, w->down_g, N * B, w->H, r, hdg, base, base_ld,
+                                     rows, V, c, cand, base_c, anchor, init ? blk : nullptr, B,
+                                     at<uint16_t>(ws, L.cmax), s),
+           "hidden gemm + top-C select");
+  else if (init)
     XP_TRY(xpress::launch_step_start(h, w->down_h, w->down_g, N * B, w->H, r, hdg, base, base_ld,
                                      anchor, N, B, V, blk, s),
            "hidden gemm + starting block");
@@ -422,15 +430,7 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
     XP_TRY(xpress::launch_hidden_gemm(h, w->down_h, w->down_g, N * B, w->H, r, hdg, s), "hidden gemm");
   XP_TRY(xpress::launch_hidden_project(hdg, w->H, w->in_proj, N, B, r, xh, s), "hidden project");
   if (!init) XP_TRY(xpress::launch_set_anchor(anchor, N, B, blk, s), "set anchor");
-  int64_t* cand = at<int64_t>(ws, L.cand);
-  xpress_bf16* base_c = at<xpress_bf16>(ws, L.base_c);
-  xpress_bf16* w2c = at<xpress_bf16>(ws, L.w2c);
-  if (c > 0) {
-    XP_TRY(xpress::launch_topc_select(base, base_ld, rows, V, c, cand, base_c, anchor,
-                                      init ? blk : nullptr, B, at<uint16_t>(ws, L.cmax), s),
-           "top-C select");
-    XP_TRY(xpress::launch_topc_gather(cand, w->w2, rows, c, r, w2c, s), "top-C gather");
-  }
+  if (c > 0) XP_TRY(xpress::launch_topc_gather(cand, w->w2, rows, c, r, w2c, s), "top-C gather");
   const bool stop = (flags & XPRESS_STOP_AT_FIXED_POINT) != 0;
   const bool fused = use_table(w, N);
   int32_t* pf = stop ? at<int32_t>(ws, L.flags) : nullptr;
