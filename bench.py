@@ -13,6 +13,9 @@ included). Also reported:
     + lat, or w2c + base_c + cand + lat) over its average duration measured with HIP events on
     the launch stream, against the 8 TB/s HBM peak; its rate against the 2.5 PFLOP/s bf16 MFMA
     peak is in `extra`;
+  * `extra.measured_peaks`: achievable yardsticks timed on the same GPU with library kernels
+    (a 1 GiB device-to-device copy and a 2 GiB reduction for HBM, an 8192^3 bf16 torch.matmul
+    for the matrix cores), and the readout's fractions of them;
   * `cpu_baseline`: the CPU oracle timed on this host on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -45,6 +48,8 @@ def parse():
     ap.add_argument("--workload", type=int, default=3, help="synthetic workload id (2..5)")
     ap.add_argument("--kernel-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured streaming-read and bf16-GEMM reference peaks")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB three times "
@@ -255,10 +260,60 @@ def main() -> int:
         },
     }
 
+    if not args.no_peaks:
+        pk = measured_peaks(dev)
+        out["extra"]["measured_peaks"] = pk
+        out["extra"]["readout_frac_of_measured_hbm"] = round(achieved_gbs / pk["hbm_GBps"], 4)
+        out["extra"]["readout_frac_of_measured_bf16_gemm"] = round(mfma_tflops / pk["bf16_gemm_TFLOPs"], 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, K, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def measured_peaks(dev):
+    """Achievable references on this GPU, beside the published peaks: the HBM rate of a reduction
+    over 2 GiB and of a 1 GiB device-to-device copy (torch's own kernels; the larger is the
+    reference) and the throughput of a large bf16 GEMM (torch.matmul, i.e. hipBLASLt). Library
+    kernels, timed here only as yardsticks."""
+    import torch
+
+    log("measured peaks: streaming read and bf16 GEMM references")
+    x = torch.empty(1 << 29, dtype=torch.float32, device=dev).fill_(1.0)  # 2 GiB
+    a = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    x.sum()
+    torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        x.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    read_gbs = 10 * x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    y = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB copied from half of x
+    y.copy_(x[: 1 << 28])
+    e0.record()
+    for _ in range(10):
+        y.copy_(x[: 1 << 28])
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 10 * 2 * y.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del y
+    e0.record()
+    for _ in range(10):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 10 * 2.0 * 8192 ** 3 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del x, a, b
+    torch.cuda.empty_cache()
+    return {"hbm_GBps": round(max(read_gbs, copy_gbs), 1),
+            "sum_read_GBps": round(read_gbs, 1), "sum_kernel": "torch sum over 2 GiB fp32",
+            "copy_GBps": round(copy_gbs, 1), "copy": "1 GiB device-to-device copy, read + write bytes",
+            "bf16_gemm_TFLOPs": round(gemm_tflops, 1),
+            "bf16_gemm": "torch.matmul 8192 x 8192 x 8192 bf16"}
 
 
 def cpu_baseline(inp, K, budget_s):
