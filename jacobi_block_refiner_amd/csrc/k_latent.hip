@@ -1,4 +1,5 @@
-// Latent stage of one XPress pass (gfx950), as three wide kernels.
+// Latent stage of one XPress pass (gfx950): two kernels from a projected embedding table, or
+// three wide kernels that project the gathered embeddings themselves.
 //
 // For every block (vLLM API page "vllm.v1.worker.gpu.spec_decode.xpress.kernels",
 // _xpress_latent_kernel docstring; "vllm.model_executor.models.qwen3_xpress",
@@ -18,6 +19,10 @@
 //   latent_down_kernel  (row tile, 64 channels): step 5, lat in bf16.
 // Each workgroup reads at most 64 KB of weights; row tiles of 64 rows (4 blocks) share weight
 // reads when there are many blocks.
+// With the projected table w1p = P_e applied to every row of w1 (fold_embedding_kernel, once per
+// weight set), step 2 is a row gather, and below 128 blocks the stage runs as
+//   latent_share_kernel (block, 64 hidden units): steps 1-4 and the slice's share of step 5;
+//   latent_sum_kernel   (block, slots): the shares summed in slice order into lat.
 //
 // v_mfma_f32_16x16x32_bf16 operand layout (wave64):
 //   A (16 x 32): lane l holds row l%16, k = 8*(l/16) + e, e = 0..7
