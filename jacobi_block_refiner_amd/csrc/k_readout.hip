@@ -156,34 +156,39 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
     return l;
   };
-  // Issue the copies of step t into stage st.
+  // Issue the copies of step t into stage st. The LDS destinations are scalar (the wave index is
+  // uniform), and one uniform branch per step picks the clamped offsets of the vocabulary's last
+  // step, so the common path is the copies alone.
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   auto copy_step = [&](int t, int st) __attribute__((always_inline)) {
     const uint32_t sbase = lds0 + (uint32_t)st * (SCH * 16);
     const uint16_t* gw = w2 + (int64_t)t * 32 * R;
     const uint16_t* gb = base_rc + 32 * t;
-    const bool tail = 32 * t + 32 > V;  // uniform
+    if (32 * t + 32 > V) {  // uniform: the last step of the vocabulary
 #pragma unroll
-    for (int q = 0; q < WI; ++q) {
-      const int ins = (wave + q * kNW) % NI;
-      uint32_t off = offw[q];
-      if (tail) {
+      for (int q = 0; q < WI; ++q) {
+        const int ins = (wave_s + q * kNW) % NI;
         const int ln = opaque_lane_id();
         const int i = (ln / RQ) * NI + ins, c = ln % RQ;
-        off = (uint32_t)(((min(32 * t + w2_row_id(i), V - 1) - 32 * t) * R + 8 * c) * 2);
+        const uint32_t off = (uint32_t)(((min(32 * t + w2_row_id(i), V - 1) - 32 * t) * R + 8 * c) * 2);
+        lds_copy16(gw, off, sbase + ins * WP * 16);
       }
-      lds_copy16(gw, off, __builtin_amdgcn_readfirstlane(sbase + ins * WP * 16));
-    }
 #pragma unroll
-    for (int q = 0; q < BI; ++q) {
-      const int ins = (wave + q * kNW) % NBI;
-      uint32_t off = offb[q];
-      if (tail) {
+      for (int q = 0; q < BI; ++q) {
+        const int ins = (wave_s + q * kNW) % NBI;
         const int p = ins * 64 + opaque_lane_id();
         const int rr = p >> 2, c = (p & 3) ^ ((rr >> 2) & 3);
-        off = (uint32_t)(((int64_t)(min(row0 + rr, rows - 1) - row0) * ld +
-                          8 * (min(4 * t + c, last_chunk) - 4 * t)) * 2);
+        const uint32_t off = (uint32_t)(((int64_t)(min(row0 + rr, rows - 1) - row0) * ld +
+                                         8 * (min(4 * t + c, last_chunk) - 4 * t)) * 2);
+        lds_copy16(gb, off, sbase + (WCH + ins * 64) * 16);
       }
-      lds_copy16(gb, off, __builtin_amdgcn_readfirstlane(sbase + (WCH + ins * 64) * 16));
+    } else {
+#pragma unroll
+      for (int q = 0; q < WI; ++q)
+        lds_copy16(gw, offw[q], sbase + ((wave_s + q * kNW) % NI) * WP * 16);
+#pragma unroll
+      for (int q = 0; q < BI; ++q)
+        lds_copy16(gb, offb[q], sbase + (WCH + ((wave_s + q * kNW) % NBI) * 64) * 16);
     }
   };
 
