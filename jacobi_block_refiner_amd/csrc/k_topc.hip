@@ -617,7 +617,7 @@ __global__ __launch_bounds__(256) void topc_readout_kernel(
   if (pass_skipped(flags, pass)) return;
   constexpr int G = R / 8;        // lanes per candidate
   constexpr int CPW = 64 / G;     // candidates per wave per load
-  constexpr int U = 8;            // loads in flight per lane
+  constexpr int U = 4;            // loads in flight per lane (2, 3, 6, 8 and 16 measured slower)
   constexpr int CPR = 4 * CPW * U;  // candidates per workgroup round
   __shared__ float s_v[4];
   __shared__ int s_i[4];
