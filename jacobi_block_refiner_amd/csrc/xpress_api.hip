@@ -99,12 +99,12 @@ xpress_status check_base(const xpress_bf16* base, int64_t ld, int64_t V) {
   return XPRESS_OK;
 }
 
-// Whether the latent stage runs from the projected embedding table (share + sum kernels). From
-// 128 blocks on the three-kernel path is faster (46 against 50 us per pass at 256 blocks: the
-// shares of the down product, G fp32 copies of lat, then cost more traffic than the projection
-// they replace) and is taken even when the table is given; the results agree within fp32
-// rounding either way.
-constexpr int kTableMaxN = 127;
+// Whether the latent stage runs from the projected embedding table (share + sum kernels). Per
+// pass: 11 against 16 us at 32 blocks, equal at 64 and 96; from there on the three-kernel path
+// wins (34 against 37 us at 127 blocks, 46 against 50 at 256: the fp32 shares of the down
+// product, G copies of lat, then cost more than the projection they replace) and is taken even
+// when the table is given. The results agree within fp32 rounding either way.
+constexpr int kTableMaxN = 96;
 bool use_table(const xpress_weights* w, int N) { return w->w1p != nullptr && N <= kTableMaxN; }
 
 // Scratch of the latent stage: the three-kernel path's, or the larger projected-table path's
