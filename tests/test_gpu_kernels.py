@@ -214,6 +214,8 @@ def test_fold_embedding_matches_oracle_projection(r, V):
                                          (3, 2, {"V": 2048, "M": 1024}),
                                          (1, 37, {"B": 16, "r": 256, "M": 512, "V": 3000}),
                                          (1, 5, {"B": 2, "r": 64, "M": 64, "V": 700}),
+                                         # 96 blocks: the largest the table path takes;
+                                         (1, 96, {"B": 16, "r": 256, "M": 512, "V": 3000}),
                                          # from 97 blocks on the three-kernel path runs, table or not
                                          (1, 130, {"B": 16, "r": 256, "M": 512, "V": 3000}),
                                          (1, 129, {"B": 5, "r": 128, "M": 128, "V": 1000})])
