@@ -146,7 +146,7 @@ def main() -> int:
     lat = torch.empty(wl.N, wl.B - 1, wl.r, dtype=torch.bfloat16, device=dev)
     blk2 = blk.clone()
     xpress.latent_pass(w, blk2, am1, xh, lat, ws)
-    ntiles = xpress.readout_tiles(wl.V)
+    ntiles = xpress.readout_tiles(wl.V, rows)
     part = torch.empty(ntiles, rows, 2, dtype=torch.int32, device=dev)
 
     def timed(fn, reps):

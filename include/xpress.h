@@ -155,14 +155,18 @@ xpress_status xpress_readout_argmax(const xpress_weights* w, const xpress_bf16* 
  * themselves (for example across GPUs that each hold a slice of the vocabulary) and for timing
  * the readout GEMM on its own (kernels page, _xpress_add_argmax_partial_kernel and
  * _xpress_add_argmax_reduce_to_blk_kernel).
- * xpress_readout_tiles: number of partials per readout row: the vocabulary is cut into
- *   ntiles = min(256, ceil(V / 32)) contiguous ranges of whole 32-id steps (depends on V only).
+ * xpress_readout_tiles: number of partials per readout row for `rows` = N*(B-1) readout rows:
+ *   the vocabulary is cut into ntiles contiguous ranges of whole 32-id steps, ntiles =
+ *   min(ceil(V / 32), 256) up to 512 rows and min(ceil(V / 32), max(8, floor(256 / k) rounded
+ *   down to a multiple of 8)) with k = ceil(rows / 512) beyond (about one workgroup per CU).
+ *   With S = ceil(V / 32) steps, range t holds the ids of steps floor(S*t / ntiles) up to (not
+ *   including) floor(S*(t+1) / ntiles), the last clipped to V. rows < 1 is XPRESS_ERR_ARG.
  * xpress_readout_partials: part[t * N*(B-1) + p] = {bits of the fp32 maximum of base + lat . w2
  *   over range t of row p, the lowest vocabulary id attaining it}. part: [ntiles, N*(B-1)] pairs
  *   of uint32, range-major (caller-owned, 8 bytes each).
  * xpress_argmax_reduce: blk[n, b] = the id of the largest pair of row p = n*(B-1)+b-1 (ties:
  *   lowest id), written in place; `changed` as in xpress_readout_argmax. */
-xpress_status xpress_readout_tiles(int64_t V, int32_t* ntiles);
+xpress_status xpress_readout_tiles(int64_t V, int32_t rows, int32_t* ntiles);
 xpress_status xpress_readout_partials(const xpress_weights* w, const xpress_bf16* lat,
                                       const xpress_bf16* base, int64_t base_ld, int32_t N,
                                       uint32_t* part, xpress_stream stream);

@@ -422,7 +422,7 @@ template <int R, int NW, int RW, int NS, int TR>
 hipError_t launch_partial_t(const uint16_t* lat, const uint16_t* w2, const uint16_t* base,
                             int64_t ld, int rows, int64_t V, uint2* part, const int32_t* flags,
                             int pass, hipStream_t s) {
-  const int nvr = readout_tiles(V);
+  const int nvr = readout_tiles(V, rows);
   constexpr int CH = TR * 32;
   const int n_rc = (rows + CH - 1) / CH;
   hipLaunchKernelGGL((readout_partial_kernel<R, NW, RW, NS, TR>), dim3((unsigned)(nvr * n_rc)), dim3(64 * NW),
@@ -451,9 +451,17 @@ hipError_t launch_partial_shape(const uint16_t* lat, const uint16_t* w2, const u
 
 }  // namespace
 
-int readout_tiles(int64_t V) {
+// Up to 512 rows a launch is one row chunk and the vocabulary is cut into 256 ranges (one
+// workgroup per CU); with n_rc > 1 chunks of 512 rows, into about 256 / n_rc ranges (a multiple of
+// 8, at least 8), so the launch is still about one workgroup per CU, each over a longer range: the
+// lat loads and the copy ring's start are paid once per workgroup (3840 rows: 32 ranges, 357-360
+// us against 399-414 us with 256 ranges, 364 with 64, 375 with 128; 48 ranges, 384 workgroups,
+// leave half the CUs a second round: 400 us).
+int readout_tiles(int64_t V, int rows) {
   const int64_t steps = (V + 31) / 32;
-  return (int)(steps < kMaxRanges ? steps : kMaxRanges);
+  const int n_rc = rows <= 512 ? 1 : (rows + 511) / 512;
+  const int target = n_rc == 1 ? kMaxRanges : max(8, (kMaxRanges / n_rc) & ~7);
+  return (int)(steps < target ? steps : target);
 }
 
 hipError_t launch_readout_partial(const uint16_t* lat, const uint16_t* w2, const uint16_t* base,

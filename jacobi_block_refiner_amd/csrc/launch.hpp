@@ -7,9 +7,10 @@
 
 namespace xpress {
 
-// Readout partials per row: the vocabulary is cut into min(256, ceil(V/32)) contiguous ranges of
-// 32-id steps; the readout kernel leaves one (max, lowest id) partial per (row, range).
-int readout_tiles(int64_t V);
+// Readout partials per row: the vocabulary is cut into contiguous ranges of 32-id steps, at most
+// min(256, ceil(V/32)) of them (fewer above 512 rows: about one workgroup per CU either way);
+// the readout kernel leaves one (max, lowest id) partial per (row, range).
+int readout_tiles(int64_t V, int rows);
 
 // K1a: split-K partials of hdg[m, j] = sum_k h[m, k] * Wcat[j, k], Wcat = [down_h; down_g],
 // m < NB = N*B, j < 2r; scratch [hidden_splits, NB, 2r] fp32.

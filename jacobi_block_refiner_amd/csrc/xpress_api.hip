@@ -138,7 +138,8 @@ Layout step_layout(int N, int B, int r, int H, int64_t V, int C, int K) {
   L.xh = take((size_t)N * B * r * sizeof(float));
   L.lat = take(rows * r * 2);
   L.lscr = take(latent_bytes(N, r, kMaxM));
-  L.part = take(C > 0 ? 0 : rows * (size_t)xpress::readout_tiles(V) * sizeof(uint2));
+  // sized for the largest range count (the count at one row chunk)
+  L.part = take(C > 0 ? 0 : rows * (size_t)xpress::readout_tiles(V, 1) * sizeof(uint2));
   L.flags = take((size_t)(K + 1) * sizeof(int32_t));
   L.cand = take(rows * c * sizeof(int64_t));
   L.base_c = take(rows * c * 2);
@@ -283,7 +284,7 @@ xpress_status xpress_readout_argmax(const xpress_weights* w, const xpress_bf16* 
   XP_PTR(blk);
   XP_PTR(ws);
   const int rows = N * (w->B - 1);
-  const int ntiles = xpress::readout_tiles(w->V);
+  const int ntiles = xpress::readout_tiles(w->V, rows);
   const size_t need = (size_t)rows * ntiles * sizeof(uint2);
   if (ws_bytes < need)
     return fail(XPRESS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed for N=%d", ws_bytes, need, N);
@@ -296,11 +297,12 @@ xpress_status xpress_readout_argmax(const xpress_weights* w, const xpress_bf16* 
   return XPRESS_OK;
 }
 
-xpress_status xpress_readout_tiles(int64_t V, int32_t* ntiles) {
+xpress_status xpress_readout_tiles(int64_t V, int32_t rows, int32_t* ntiles) {
   if (ntiles == nullptr) return fail(XPRESS_ERR_ARG, "ntiles is NULL");
   xpress_status st = check_dims(2, 64, V);
   if (st != XPRESS_OK) return st;
-  *ntiles = xpress::readout_tiles(V);
+  if (rows < 1) return fail(XPRESS_ERR_ARG, "rows=%d < 1", rows);
+  *ntiles = xpress::readout_tiles(V, rows);
   return XPRESS_OK;
 }
 
@@ -436,7 +438,7 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
   int32_t* pf = stop ? at<int32_t>(ws, L.flags) : nullptr;
   if (stop) XP_TRY(xpress::launch_flags_reset(pf, K + 1, s), "flags reset");
   uint2* part = at<uint2>(ws, L.part);
-  const int ntiles = xpress::readout_tiles(V);
+  const int ntiles = xpress::readout_tiles(V, rows);
   // Full vocabulary: the argmax reduce of pass p-1 runs inside pass p's first latent kernel (each
   // block finishes its own rows); only the last pass's reduce is a launch of its own.
   for (int p = 0; p < K; ++p) {

@@ -66,7 +66,7 @@ def lib() -> ctypes.CDLL:
             "xpress_initial_block": [P, i64, P, i32, i32, i64, P, P],
             "xpress_latent_pass": [W, P, P, P, i32, P, P, sz, P],
             "xpress_readout_argmax": [W, P, P, i64, i32, P, P, P, sz, P],
-            "xpress_readout_tiles": [i64, ctypes.POINTER(i32)],
+            "xpress_readout_tiles": [i64, i32, ctypes.POINTER(i32)],
             "xpress_readout_partials": [W, P, P, i64, i32, P, P],
             "xpress_argmax_reduce": [P, i32, i32, i32, P, P, P],
             "xpress_topc_prepare": [W, P, i64, i32, i32, P, P, P, P, sz, P],
@@ -221,9 +221,9 @@ def readout_argmax(w: Weights, lat, base, blk, ws, changed=None) -> torch.Tensor
     return blk
 
 
-def readout_tiles(V: int) -> int:
+def readout_tiles(V: int, rows: int) -> int:
     out = ctypes.c_int32()
-    _check(lib().xpress_readout_tiles(V, ctypes.byref(out)))
+    _check(lib().xpress_readout_tiles(V, rows, ctypes.byref(out)))
     return int(out.value)
 
 

@@ -110,3 +110,21 @@ def test_workspace_for_n_max_fits_every_smaller_n():
         for n in (1, 32, 96, 97, 127, 128, n_max):
             if n <= n_max:
                 assert xpress.workspace_size(n, 16, 256, 151936, 0, 15) <= big, (n, n_max)
+
+
+@pytest.mark.parametrize("V,rows,want", [(151936, 15, 256), (151936, 512, 256), (151936, 513, 128),
+                                         (151936, 1536, 80), (151936, 3840, 32),
+                                         (151936, 20000, 8), (100, 3840, 4), (33, 1, 2),
+                                         (5003, 600, 128)])
+def test_readout_range_count(V, rows, want):
+    """Partials per readout row: 256 ranges (at most ceil(V/32)) up to one 512-row chunk, about
+    256 / chunks beyond, a multiple of 8 and at least 8 (host-side arithmetic, no kernel)."""
+    assert xpress.readout_tiles(V, rows) == want
+
+
+def test_readout_range_count_rejects_bad_arguments():
+    L = xpress.lib()
+    out = ctypes.c_int32()
+    assert L.xpress_readout_tiles(151936, 0, ctypes.byref(out)) == xpress.ERR_ARG
+    assert L.xpress_readout_tiles(0, 15, ctypes.byref(out)) == xpress.ERR_ARG
+    assert L.xpress_readout_tiles(151936, 15, None) == xpress.ERR_ARG

@@ -105,6 +105,42 @@ def test_readout_argmax_dyadic_exact(r, V, N):
     assert int(changed.item()) == int(not np.array_equal(draft_rows(blk0), best))
 
 
+# 45 rows: one row chunk, 256 ranges; 600 and 1800 rows: two and four chunks of 512 rows, so
+# 128 and 64 longer ranges
+@pytest.mark.parametrize("r,V,N", [(128, 8192, 3), (128, 8195, 40), (64, 20000, 120)])
+def test_readout_partials_per_range_and_reduce(r, V, N):
+    """The two-stage readout through the C ABI: each (range, row) partial is the exact maximum
+    and lowest id over range t = steps [S*t // ntiles, S*(t+1) // ntiles) of the S = ceil(V/32)
+    32-id steps (dyadic values, so every fp32 sum is exact), and their reduce gives the one-call
+    readout's block."""
+    B = 16
+    rows = N * (B - 1)
+    lat, w2, base = _readout_case(6, N, B, r, V)
+    w = _weights_with(w2, r, B, V)
+    ntiles = xpress.readout_tiles(V, rows)
+    S = (V + 31) // 32
+    want_nt = min(S, 256 if rows <= 512 else max(8, (256 // -(-rows // 512)) & ~7))
+    assert ntiles == want_nt
+    part = torch.full((ntiles, rows, 2), -1, dtype=torch.int32, device="cuda")
+    lat_d, base_d = upload.bf16_tensor(lat), upload.base_logits(base)
+    log(f"readout partials r={r} V={V} N={N} ntiles={ntiles}")
+    xpress.readout_partials(w, lat_d, base_d, part)
+    blk_two = torch.zeros(N, B, dtype=torch.int64, device="cuda")
+    xpress.argmax_reduce(part, blk_two)
+    blk_one = torch.zeros(N, B, dtype=torch.int64, device="cuda")
+    xpress.readout_argmax(w, lat_d, base_d, blk_one, xpress.alloc_workspace(N, B, r, V, 0, 1))
+    torch.cuda.synchronize()
+    got = part.cpu().numpy()
+    for t in range(ntiles):
+        a, b = 32 * (S * t // ntiles), min(V, 32 * (S * (t + 1) // ntiles))
+        best, _, val = O.readout_argmax(lat, w2[a:b], np.ascontiguousarray(base[:, a:b]))
+        assert np.array_equal(got[t, :, 1], best + a), t
+        assert np.array_equal(got[t, :, 0].view(np.float32), val.astype(np.float32)), t
+    full, _, _ = O.readout_argmax(lat, w2, base)
+    assert np.array_equal(draft_rows(blk_two.cpu().numpy()), full)
+    assert torch.equal(blk_two, blk_one)
+
+
 @pytest.mark.parametrize("V", [1, 7, 31, 33])
 def test_readout_argmax_small_vocabulary(V):
     """A vocabulary of fewer ids than one 32-id step (or just past it): the single partial step's
