@@ -37,28 +37,35 @@ namespace xpress {
 
 namespace {
 
-// The token each of the 16 slots of block n reads (slot 0: am1[n], slot b: blk[n, b-1]; -1 for
-// slots past B) into tok (LDS). With `part` (inside a step, pass >= 1) the block first finishes
-// the previous pass: the partial winners of its readout rows (range-major, `ntiles` <= 256
-// ranges) are reduced to the block's new tokens -- the work of the argmax-reduce kernel for these
-// rows, without its launch. Every workgroup of the block reduces them (the same result); the one
-// with `writer` set writes them into blk and raises flags[pass-1] on a change. Called by all 256
-// threads; the caller synchronises before reading tok.
-__device__ __forceinline__ void block_tokens(const uint2* __restrict__ part, int ntiles, int rows,
-                                             int64_t* __restrict__ blk,
-                                             const int64_t* __restrict__ am1, int n, int B,
-                                             bool writer, int32_t* __restrict__ flags, int pass,
-                                             int64_t* tok) {
+// block_tokens_*: the token each of the 16 slots of block n reads (slot 0: am1[n], slot b:
+// blk[n, b-1]; -1 for slots past B) into tok (LDS). With `part` (inside a step, pass >= 1) the
+// block first finishes the previous pass: the partial winners of its readout rows (range-major,
+// `ntiles` <= 256 ranges) are reduced to the block's new tokens -- the work of the argmax-reduce
+// kernel for these rows, without its launch. Every workgroup of the block reduces them (the same
+// result); the one with `writer` set writes them into blk and raises flags[pass-1] on a change.
+// Two halves, so that a kernel can issue the partials' loads (the head of its dependency chain)
+// before its other loads and reduce them after: block_tokens_load fills this thread's 16
+// partials (thread: readout row tid/16 of the block, ranges tid%16 + 16k; clamped repeats change
+// nothing), block_tokens_finish reduces them (q is ignored without part). Both are called by all
+// 256 threads; the caller synchronises before reading tok.
+__device__ __forceinline__ void block_tokens_load(const uint2* __restrict__ part, int ntiles,
+                                                  int rows, int n, int B, uint2 (&q)[16]) {
+  const int rb = threadIdx.x >> 4, j = threadIdx.x & 15;
+  const uint2* pr = part + (int64_t)n * (B - 1) + min(rb, B - 2);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) q[k] = pr[(int64_t)min(j + 16 * k, ntiles - 1) * rows];
+}
+
+__device__ __forceinline__ void block_tokens_finish(bool has_part, const uint2 (&q)[16],
+                                                    int64_t* __restrict__ blk,
+                                                    const int64_t* __restrict__ am1, int n, int B,
+                                                    bool writer, int32_t* __restrict__ flags,
+                                                    int pass, int64_t* tok) {
   const int tid = threadIdx.x;
-  if (part) {
-    // all 16 loads per thread are issued before the first merge (clamped repeats change nothing)
+  if (has_part) {
     const int rb = tid >> 4, j = tid & 15;  // readout row rb of the block, range slice j
     float bv = -INFINITY;
     int bi = INT_MAX;
-    const uint2* pr = part + (int64_t)n * (B - 1) + min(rb, B - 2);
-    uint2 q[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) q[k] = pr[(int64_t)min(j + 16 * k, ntiles - 1) * rows];
     if (rb < B - 1) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) argmax_merge(bv, bi, __uint_as_float(q[k].x), (int)q[k].y);
@@ -91,7 +98,7 @@ __device__ __forceinline__ void block_tokens(const uint2* __restrict__ part, int
 }
 
 // Steps 1-3 for one block and 64 channels (blockIdx.y); 4 waves. With `part` given (inside a
-// step), the block first finishes the previous pass (block_tokens); slice 0 writes blk.
+// step), the block first finishes the previous pass (block_tokens_*); slice 0 writes blk.
 template <int R>
 __global__ __launch_bounds__(256) void latent_mix_kernel(
     const uint2* __restrict__ part, int ntiles, int rows, int64_t* __restrict__ blk,
@@ -105,9 +112,12 @@ __global__ __launch_bounds__(256) void latent_mix_kernel(
   const int n = blockIdx.x, c0 = blockIdx.y * 64, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
 
-  // Mixer taps of this thread's channel c0 + lane for slots 4*wave .. 4*wave+3 (independent of
-  // the tokens, so loaded first): mix_L is [B, B, r], channel innermost, so a tap is one
-  // coalesced 2-byte load across the wave. Taps past B or above the diagonal are not used.
+  // The previous pass's partials first (they head the dependency chain), then the mixer taps of
+  // this thread's channel c0 + lane for slots 4*wave .. 4*wave+3 (independent of the tokens):
+  // mix_L is [B, B, r], channel innermost, so a tap is one coalesced 2-byte load across the wave.
+  // Taps past B or above the diagonal are not used.
+  uint2 qp[16];
+  if (part) block_tokens_load(part, ntiles, rows, n, B, qp);
   uint16_t tap[4][16];
   {
     const int bb = min(4 * wave, B - 1);
@@ -120,7 +130,7 @@ __global__ __launch_bounds__(256) void latent_mix_kernel(
       }
   }
 
-  block_tokens(part, ntiles, rows, blk, am1, n, B, blockIdx.y == 0, flags, pass, s_tok);
+  block_tokens_finish(part != nullptr, qp, blk, am1, n, B, blockIdx.y == 0, flags, pass, s_tok);
   __syncthreads();
 
   // steps 1-2: x[slot, c] = xh[slot, c] + sum_k P_e[c, k] w1[tok(slot), k]; wave w computes the
@@ -317,7 +327,7 @@ __global__ __launch_bounds__(256) void fold_embedding_kernel(const uint16_t* __r
 // The latent stage from the projected embedding table w1p, in two launches. Workgroup (n, g)
 // of latent_share_kernel takes block n and the 64 SwiGLU units g*64 .. g*64+63 (G = M/64
 // workgroups per block):
-//   0. the block's tokens (block_tokens; inside a step this finishes the previous pass);
+//   0. the block's tokens (block_tokens_*; inside a step this finishes the previous pass);
 //   1. x[b, c] = xh[b, c] + w1p[tok(b), c]            thread c < r, all 16 slots in registers;
 //   2. u[b, c] = sum_{j<=b} L[b, j, c] x[j, c]          same thread, taps in registers;
 //   3. a = w_gate[units] . u, e = w_up[units] . u,  s = silu(a) * e   (16x16x32 MFMAs);
@@ -348,7 +358,11 @@ __global__ __launch_bounds__(256) void latent_share_kernel(
   const bool chan = tid < R;  // thread tid owns channel tid in steps 1-2
   const int c = min(tid, R - 1);
 
-  // Loads that do not depend on the tokens go first: the slice's gate/up rows, xh and the taps.
+  // The previous pass's partials head the dependency chain (partials -> tokens -> w1p rows), so
+  // their loads are issued first (1% faster steps than issuing them after the others); then the
+  // loads that do not depend on the tokens: the slice's gate/up rows, xh and the taps.
+  uint2 qp[16];
+  if (part) block_tokens_load(part, ntiles, rows, n, B, qp);
   const int m = g * 64 + wave * 16 + l16;
   bf16x8 gB[KS], uB[KS];
   {
@@ -375,7 +389,7 @@ __global__ __launch_bounds__(256) void latent_share_kernel(
     for (int j = 0; j <= b; ++j, ++k)
       tap[k] = mix_L[((int64_t)min(b, B - 1) * B + min(j, B - 1)) * R + c];
 
-  block_tokens(part, ntiles, rows, blk, am1, n, B, g == 0, flags, pass, s_tok);
+  block_tokens_finish(part != nullptr, qp, blk, am1, n, B, g == 0, flags, pass, s_tok);
   __syncthreads();
 
   // steps 1-2
