@@ -106,8 +106,10 @@ def test_readout_argmax_dyadic_exact(r, V, N):
 
 
 # 45 rows: one row chunk, 256 ranges; 600 and 1800 rows: two and four chunks of 512 rows, so
-# 128 and 64 longer ranges
-@pytest.mark.parametrize("r,V,N", [(128, 8192, 3), (128, 8195, 40), (64, 20000, 120)])
+# 128 and 64 longer ranges; V = 3001 at 600 rows: 94 ranges of one or two steps (not a multiple
+# of 8, so the plain workgroup order rather than the per-XCD one)
+@pytest.mark.parametrize("r,V,N", [(128, 8192, 3), (128, 8195, 40), (64, 20000, 120),
+                                   (128, 3001, 40)])
 def test_readout_partials_per_range_and_reduce(r, V, N):
     """The two-stage readout through the C ABI: each (range, row) partial is the exact maximum
     and lowest id over range t = steps [S*t // ntiles, S*(t+1) // ntiles) of the S = ceil(V/32)
