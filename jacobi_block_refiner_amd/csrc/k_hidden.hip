@@ -42,27 +42,31 @@ __global__ __launch_bounds__(256) void step_start_kernel(
     initial_block_row(base, ld, anchor, B, V, blk, i - g1);
 }
 
-// One workgroup per (block n, 64 output channels), in fp32:
+// One workgroup per (block n, CW output channels), in fp32:
 //   hdg[n, b, j] = sum_s part[s, n*B + b, j]            (splits in ascending order)
 //   hg[k] = (1/B) sum_b hdg[n, b, r + k]                 (slots in ascending order)
 //   xh[n, b, c] = sum_k P[c, k] hdg[n, b, k] + sum_k P[c, r + k] hg[k]
-// The block's slots and its 64 rows of in_proj's hidden half are staged in LDS with coalesced
+// The block's slots and its CW rows of in_proj's hidden half are staged in LDS with coalesced
 // loads (many in flight); hd and hg are then read as broadcasts, the in_proj rows with a padded
-// pitch (no bank conflicts).
-template <int R>
+// pitch (no bank conflicts). Thread (channel tid % CW, slot group tid / CW) computes CW/16
+// slots. Fewer channels per workgroup give more workgroups (each re-reads the block's partials,
+// L2 hits) and less arithmetic per thread; the launcher picks CW for about 256 workgroups.
+template <int R, int CW>
 __global__ __launch_bounds__(256) void hidden_project_kernel(const float* __restrict__ part,
                                                              int nsplit, int NB,
                                                              const uint16_t* __restrict__ in_proj,
                                                              int B, float* __restrict__ xh) {
+  static_assert(CW == 16 || CW == 32 || CW == 64, "channels per workgroup");
   constexpr int PQ = 2 * R / 8;     // 16-byte chunks of a staged in_proj row
   constexpr int PP = PQ + 1;        // padded pitch
+  constexpr int SPG = CW / 16;      // slots per thread
   __shared__ float s_hdg[16][2 * R];
   __shared__ float s_hg[R];
-  __shared__ float s_gp[64];
-  __shared__ uint4 s_p[64 * PP];
-  const int n = blockIdx.x, c0 = blockIdx.y * 64, tid = threadIdx.x;
+  __shared__ float s_gp[CW];
+  __shared__ uint4 s_p[CW * PP];
+  const int n = blockIdx.x, c0 = blockIdx.y * CW, tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 64 * PQ / 256; ++i) {  // all of the thread's loads in flight together
+  for (int i = 0; i < CW * PQ / 256; ++i) {  // all of the thread's loads in flight together
     const int q = tid + 256 * i, row = q / PQ, col = q % PQ;
     s_p[row * PP + col] = reinterpret_cast<const uint4*>(in_proj + (int64_t)(c0 + row) * 3 * R)[col];
   }
@@ -107,7 +111,7 @@ __global__ __launch_bounds__(256) void hidden_project_kernel(const float* __rest
     s_hg[k] = sum / (float)B;
   }
   __syncthreads();
-  const int c = tid & 63, grp = tid >> 6;  // grp: slots 4*grp .. 4*grp+3
+  const int c = tid % CW, grp = tid / CW;  // grp: slots SPG*grp .. SPG*grp+SPG-1
   const uint4* prow = s_p + c * PP;
   if (grp == 0) {
     float g = 0.f;
@@ -120,8 +124,10 @@ __global__ __launch_bounds__(256) void hidden_project_kernel(const float* __rest
     }
     s_gp[c] = g;
   }
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  const int b0 = min(4 * grp, 15);
+  float acc[SPG];
+#pragma unroll
+  for (int v = 0; v < SPG; ++v) acc[v] = 0.f;
+  const int b0 = SPG * grp;  // < 16
   for (int kq = 0; kq < R / 8; ++kq) {
     const uint4 u = prow[kq];
     const float w8[8] = {bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y),
@@ -129,12 +135,12 @@ __global__ __launch_bounds__(256) void hidden_project_kernel(const float* __rest
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] = fmaf(w8[e], s_hdg[min(b0 + v, 15)][8 * kq + e], acc[v]);
+      for (int v = 0; v < SPG; ++v) acc[v] = fmaf(w8[e], s_hdg[b0 + v][8 * kq + e], acc[v]);
   }
   __syncthreads();
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int b = 4 * grp + v;
+  for (int v = 0; v < SPG; ++v) {
+    const int b = SPG * grp + v;
     if (b < B) xh[((int64_t)n * B + b) * R + c0 + c] = acc[v] + s_gp[c];
   }
 }
@@ -200,24 +206,37 @@ hipError_t launch_step_start(const uint16_t* h, const uint16_t* down_h, const ui
   return hipGetLastError();
 }
 
+template <int R>
+hipError_t launch_project_r(const float* part, int ns, int NB, const uint16_t* in_proj, int N,
+                            int B, float* xh, hipStream_t s) {
+  // the most channels per workgroup that still give >= 256 workgroups (16 below that)
+  const int cw = N * (R / 64) >= 256 ? 64 : (N * (R / 32) >= 256 ? 32 : 16);
+  switch (cw) {
+    case 64:
+      hipLaunchKernelGGL((hidden_project_kernel<R, 64>), dim3(N, R / 64), dim3(256), 0, s, part,
+                         ns, NB, in_proj, B, xh);
+      break;
+    case 32:
+      hipLaunchKernelGGL((hidden_project_kernel<R, 32>), dim3(N, R / 32), dim3(256), 0, s, part,
+                         ns, NB, in_proj, B, xh);
+      break;
+    default:
+      hipLaunchKernelGGL((hidden_project_kernel<R, 16>), dim3(N, R / 16), dim3(256), 0, s, part,
+                         ns, NB, in_proj, B, xh);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_hidden_project(const float* part, int H, const uint16_t* in_proj, int N, int B,
                                  int r, float* xh, hipStream_t s) {
   const int NB = N * B;
   const int ns = hidden_splits(NB, H, r);
-  dim3 grid(N, r / 64);
   switch (r) {
-    case 64:
-      hipLaunchKernelGGL(hidden_project_kernel<64>, grid, dim3(256), 0, s, part, ns, NB, in_proj, B, xh);
-      break;
-    case 128:
-      hipLaunchKernelGGL(hidden_project_kernel<128>, grid, dim3(256), 0, s, part, ns, NB, in_proj, B, xh);
-      break;
-    case 256:
-      hipLaunchKernelGGL(hidden_project_kernel<256>, grid, dim3(256), 0, s, part, ns, NB, in_proj, B, xh);
-      break;
+    case 64: return launch_project_r<64>(part, ns, NB, in_proj, N, B, xh, s);
+    case 128: return launch_project_r<128>(part, ns, NB, in_proj, N, B, xh, s);
+    case 256: return launch_project_r<256>(part, ns, NB, in_proj, N, B, xh, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace xpress
