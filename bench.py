@@ -9,8 +9,9 @@ step; the eager (kernel-by-kernel) rate is reported beside it, and both must giv
 Prints one JSON line. `value` is Jacobi passes per second of whole steps (per-step setup
 included). Also reported:
   * `roofline`: the readout kernel (the dominant kernel: the full-vocabulary MFMA readout, or the
-    gathered top-C readout when the workload has C > 0), algorithmic bytes per launch (w2 + base
-    + lat, or w2c + base_c + cand + lat) over its average duration measured with HIP events on
+    top-C readout when the workload has C > 0, reading w2[cand] through the ids as the step does),
+    algorithmic bytes per launch (w2 + base + lat, or the candidates' w2 rows + base_c + cand +
+    lat) over its average duration measured with HIP events on
     the launch stream, against the 8 TB/s HBM peak; its rate against the 2.5 PFLOP/s bf16 MFMA
     peak is in `extra`;
   * `extra.measured_peaks`: achievable yardsticks timed on the same GPU with library kernels
@@ -168,9 +169,8 @@ def main() -> int:
     if wl.C > 0:
         cand = torch.empty(rows, wl.C, dtype=torch.int64, device=dev)
         base_c = torch.empty(rows, wl.C, dtype=torch.bfloat16, device=dev)
-        w2c = torch.empty(rows, wl.C, wl.r, dtype=torch.bfloat16, device=dev)
-        xpress.topc_prepare(w, base, wl.N, wl.C, cand, base_c, w2c)
-        fn_readout = lambda: xpress.readout_argmax_topc(lat, w2c, base_c, cand, blk2)
+        xpress.topc_prepare(w, base, wl.N, wl.C, cand, base_c)  # no gathered copy: the step's form
+        fn_readout = lambda: xpress.readout_argmax_topc_ids(w, lat, base_c, cand, blk2)
         fn_reduce = None
         readout_pass = fn_readout
     else:
@@ -207,10 +207,10 @@ def main() -> int:
         del src, dst
 
     if wl.C > 0:
-        # gathered w2c rows + base_c + cand (int64) + lat, per launch
+        # the candidates' w2 rows (one per row and candidate) + base_c + cand (int64) + lat
         alg_bytes = rows * wl.C * (wl.r * 2 + 2 + 8) + rows * wl.r * 2
         kname = "topc_readout_kernel"
-        kdesc = "topc_readout_kernel (gathered GEMV + base_c add + argmax into blk)"
+        kdesc = "topc_readout_kernel (GEMV over w2[cand] + base_c add + argmax into blk)"
     else:
         alg_bytes = wl.V * wl.r * 2 + rows * wl.V * 2 + rows * wl.r * 2
         kname = "readout_partial_kernel"

@@ -176,8 +176,10 @@ xpress_status xpress_argmax_reduce(const uint32_t* part, int32_t ntiles, int32_t
 /* Top-C preparation, once per step (qwen3_xpress page, top-C branch of jacobi_refine_greedy):
  * cand[p] = the c = min(C, V) ids with the largest base[p, :] under the order (value descending,
  * id ascending), stored in ascending id order; base_c[p, k] = base[p, cand[p, k]];
- * w2c[p, k, :] = w2[cand[p, k], :].
- * cand: [N*(B-1), c] int64; base_c: [N*(B-1), c] bf16; w2c: [N*(B-1), c, r] bf16 (written).
+ * w2c[p, k, :] = w2[cand[p, k], :] (the gather is skipped when w2c is NULL, for callers of
+ * xpress_readout_argmax_topc_ids, which reads the rows from w2 through cand).
+ * cand: [N*(B-1), c] int64; base_c: [N*(B-1), c] bf16; w2c: [N*(B-1), c, r] bf16 (written;
+ * nullable, else 16-byte aligned).
  * ws (optional, may be NULL): device scratch; when it is 16-byte aligned and holds at least
  * N*(B-1) * 8*ceil(ceil(V/8)/8) * 2 bytes, the selection keeps per-chunk maxima there and its
  * second pass over base reads only the chunks that can hold an answer (same result, less
@@ -195,10 +197,20 @@ xpress_status xpress_readout_argmax_topc(const xpress_bf16* lat, const xpress_bf
                                          int32_t N, int32_t B, int32_t r, int32_t c,
                                          int64_t* blk, int32_t* changed, xpress_stream stream);
 
+/* The same top-C readout with the candidates' rows read from w->w2 through their ids (w2[cand[p,
+ * k]] in place of w2c[p, k]; same result): no gathered copy is needed. This is the form a draft
+ * step runs. Shapes and errors as in xpress_readout_argmax_topc; c in [1, w->V]; every
+ * cand[p, k] must be in [0, w->V) (as xpress_topc_prepare writes them; not checked). */
+xpress_status xpress_readout_argmax_topc_ids(const xpress_weights* w, const xpress_bf16* lat,
+                                             const xpress_bf16* base_c, const int64_t* cand,
+                                             int32_t N, int32_t c, int64_t* blk,
+                                             int32_t* changed, xpress_stream stream);
+
 /* One draft step (qwen3_xpress page, jacobi_refine_greedy): hidden cache, starting block (with
  * XPRESS_INIT_FROM_BASE; otherwise blk[:, 1:] is taken as given and blk[:, 0] is set to anchor),
- * top-C preparation when C > 0, then K passes of latent + readout + argmax. On return blk[:, 1:]
- * is the draft.
+ * top-C preparation when C > 0 (candidates and base_c; the passes read the candidates' w2 rows
+ * through their ids, as xpress_readout_argmax_topc_ids), then K passes of latent + readout +
+ * argmax. On return blk[:, 1:] is the draft.
  * h: [N, B, H]; base: [N*(B-1), V] stride base_ld; anchor, am1: [N]; blk: [N, B] in/out.
  * passes_run (nullable, device int32): number of passes that ran (with
  * XPRESS_STOP_AT_FIXED_POINT, the pass that changed nothing is counted). */

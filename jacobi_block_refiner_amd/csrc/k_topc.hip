@@ -3,10 +3,14 @@
 // Once per step (vLLM API page "vllm.model_executor.models.qwen3_xpress", top-C branch of
 // jacobi_refine_greedy): each draft row's candidate set is the c = min(C, V) ids with the largest
 // base logits, under the total order (value descending, id ascending), kept in ascending id
-// order; base_c and the readout rows w2c = w2[cand] are gathered once and reused by every pass.
+// order; base_c is gathered once and reused by every pass (and, for callers that want it, the
+// readout rows w2c = w2[cand]).
 // Per pass (vLLM API page "vllm.v1.worker.gpu.spec_decode.xpress.kernels",
-// _xpress_topc_argmax_to_blk_kernel): a gathered GEMV base_c + w2c . lat, its argmax (lowest
-// vocabulary id on ties) and the candidate -> vocabulary id -> blk write, in one kernel.
+// _xpress_topc_argmax_to_blk_kernel): the GEMV base_c + w2[cand] . lat, its argmax (lowest
+// vocabulary id on ties) and the candidate -> vocabulary id -> blk write, in one kernel. A step
+// reads the candidates' rows from w2 through their ids: no gathered copy (rows*c*r*2 bytes, 126
+// MB at 480 rows of 512 candidates) and no gather launch, and 10% faster top-512 steps than
+// reading the copy. The kernel also reads a caller's gathered w2c.
 //
 // Selection is a per-row radix select on the 16-bit order-preserving key of the bf16 value
 // (high byte histogram, then low byte histogram inside the boundary bin), followed by one ordered
@@ -602,22 +606,26 @@ __global__ __launch_bounds__(256) void topc_gather_kernel(const int64_t* __restr
   reinterpret_cast<uint4*>(w2c)[i] = reinterpret_cast<const uint4*>(w2)[id * rq + q];
 }
 
-// One workgroup per draft row. Lanes form groups of G = R/8 that each hold one candidate's w2c
-// row (16 bytes per lane, so a wave reads 1 KiB of contiguous rows per load); the group's
-// partial dot products are summed with xor shuffles. Each lane keeps U loads in flight per round
-// (the gathered rows stream once per pass: the kernel is bound by how many bytes are in flight).
-// The winner is tracked by candidate index -- cand is ascending, so the lowest index is the lowest
-// vocabulary id -- and translated to its id once at the end.
-template <int R>
+// One workgroup per draft row. Lanes form groups of G = R/8 that each hold one candidate's row
+// (16 bytes per lane, so a load reads whole 512-byte rows); the group's partial dot products are
+// summed with xor shuffles. Each lane keeps U loads in flight per round (the rows stream once
+// per pass: the kernel is bound by how many bytes are in flight). BY_ID: the rows are w2[cand[p,
+// k]] (table = w2 [V, r]), and each lane loads the ids of its next round's candidates one round
+// ahead; otherwise table = w2c [rows, c, r], the gathered copy. The winner is tracked by
+// candidate index -- cand is ascending, so the lowest index is the lowest vocabulary id -- and
+// translated to its id once at the end.
+template <int R, bool BY_ID>
 __global__ __launch_bounds__(256) void topc_readout_kernel(
     const uint16_t* __restrict__ lat, const float* __restrict__ shares, int nsh,
-    const uint16_t* __restrict__ w2c, const uint16_t* __restrict__ base_c,
+    const uint16_t* __restrict__ table, const uint16_t* __restrict__ base_c,
     const int64_t* __restrict__ cand, int B, int c, int64_t* __restrict__ blk, int32_t* changed,
     int32_t* flags, int pass) {
   if (pass_skipped(flags, pass)) return;
   constexpr int G = R / 8;        // lanes per candidate
   constexpr int CPW = 64 / G;     // candidates per wave per load
-  constexpr int U = 4;            // loads in flight per lane (2, 3, 6, 8 and 16 measured slower)
+  // loads in flight per lane: gathered rows 4 (2, 3, 6, 8 and 16 measured slower); rows through
+  // the ids 6 (4: 10% slower whole top-512 steps, 5 the same, 7 and 8 slower)
+  constexpr int U = BY_ID ? 6 : 4;
   constexpr int CPR = 4 * CPW * U;  // candidates per workgroup round
   __shared__ float s_v[4];
   __shared__ int s_i[4];
@@ -656,17 +664,28 @@ __global__ __launch_bounds__(256) void topc_readout_kernel(
     lv[0] = bf16_lo(u.x); lv[1] = bf16_hi(u.x); lv[2] = bf16_lo(u.y); lv[3] = bf16_hi(u.y);
     lv[4] = bf16_lo(u.z); lv[5] = bf16_hi(u.z); lv[6] = bf16_lo(u.w); lv[7] = bf16_hi(u.w);
   }
-  const uint4* wrow = reinterpret_cast<const uint4*>(w2c + (int64_t)p * c * R);
+  // BY_ID: the whole table, indexed by vocabulary id; otherwise this row's gathered rows
+  const uint4* wrow = reinterpret_cast<const uint4*>(table + (BY_ID ? 0 : (int64_t)p * c * R));
+  const int64_t* crow = cand + (int64_t)p * c;
   float bv = -INFINITY;
   int bk = INT_MAX;
+  int64_t idn[U];  // BY_ID: the ids of this lane's candidates in the coming round
+  if constexpr (BY_ID) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) idn[j] = crow[min((j * 4 + wave) * CPW + sub, c - 1)];
+  }
   for (int k0 = 0; k0 < c; k0 += CPR) {
     uint4 u[U];
     uint16_t bk16[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const int k = min(k0 + (j * 4 + wave) * CPW + sub, c - 1);  // past c: repeats, masked
-      u[j] = wrow[(int64_t)k * G + q];
+      u[j] = wrow[(BY_ID ? idn[j] : (int64_t)k) * G + q];
       bk16[j] = bc[k];
+    }
+    if constexpr (BY_ID) {  // the next round's ids (past c: clamped, unused)
+#pragma unroll
+      for (int j = 0; j < U; ++j) idn[j] = crow[min(k0 + CPR + (j * 4 + wave) * CPW + sub, c - 1)];
     }
 #pragma unroll
     for (int j = 0; j < U; ++j) {
@@ -697,7 +716,7 @@ __global__ __launch_bounds__(256) void topc_readout_kernel(
   __syncthreads();
   if (tid == 0) {
     for (int w = 1; w < 4; ++w) argmax_merge(bv, bk, s_v[w], s_i[w]);
-    const int64_t id = cand[(int64_t)p * c + bk];
+    const int64_t id = crow[bk];
     const int n = p / (B - 1), b = 1 + p % (B - 1);
     int64_t* slot = blk + (int64_t)n * B + b;
     if (*slot != id) {
@@ -748,26 +767,37 @@ hipError_t launch_topc_gather(const int64_t* cand, const uint16_t* w2, int rows,
   return hipGetLastError();
 }
 
-hipError_t launch_topc_readout(const uint16_t* lat, const float* shares, int nsh,
-                               const uint16_t* w2c, const uint16_t* base_c, const int64_t* cand,
-                               int rows, int B, int r, int c, int64_t* blk, int32_t* changed,
-                               int32_t* flags, int pass, hipStream_t s) {
+template <bool BY_ID>
+hipError_t launch_readout_t(const uint16_t* lat, const float* shares, int nsh,
+                            const uint16_t* table, const uint16_t* base_c, const int64_t* cand,
+                            int rows, int B, int r, int c, int64_t* blk, int32_t* changed,
+                            int32_t* flags, int pass, hipStream_t s) {
   switch (r) {
     case 64:
-      hipLaunchKernelGGL(topc_readout_kernel<64>, dim3(rows), dim3(256), 0, s, lat, shares, nsh,
-                         w2c, base_c, cand, B, c, blk, changed, flags, pass);
+      hipLaunchKernelGGL((topc_readout_kernel<64, BY_ID>), dim3(rows), dim3(256), 0, s, lat,
+                         shares, nsh, table, base_c, cand, B, c, blk, changed, flags, pass);
       break;
     case 128:
-      hipLaunchKernelGGL(topc_readout_kernel<128>, dim3(rows), dim3(256), 0, s, lat, shares, nsh,
-                         w2c, base_c, cand, B, c, blk, changed, flags, pass);
+      hipLaunchKernelGGL((topc_readout_kernel<128, BY_ID>), dim3(rows), dim3(256), 0, s, lat,
+                         shares, nsh, table, base_c, cand, B, c, blk, changed, flags, pass);
       break;
     case 256:
-      hipLaunchKernelGGL(topc_readout_kernel<256>, dim3(rows), dim3(256), 0, s, lat, shares, nsh,
-                         w2c, base_c, cand, B, c, blk, changed, flags, pass);
+      hipLaunchKernelGGL((topc_readout_kernel<256, BY_ID>), dim3(rows), dim3(256), 0, s, lat,
+                         shares, nsh, table, base_c, cand, B, c, blk, changed, flags, pass);
       break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_topc_readout(const uint16_t* lat, const float* shares, int nsh,
+                               const uint16_t* table, bool by_id, const uint16_t* base_c,
+                               const int64_t* cand, int rows, int B, int r, int c, int64_t* blk,
+                               int32_t* changed, int32_t* flags, int pass, hipStream_t s) {
+  return by_id ? launch_readout_t<true>(lat, shares, nsh, table, base_c, cand, rows, B, r, c, blk,
+                                        changed, flags, pass, s)
+               : launch_readout_t<false>(lat, shares, nsh, table, base_c, cand, rows, B, r, c,
+                                         blk, changed, flags, pass, s);
 }
 
 }  // namespace xpress

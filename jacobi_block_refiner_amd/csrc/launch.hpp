@@ -83,13 +83,15 @@ hipError_t launch_topc_start(const uint16_t* h, const uint16_t* down_h, const ui
                              hipStream_t s);
 hipError_t launch_topc_gather(const int64_t* cand, const uint16_t* w2, int rows, int c, int r,
                               uint16_t* w2c, hipStream_t s);
-// K7: top-C gathered GEMV + argmax + candidate -> vocabulary id -> blk. The latent rows come
-// from lat (bf16), or, with shares != nullptr, from the nsh slice shares the latent share kernel
-// leaves ([N, nsh, 16, r] fp32), summed as the latent sum kernel would (same bits).
+// K7: top-C GEMV + argmax + candidate -> vocabulary id -> blk. The candidates' rows are
+// table[cand[p, k]] with by_id (table = w2 [V, r]), else the gathered table[p, k] (table = w2c
+// [rows, c, r]). The latent rows come from lat (bf16), or, with shares != nullptr, from the nsh
+// slice shares the latent share kernel leaves ([N, nsh, 16, r] fp32), summed as the latent sum
+// kernel would (same bits).
 hipError_t launch_topc_readout(const uint16_t* lat, const float* shares, int nsh,
-                               const uint16_t* w2c, const uint16_t* base_c, const int64_t* cand,
-                               int rows, int B, int r, int c, int64_t* blk, int32_t* changed,
-                               int32_t* pass_flags, int pass, hipStream_t s);
+                               const uint16_t* table, bool by_id, const uint16_t* base_c,
+                               const int64_t* cand, int rows, int B, int r, int c, int64_t* blk,
+                               int32_t* changed, int32_t* pass_flags, int pass, hipStream_t s);
 // mix_L = bf16(raw * tril + I), per channel.
 hipError_t launch_fold_mixer(const uint16_t* raw, int r, int B, uint16_t* mix_L, hipStream_t s);
 // blk[n, 0] = anchor[n] (the step without the argmax start).

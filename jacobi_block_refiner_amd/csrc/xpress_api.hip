@@ -117,11 +117,9 @@ size_t latent_bytes(int N, int r, int M) {
 
 // Workspace regions of a call with N blocks.
 struct Layout {
-  size_t hdg = 0, xh = 0, lat = 0, lscr = 0, part = 0, flags = 0, cand = 0, base_c = 0, w2c = 0,
+  size_t hdg = 0, xh = 0, lat = 0, lscr = 0, part = 0, flags = 0, cand = 0, base_c = 0,
          cmax = 0, total = 0;
 };
-
-
 
 Layout step_layout(int N, int B, int r, int H, int64_t V, int C, int K) {
   Layout L;
@@ -143,7 +141,6 @@ Layout step_layout(int N, int B, int r, int H, int64_t V, int C, int K) {
   L.flags = take((size_t)(K + 1) * sizeof(int32_t));
   L.cand = take(rows * c * sizeof(int64_t));
   L.base_c = take(rows * c * 2);
-  L.w2c = take(rows * c * r * 2);
   L.cmax = take(C > 0 ? xpress::topc_select_scratch_bytes((int)rows, V) : 0);
   L.total = off;
   return L;
@@ -351,7 +348,8 @@ xpress_status xpress_topc_prepare(const xpress_weights* w, const xpress_bf16* ba
   if (st != XPRESS_OK) return st;
   XP_PTR(cand);
   XP_PTR(base_c);
-  XP_PTR(w2c);
+  if (w2c != nullptr && (reinterpret_cast<uintptr_t>(w2c) & 15) != 0)
+    return fail(XPRESS_ERR_ARG, "w2c is not 16-byte aligned");
   const int c = (int)(C < w->V ? C : w->V);
   const int rows = N * (w->B - 1);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -361,7 +359,8 @@ xpress_status xpress_topc_prepare(const xpress_weights* w, const xpress_bf16* ba
   XP_TRY(xpress::launch_topc_select(base, base_ld, rows, w->V, c, cand, base_c, nullptr, nullptr, 0,
                                     ws_ok ? static_cast<uint16_t*>(ws) : nullptr, s),
          "top-C select");
-  XP_TRY(xpress::launch_topc_gather(cand, w->w2, rows, c, w->r, w2c, s), "top-C gather");
+  if (w2c != nullptr)
+    XP_TRY(xpress::launch_topc_gather(cand, w->w2, rows, c, w->r, w2c, s), "top-C gather");
   return XPRESS_OK;
 }
 
@@ -377,8 +376,28 @@ xpress_status xpress_readout_argmax_topc(const xpress_bf16* lat, const xpress_bf
   XP_PTR(w2c);
   if (base_c == nullptr || cand == nullptr || blk == nullptr)
     return fail(XPRESS_ERR_ARG, "base_c, cand or blk is NULL");
-  XP_TRY(xpress::launch_topc_readout(lat, nullptr, 0, w2c, base_c, cand, N * (B - 1), B, r, c, blk,
-                                     changed, nullptr, 0, reinterpret_cast<hipStream_t>(stream)),
+  XP_TRY(xpress::launch_topc_readout(lat, nullptr, 0, w2c, false, base_c, cand, N * (B - 1), B, r,
+                                     c, blk, changed, nullptr, 0,
+                                     reinterpret_cast<hipStream_t>(stream)),
+         "top-C readout");
+  return XPRESS_OK;
+}
+
+xpress_status xpress_readout_argmax_topc_ids(const xpress_weights* w, const xpress_bf16* lat,
+                                             const xpress_bf16* base_c, const int64_t* cand,
+                                             int32_t N, int32_t c, int64_t* blk, int32_t* changed,
+                                             xpress_stream stream) {
+  xpress_status st = check_weights(w, false, false, true);
+  if (st != XPRESS_OK) return st;
+  if (N < 0 || c < 1 || c > w->V)
+    return fail(XPRESS_ERR_ARG, "N=%d < 0 or c=%d outside [1, V=%lld]", N, c, (long long)w->V);
+  if (N == 0) return XPRESS_OK;
+  XP_PTR(lat);
+  if (base_c == nullptr || cand == nullptr || blk == nullptr)
+    return fail(XPRESS_ERR_ARG, "base_c, cand or blk is NULL");
+  XP_TRY(xpress::launch_topc_readout(lat, nullptr, 0, w->w2, true, base_c, cand, N * (w->B - 1),
+                                     w->B, w->r, c, blk, changed, nullptr, 0,
+                                     reinterpret_cast<hipStream_t>(stream)),
          "top-C readout");
   return XPRESS_OK;
 }
@@ -418,7 +437,6 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
   // row's argmax; the anchor too); without, one launch computes it beside the hidden GEMM
   int64_t* cand = at<int64_t>(ws, L.cand);
   xpress_bf16* base_c = at<xpress_bf16>(ws, L.base_c);
-  xpress_bf16* w2c = at<xpress_bf16>(ws, L.w2c);
   if (c > 0)  // the hidden GEMM beside the selection (which also writes the starting block)
     XP_TRY(xpress::launch_topc_start(h, w->down_h, w->down_g, N * B, w->H, r, hdg, base, base_ld,
                                      rows, V, c, cand, base_c, anchor, init ? blk : nullptr, B,
@@ -432,7 +450,6 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
     XP_TRY(xpress::launch_hidden_gemm(h, w->down_h, w->down_g, N * B, w->H, r, hdg, s), "hidden gemm");
   XP_TRY(xpress::launch_hidden_project(hdg, w->H, w->in_proj, N, B, r, xh, s), "hidden project");
   if (!init) XP_TRY(xpress::launch_set_anchor(anchor, N, B, blk, s), "set anchor");
-  if (c > 0) XP_TRY(xpress::launch_topc_gather(cand, w->w2, rows, c, r, w2c, s), "top-C gather");
   const bool stop = (flags & XPRESS_STOP_AT_FIXED_POINT) != 0;
   const bool fused = use_table(w, N);
   int32_t* pf = stop ? at<int32_t>(ws, L.flags) : nullptr;
@@ -456,7 +473,7 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
              "latent");
     if (c > 0) {
       XP_TRY(xpress::launch_topc_readout(lat, fused ? static_cast<const float*>(lscr) : nullptr,
-                                         w->M / 64, w2c, base_c, cand, rows, B, r, c, blk,
+                                         w->M / 64, w->w2, true, base_c, cand, rows, B, r, c, blk,
                                          nullptr, pf, p, s),
              "top-C readout");
     } else {

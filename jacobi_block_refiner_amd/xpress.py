@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
             "xpress_argmax_reduce": [P, i32, i32, i32, P, P, P],
             "xpress_topc_prepare": [W, P, i64, i32, i32, P, P, P, P, sz, P],
             "xpress_readout_argmax_topc": [P, P, P, P, i32, i32, i32, i32, P, P, P],
+            "xpress_readout_argmax_topc_ids": [W, P, P, P, i32, i32, P, P, P],
             "xpress_jacobi_step": [W, P, P, i64, P, P, i32, i32, i32, ctypes.c_uint32, P, P, P,
                                    sz, P],
             "xpress_jacobi_step_graph": [W, P, P, i64, P, P, i32, i32, i32, ctypes.c_uint32, P, P,
@@ -247,7 +248,8 @@ def argmax_reduce(part: torch.Tensor, blk: torch.Tensor, changed=None) -> torch.
     return blk
 
 
-def topc_prepare(w: Weights, base, N: int, C: int, cand, base_c, w2c, ws=None):
+def topc_prepare(w: Weights, base, N: int, C: int, cand, base_c, w2c=None, ws=None):
+    """w2c None: candidates and base_c only (for readout_argmax_topc_ids)."""
     s = w.struct()
     _bf16(base, "base")
     assert base.stride(1) == 1
@@ -263,6 +265,17 @@ def readout_argmax_topc(lat, w2c, base_c, cand, blk, changed=None) -> torch.Tens
     rows, c, r = w2c.shape
     _check(lib().xpress_readout_argmax_topc(_ptr(lat), _ptr(w2c), _ptr(base_c), _ptr(cand), N, B,
                                             r, c, _ptr(blk), _ptr(changed), _stream()))
+    return blk
+
+
+def readout_argmax_topc_ids(w: Weights, lat, base_c, cand, blk, changed=None) -> torch.Tensor:
+    """The top-C readout reading w2[cand] through the ids (no gathered copy)."""
+    s = w.struct()
+    N = blk.shape[0]
+    c = cand.shape[-1]
+    _check(lib().xpress_readout_argmax_topc_ids(ctypes.byref(s), _ptr(lat), _ptr(base_c),
+                                                _ptr(cand), N, c, _ptr(blk), _ptr(changed),
+                                                _stream()))
     return blk
 
 

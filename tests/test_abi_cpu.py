@@ -25,8 +25,10 @@ def test_workspace_size_grows_with_blocks_and_candidates():
     b = xpress.workspace_size(256, 16, 256, 151936, 0, 15)
     c = xpress.workspace_size(32, 16, 256, 151936, 512, 15)
     assert 0 < a < b
-    # top-C holds w2c [rows, C, r] bf16 = 125.8 MB at 32 blocks of 15 draft rows
-    assert c >= 480 * 512 * 256 * 2
+    # top-C adds cand (int64) + base_c (bf16) per candidate and the selection's chunk maxima; the
+    # passes read w2 through the ids, so no gathered [rows, C, r] copy (125.8 MB here)
+    assert c >= a + 480 * 512 * (8 + 2)
+    assert c < a + 480 * 512 * 256 * 2
 
 
 @pytest.mark.parametrize("B,r,V", [(1, 256, 1000), (17, 256, 1000), (16, 96, 1000),
@@ -128,3 +130,21 @@ def test_readout_range_count_rejects_bad_arguments():
     assert L.xpress_readout_tiles(151936, 0, ctypes.byref(out)) == xpress.ERR_ARG
     assert L.xpress_readout_tiles(0, 15, ctypes.byref(out)) == xpress.ERR_ARG
     assert L.xpress_readout_tiles(151936, 15, None) == xpress.ERR_ARG
+
+
+def test_topc_ids_readout_arguments_are_checked():
+    L = xpress.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    w = xpress._Weights(B=16, r=256, H=4096, M=512, V=151936, w2=fake)
+    assert L.xpress_readout_argmax_topc_ids(None, fake, fake, fake, 4, 512, fake, None,
+                                            None) == xpress.ERR_ARG
+    assert L.xpress_readout_argmax_topc_ids(ctypes.byref(w), fake, fake, fake, 4, 151937, fake,
+                                            None, None) == xpress.ERR_ARG
+    assert L.xpress_readout_argmax_topc_ids(ctypes.byref(w), fake, None, fake, 4, 512, fake, None,
+                                            None) == xpress.ERR_ARG
+    assert L.xpress_readout_argmax_topc_ids(ctypes.byref(w), fake, fake, fake, 0, 512, fake, None,
+                                            None) == xpress.OK
+    misaligned = ctypes.c_void_p((1 << 20) + 2)
+    st = L.xpress_topc_prepare(ctypes.byref(w), fake, 151936, 4, 512, fake, fake, misaligned,
+                               None, 0, None)
+    assert st == xpress.ERR_ARG and b"w2c" in L.xpress_last_error()

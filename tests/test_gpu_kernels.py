@@ -480,19 +480,27 @@ def test_topc_prepare_adversarial_rows(C, V, chunk_maxima):
     assert np.array_equal(base_c.float().cpu().numpy(), np.take_along_axis(base, want, axis=1))
 
 
-def test_topc_readout_dyadic_exact_and_membership():
+# gathered: rows from w2c; ids: rows from w2 through cand (the step's form; topc_prepare then
+# skips the gather). C = 96 and 100 at r = 256: whole and ragged last rounds of both forms.
+@pytest.mark.parametrize("form", ["gathered", "ids"])
+@pytest.mark.parametrize("r,C", [(256, 96), (256, 100), (128, 300), (64, 37)])
+def test_topc_readout_dyadic_exact_and_membership(form, r, C):
     rng = np.random.default_rng(7)
-    N, B, r, V, C = 4, 16, 256, 6000, 96
+    N, B, V = 4, 16, 6000
     lat, w2, base = _readout_case(8, N, B, r, V)
     w = _weights_with(w2, r, B, V)
     rows = N * (B - 1)
     cand = torch.empty(rows, C, dtype=torch.int64, device="cuda")
     base_c = torch.empty(rows, C, dtype=torch.bfloat16, device="cuda")
-    w2c = torch.empty(rows, C, r, dtype=torch.bfloat16, device="cuda")
+    w2c = torch.empty(rows, C, r, dtype=torch.bfloat16, device="cuda") if form == "gathered" else None
     xpress.topc_prepare(w, upload.base_logits(base), N, C, cand, base_c, w2c)
     blk0 = rng.integers(0, V, (N, B))
     blk = upload.tokens(blk0)
-    xpress.readout_argmax_topc(upload.bf16_tensor(lat), w2c, base_c, cand, blk)
+    log(f"top-C readout {form} r={r} C={C}")
+    if form == "gathered":
+        xpress.readout_argmax_topc(upload.bf16_tensor(lat), w2c, base_c, cand, blk)
+    else:
+        xpress.readout_argmax_topc_ids(w, upload.bf16_tensor(lat), base_c, cand, blk)
     torch.cuda.synchronize()
     cand_o = O.topc_select(base, C)
     best, gap, _ = O.readout_argmax(lat, w2, base, cand=cand_o)
