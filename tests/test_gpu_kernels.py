@@ -561,3 +561,38 @@ def test_topc_step_matches_oracle(path, M):
         assert int(passes.item()) == n_pass
     for p, tok in enumerate(draft_rows(got)):
         assert tok in cand[p]
+
+
+# B = 2: one draft slot per block (slot 1 reads the anchor; rows = N); B = 16 at r = 128 with a
+# ragged V, K > B; each with and without candidates, on both latent paths
+@pytest.mark.parametrize("path", ["table", "project"])
+@pytest.mark.parametrize("B,r,V,N,C", [(2, 64, 1001, 5, 0), (2, 64, 1001, 5, 7),
+                                       (16, 128, 3001, 3, 0), (16, 128, 3001, 3, 100)])
+def test_step_edge_shapes(B, r, V, N, C, path):
+    inp = strong(synth.make_inputs(replace(synth.WORKLOADS[1], B=B, r=r, V=V), N=N, seed=9))
+    wl = inp.wl
+    K = 2 * B + 1
+    d = _dev(inp, path)
+    blk = upload.tokens(inp.blk)
+    passes = torch.zeros(1, dtype=torch.int32, device="cuda")
+    log(f"step edge shape B={B} r={r} V={V} N={N} C={C} {path}")
+    xpress.jacobi_step(d.w, d.h, d.base, d.anchor, d.am1, blk, K=K, C=C,
+                       flags=xpress.INIT_FROM_BASE | xpress.STOP_AT_FIXED_POINT,
+                       ws=xpress.alloc_workspace(N, B, r, V, C, K), passes_run=passes)
+    torch.cuda.synchronize()
+    L = oracle_mixer(inp)
+    xh = O.hidden_cache(inp.h, inp.down_h, inp.down_g, inp.in_proj)
+    cand = O.topc_select(inp.base, C) if C else None
+    start = O.initial_block(inp.base, inp.anchor, N, B)
+    want, n_pass, _, hg = O.jacobi(inp, L, xh, start, K=K, stop_at_fixed_point=True, cand=cand,
+                                   history=True)
+    got = blk.cpu().numpy()
+    bad, exempt = end_to_end_ok(got, want, hg)
+    log(f"  passes gpu {int(passes.item())} oracle {n_pass}, exempt rows {exempt}")
+    assert bad == 0
+    assert np.array_equal(got[:, 0], inp.anchor)
+    if exempt == 0:
+        assert np.array_equal(got, want)
+        assert int(passes.item()) == n_pass
+    if C:
+        assert all(got[n, b] in cand[n * (B - 1) + b - 1] for n in range(N) for b in range(1, B))
