@@ -148,3 +148,13 @@ def test_topc_ids_readout_arguments_are_checked():
     st = L.xpress_topc_prepare(ctypes.byref(w), fake, 151936, 4, 512, fake, fake, misaligned,
                                None, 0, None)
     assert st == xpress.ERR_ARG and b"w2c" in L.xpress_last_error()
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: without the built library every entry point raises."""
+    monkeypatch.setattr(xpress, "LIB_PATH", tmp_path / "libxpress.so")
+    monkeypatch.setattr(xpress, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        xpress.readout_tiles(151936, 480)
+    with pytest.raises(RuntimeError, match="missing"):
+        xpress.lib()
