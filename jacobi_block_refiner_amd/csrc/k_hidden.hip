@@ -29,13 +29,17 @@ __global__ __launch_bounds__(256) void hidden_gemm_kernel(const uint16_t* __rest
 
 // The start of a step in one launch: workgroups [0, g1) are the hidden GEMM's tiles (mt x nt
 // tiles per split, split-major), the rest the starting block's rows. The two are independent; the
-// GEMM is latency-bound and the starting block bandwidth-bound, so they overlap well.
+// GEMM is latency-bound and the starting block bandwidth-bound, so they overlap well. With
+// zero_flags, workgroup 0 also clears the step's nzero pass flags (read only by later launches).
 __global__ __launch_bounds__(256) void step_start_kernel(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ down_h,
     const uint16_t* __restrict__ down_g, int NB, int H, int r, int kslice,
     float* __restrict__ part, int g1, int mt, int nt, const uint16_t* __restrict__ base,
-    int64_t ld, const int64_t* __restrict__ anchor, int B, int64_t V, int64_t* __restrict__ blk) {
+    int64_t ld, const int64_t* __restrict__ anchor, int B, int64_t V, int64_t* __restrict__ blk,
+    int32_t* __restrict__ zero_flags, int nzero) {
   const int i = blockIdx.x;
+  if (zero_flags && i == 0)
+    for (int q = threadIdx.x; q < nzero; q += blockDim.x) zero_flags[q] = 0;
   if (i < g1)
     hidden_gemm_tile(h, down_h, down_g, NB, H, r, kslice, part, i % mt, (i / mt) % nt, i / (mt * nt));
   else
@@ -195,14 +199,14 @@ hipError_t launch_hidden_gemm(const uint16_t* h, const uint16_t* down_h, const u
 hipError_t launch_step_start(const uint16_t* h, const uint16_t* down_h, const uint16_t* down_g,
                              int NB, int H, int r, float* part, const uint16_t* base, int64_t ld,
                              const int64_t* anchor, int N, int B, int64_t V, int64_t* blk,
-                             hipStream_t s) {
+                             hipStream_t s, int32_t* zero_flags, int nzero) {
   const int ns = hidden_splits(NB, H, r);
   const int kslice = hidden_chunks_per_split(NB, H, r) * kTK;
   const int mt = (NB + kTM - 1) / kTM, nt = (2 * r) / kTN;
   const int g1 = mt * nt * ns;
   hipLaunchKernelGGL(step_start_kernel, dim3((unsigned)(g1 + N * (B - 1))), dim3(256), 0, s, h,
                      down_h, down_g, NB, H, r, kslice, part, g1, mt, nt, base, ld, anchor, B, V,
-                     blk);
+                     blk, zero_flags, nzero);
   return hipGetLastError();
 }
 

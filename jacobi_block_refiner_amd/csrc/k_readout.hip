@@ -373,11 +373,22 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
 // Partials of 64 consecutive rows per workgroup: thread (row lr, slice j) scans ranges j, j+4, ...
 // (each wave reads 64 consecutive rows of one range: 512 contiguous bytes), the four slice
 // winners of a row are merged in LDS, and the row's winner is written into blk in place.
+// With passes_run (the last pass of a step, pass = K-1): workgroup 0 also writes the number of
+// passes that ran, which flags[0 .. K-2] already fix (pass p >= 1 ran iff pass p-1 changed a
+// slot), so the step needs no launch of its own for it.
 __global__ __launch_bounds__(256) void argmax_reduce_kernel(const uint2* __restrict__ part,
                                                             int ntiles, int rows, int B,
                                                             int64_t* __restrict__ blk,
                                                             int32_t* changed, int32_t* flags,
-                                                            int pass) {
+                                                            int pass, int32_t* passes_run) {
+  if (passes_run && blockIdx.x == 0 && threadIdx.x == 0) {
+    int n = pass + 1;
+    if (flags) {
+      n = 1;
+      for (int q = 0; q < pass; ++q) n += flags[q] != 0;
+    }
+    *passes_run = n;
+  }
   if (pass_skipped(flags, pass)) return;
   __shared__ float s_v[4][64];
   __shared__ int s_i[4][64];
@@ -473,9 +484,10 @@ hipError_t launch_readout_partial(const uint16_t* lat, const uint16_t* w2, const
 }
 
 hipError_t launch_argmax_reduce(const uint2* part, int ntiles, int rows, int B, int64_t* blk,
-                                int32_t* changed, int32_t* flags, int pass, hipStream_t s) {
+                                int32_t* changed, int32_t* flags, int pass, hipStream_t s,
+                                int32_t* passes_run) {
   hipLaunchKernelGGL(argmax_reduce_kernel, dim3((rows + 63) / 64), dim3(256), 0, s, part, ntiles,
-                     rows, B, blk, changed, flags, pass);
+                     rows, B, blk, changed, flags, pass, passes_run);
   return hipGetLastError();
 }
 

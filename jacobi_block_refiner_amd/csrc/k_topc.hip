@@ -586,8 +586,10 @@ __global__ __launch_bounds__(256) void topc_start_kernel(
     float* __restrict__ part, int g1, int mt, int nt, const uint16_t* __restrict__ base,
     int64_t ld, int64_t V, int c, int64_t* __restrict__ cand, uint16_t* __restrict__ base_c,
     const int64_t* __restrict__ anchor, int64_t* __restrict__ blk, int B,
-    uint16_t* __restrict__ cmax) {
+    uint16_t* __restrict__ cmax, int32_t* __restrict__ zero_flags, int nzero) {
   const int i = blockIdx.x;
+  if (zero_flags && i == 0)  // the step's pass flags (read only by later launches)
+    for (int q = threadIdx.x; q < nzero; q += blockDim.x) zero_flags[q] = 0;
   if (i < g1)
     hidden_gemm_tile(h, down_h, down_g, NB, H, r, kslice, part, i % mt, (i / mt) % nt, i / (mt * nt));
   else
@@ -741,14 +743,14 @@ hipError_t launch_topc_start(const uint16_t* h, const uint16_t* down_h, const ui
                              int NB, int H, int r, float* part, const uint16_t* base, int64_t ld,
                              int rows, int64_t V, int c, int64_t* cand, uint16_t* base_c,
                              const int64_t* anchor, int64_t* blk, int B, uint16_t* cmax,
-                             hipStream_t s) {
+                             hipStream_t s, int32_t* zero_flags, int nzero) {
   const int ns = hidden_splits(NB, H, r);
   const int kslice = hidden_chunks_per_split(NB, H, r) * kTK;
   const int mt = (NB + kTM - 1) / kTM, nt = (2 * r) / kTN;
   const int g1 = mt * nt * ns;
   hipLaunchKernelGGL(topc_start_kernel, dim3((unsigned)(g1 + rows)), dim3(256), 0, s, h, down_h,
                      down_g, NB, H, r, kslice, part, g1, mt, nt, base, ld, V, c, cand, base_c,
-                     anchor, blk, B, cmax);
+                     anchor, blk, B, cmax, zero_flags, nzero);
   return hipGetLastError();
 }
 

@@ -24,10 +24,11 @@ hipError_t launch_hidden_gemm(const uint16_t* h, const uint16_t* down_h, const u
 // xh[n, b] = in_proj[:, :r] . hdg[n, b, :r] + in_proj[:, r:2r] . mean_b hdg[n, b, r:]; `part` is
 // the scratch of launch_hidden_gemm (hidden_scratch_bytes long).
 // K1a + K2 in one launch (independent): the hidden GEMM's tiles and the starting block's rows.
+// With zero_flags (nullable) it also clears the step's nzero pass flags.
 hipError_t launch_step_start(const uint16_t* h, const uint16_t* down_h, const uint16_t* down_g,
                              int NB, int H, int r, float* part, const uint16_t* base, int64_t ld,
                              const int64_t* anchor, int N, int B, int64_t V, int64_t* blk,
-                             hipStream_t s);
+                             hipStream_t s, int32_t* zero_flags = nullptr, int nzero = 0);
 hipError_t launch_hidden_project(const float* part, int H, const uint16_t* in_proj, int N, int B,
                                  int r, float* xh, hipStream_t s);
 // K2: blk[n, 0] = anchor[n]; blk[n, b] = argmax_v base[n*(B-1)+b-1, v].
@@ -62,8 +63,11 @@ hipError_t launch_readout_partial(const uint16_t* lat, const uint16_t* w2, const
                                   int64_t ld, int rows, int64_t V, int r, uint2* part,
                                   const int32_t* flags, int pass, hipStream_t s);
 // K6: per-row reduce of the partials into blk[n, 1 + p % (B-1)].
+// With passes_run (nullable; the last pass of a step, pass = K-1), also writes the number of
+// passes that ran, as launch_count_passes would.
 hipError_t launch_argmax_reduce(const uint2* part, int ntiles, int rows, int B, int64_t* blk,
-                                int32_t* changed, int32_t* pass_flags, int pass, hipStream_t s);
+                                int32_t* changed, int32_t* pass_flags, int pass, hipStream_t s,
+                                int32_t* passes_run = nullptr);
 // K3: top-C candidate selection (+ base_c) and the w2 gather. With blk non-null the selection
 // also writes the starting block: each row's best candidate into blk[n, 1 + p % (B-1)] and the
 // anchor into blk[n, 0].
@@ -80,7 +84,7 @@ hipError_t launch_topc_start(const uint16_t* h, const uint16_t* down_h, const ui
                              int NB, int H, int r, float* part, const uint16_t* base, int64_t ld,
                              int rows, int64_t V, int c, int64_t* cand, uint16_t* base_c,
                              const int64_t* anchor, int64_t* blk, int B, uint16_t* cmax,
-                             hipStream_t s);
+                             hipStream_t s, int32_t* zero_flags = nullptr, int nzero = 0);
 hipError_t launch_topc_gather(const int64_t* cand, const uint16_t* w2, int rows, int c, int r,
                               uint16_t* w2c, hipStream_t s);
 // K7: top-C GEMV + argmax + candidate -> vocabulary id -> blk. The candidates' rows are

@@ -437,23 +437,24 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
   // row's argmax; the anchor too); without, one launch computes it beside the hidden GEMM
   int64_t* cand = at<int64_t>(ws, L.cand);
   xpress_bf16* base_c = at<xpress_bf16>(ws, L.base_c);
+  // per-pass change flags of the device-side early exit, cleared by the step's first launch
+  const bool stop = (flags & XPRESS_STOP_AT_FIXED_POINT) != 0;
+  int32_t* pf = stop ? at<int32_t>(ws, L.flags) : nullptr;
   if (c > 0)  // the hidden GEMM beside the selection (which also writes the starting block)
     XP_TRY(xpress::launch_topc_start(h, w->down_h, w->down_g, N * B, w->H, r, hdg, base, base_ld,
                                      rows, V, c, cand, base_c, anchor, init ? blk : nullptr, B,
-                                     at<uint16_t>(ws, L.cmax), s),
+                                     at<uint16_t>(ws, L.cmax), s, pf, K + 1),
            "hidden gemm + top-C select");
   else if (init)
     XP_TRY(xpress::launch_step_start(h, w->down_h, w->down_g, N * B, w->H, r, hdg, base, base_ld,
-                                     anchor, N, B, V, blk, s),
+                                     anchor, N, B, V, blk, s, pf, K + 1),
            "hidden gemm + starting block");
   else
     XP_TRY(xpress::launch_hidden_gemm(h, w->down_h, w->down_g, N * B, w->H, r, hdg, s), "hidden gemm");
   XP_TRY(xpress::launch_hidden_project(hdg, w->H, w->in_proj, N, B, r, xh, s), "hidden project");
   if (!init) XP_TRY(xpress::launch_set_anchor(anchor, N, B, blk, s), "set anchor");
-  const bool stop = (flags & XPRESS_STOP_AT_FIXED_POINT) != 0;
   const bool fused = use_table(w, N);
-  int32_t* pf = stop ? at<int32_t>(ws, L.flags) : nullptr;
-  if (stop) XP_TRY(xpress::launch_flags_reset(pf, K + 1, s), "flags reset");
+  if (stop && c == 0 && !init) XP_TRY(xpress::launch_flags_reset(pf, K + 1, s), "flags reset");
   uint2* part = at<uint2>(ws, L.part);
   const int ntiles = xpress::readout_tiles(V, rows);
   // Full vocabulary: the argmax reduce of pass p-1 runs inside pass p's first latent kernel (each
@@ -481,10 +482,14 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
              "readout");
     }
   }
-  if (c == 0 && K > 0)
-    XP_TRY(xpress::launch_argmax_reduce(part, ntiles, rows, B, blk, nullptr, pf, K - 1, s),
+  // the last pass's reduce also writes the pass count; otherwise a launch of its own does
+  const bool last_reduce = c == 0 && K > 0;
+  if (last_reduce)
+    XP_TRY(xpress::launch_argmax_reduce(part, ntiles, rows, B, blk, nullptr, pf, K - 1, s,
+                                        passes_run),
            "argmax reduce");
-  if (passes_run) XP_TRY(xpress::launch_count_passes(pf, K, stop ? 1 : 0, passes_run, s), "count passes");
+  if (passes_run && !last_reduce)
+    XP_TRY(xpress::launch_count_passes(pf, K, stop ? 1 : 0, passes_run, s), "count passes");
   return XPRESS_OK;
 }
 
