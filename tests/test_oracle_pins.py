@@ -108,6 +108,31 @@ def test_hidden_cache_is_linear_in_the_two_projections_and_ignores_the_embedding
     assert np.array_equal(full, O.hidden_cache(inp.h, inp.down_h, inp.down_g, other))
 
 
+def test_hidden_cache_with_general_projection_blocks_matches_float64_matmuls():
+    """Random, non-symmetric hidden blocks of in_proj: xh = (h . down_h^T) . P1^T +
+    (mean_b h . down_g^T) . P2^T, computed here with float64 NumPy matmuls. The identity blocks of
+    the tests above cannot tell P1 from its transpose; these can (qwen3_xpress, hidden_cache and
+    the transposed hidden half of in_proj that process_weights_after_loading prepares)."""
+    inp = _inp(N=3)
+    r = inp.in_proj.shape[0]
+    rng = np.random.default_rng(11)
+    P1 = rng.standard_normal((r, r)).astype(np.float32)
+    P2 = rng.standard_normal((r, r)).astype(np.float32)
+    P1[np.triu_indices(r, 1)] *= 3.0  # make the blocks visibly non-symmetric
+    P2[np.tril_indices(r, -1)] *= -2.0
+    assert not np.allclose(P1, P1.T) and not np.allclose(P2, P2.T)
+    P = _with_inproj(inp, P1, P2, pe=rng.standard_normal((r, r)).astype(np.float32))
+    xh = O.hidden_cache(inp.h, inp.down_h, inp.down_g, P)
+    h = inp.h.astype(np.float64)
+    hd = np.matmul(h, inp.down_h.astype(np.float64).T)                 # [N, B, r]
+    hg = np.matmul(np.mean(h, axis=1), inp.down_g.astype(np.float64).T)  # [N, r]
+    want = np.matmul(hd, P1.astype(np.float64).T) + np.matmul(hg, P2.astype(np.float64).T)[:, None, :]
+    np.testing.assert_allclose(xh, want, rtol=1e-10, atol=1e-12)
+    # the transposed reading of either block is far off
+    wrong = np.matmul(hd, P1.astype(np.float64)) + np.matmul(hg, P2.astype(np.float64))[:, None, :]
+    assert np.max(np.abs(xh - wrong)) > 1e-3 * np.max(np.abs(want))
+
+
 # ----------------------------------------------------------------------------------------------
 # Latent (qwen3_xpress, _refine_latent; kernels page, _xpress_latent_kernel docstring)
 
@@ -361,6 +386,35 @@ def test_initial_block_is_anchor_then_base_argmax():
     assert np.array_equal(blk[:, 0], inp.anchor)
     want = np.argmax(inp.base, axis=1).reshape(3, 4)
     assert np.array_equal(blk[:, 1:], want)
+
+
+def test_initial_block_ties_go_to_the_lowest_id():
+    """Rows with planted duplicate maxima (before and after the first occurrence, at both ends of
+    the vocabulary), and -0/+0 as the maximum: the starting block is NumPy's argmax, the first
+    maximum (qwen3_xpress, jacobi_refine_greedy starts from the base logits' argmax)."""
+    inp = _inp(N=3, B=5)
+    base = inp.base.copy()
+    V = base.shape[1]
+    rng = np.random.default_rng(4)
+    plants = [(0, [17, 5000]), (1, [V - 1, 3]), (2, [0, V - 1]), (3, [700, 701, 702]),
+              (4, [8000, 12, 4096]), (5, [6, 2, 8191])]
+    for row, ids in plants:
+        base[row, ids] = base[row].max() + 1.5
+    base[6] = -1.0
+    base[6, 900] = -0.0
+    base[6, 40] = 0.0   # +0 after -0 in value order; the lower id (40) must win
+    base[7] = -3.0
+    base[7, [3000, 9, 6000]] = 0.0
+    base[7, 9] = -0.0
+    for row in range(8, 12):
+        k = int(rng.integers(2, 6))
+        ids = rng.choice(V, size=k, replace=False)
+        base[row, ids] = base[row].max() + 0.25
+    blk = O.initial_block(base, inp.anchor, 3, 5)
+    want = np.argmax(base, axis=1).reshape(3, 4)
+    assert np.array_equal(blk[:, 1:], want)
+    assert want.reshape(-1)[0] == 17 and want.reshape(-1)[1] == 3 and want.reshape(-1)[2] == 0
+    assert want.reshape(-1)[6] == 40 and want.reshape(-1)[7] == 9
 
 
 def _prep(inp):
