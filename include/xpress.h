@@ -30,10 +30,18 @@
  *     a non-zero status and xpress_last_error() describes it. XPRESS_ERR_HIP reports a launch
  *     failure from the HIP runtime.
  *   - N == 0 is a no-op that returns XPRESS_OK.
- *   - Supported shapes on the GPU path: r in {64, 128, 256}; 2 <= B <= 16; M a multiple of 64
- *     (64..1024); H a multiple of 64; V >= 1 and V*r < 2^31; all pointers 16-byte aligned and
- *     base_ld a multiple of 8 elements. Inputs must be finite; results for NaN/Inf inputs are
- *     unspecified.
+ *   - Supported shapes on the GPU path: r in {64, 128, 256}; 2 <= B <= 16; M in
+ *     {64, 128, 256, 512, 1024}; H a multiple of 64 in [64, 16384]; V >= 1 and V*r < 2^31; all
+ *     pointers 16-byte aligned and base_ld a multiple of 8 elements. Other values are
+ *     XPRESS_ERR_ARG.
+ *   - Capacity: a workspace sized by xpress_workspace_size(n_max, ...) serves every N <= n_max;
+ *     a call whose N needs more than ws_bytes (N beyond the n_max the workspace was sized for,
+ *     among other cases) returns XPRESS_ERR_WORKSPACE before enqueueing anything. That one
+ *     status covers both the capacity and the size check, since the size in bytes is what
+ *     records n_max.
+ *   - Inputs should be finite. For -inf/NaN values the chosen tokens are unspecified (except
+ *     that -inf orders below every finite value and ties like any other value), but every id
+ *     written is in [0, V) (for top-C: one of the row's candidates).
  */
 #ifndef XPRESS_H
 #define XPRESS_H
@@ -191,7 +199,9 @@ xpress_status xpress_topc_prepare(const xpress_weights* w, const xpress_bf16* ba
 
 /* Top-C readout and argmax (kernels page, _xpress_topc_argmax_to_blk_kernel): for every row p,
  * k* = argmax_k (base_c[p, k] + lat[p] . w2c[p, k]) and blk[n, b] = cand[p, k*]; ties go to the
- * lowest vocabulary id. Shapes as in xpress_topc_prepare with c candidates per row. */
+ * lowest vocabulary id cand[p, k], whatever the order of the candidates in the row (the
+ * qwen3_xpress page notes that the candidate order does not matter). Shapes as in
+ * xpress_topc_prepare with c candidates per row; cand may hold the ids in any order. */
 xpress_status xpress_readout_argmax_topc(const xpress_bf16* lat, const xpress_bf16* w2c,
                                          const xpress_bf16* base_c, const int64_t* cand,
                                          int32_t N, int32_t B, int32_t r, int32_t c,

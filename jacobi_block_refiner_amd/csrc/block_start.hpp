@@ -56,6 +56,8 @@ __device__ __forceinline__ void initial_block_row(const uint16_t* __restrict__ b
   __syncthreads();
   if (tid == 0) {
     for (int w = 1; w < 4; ++w) argmax_merge(bv, bi, s_v[w], s_i[w]);
+    // nothing rose above -inf (a row of -inf, or NaN): the lowest id, 0, as for equal values
+    if (bi == INT_MAX) bi = 0;
     const int n = p / (B - 1), b = 1 + p % (B - 1);
     blk[(int64_t)n * B + b] = bi;
     if (b == 1) blk[(int64_t)n * B] = anchor[n];

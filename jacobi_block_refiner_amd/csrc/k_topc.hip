@@ -444,7 +444,11 @@ __device__ __forceinline__ void topc_select_row(int p, const uint16_t* __restric
   if (lane == 0) s_cnt[wave] = wcnt;
   __syncthreads();
   const int wmax = max(max(s_cnt[0], s_cnt[1]), max(s_cnt[2], s_cnt[3]));
-  if (wmax > kSeg) {  // uniform
+  const int wsum = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+  // A quarter that overflowed, or fewer than c buffered elements (a row with fewer than c finite
+  // values: -inf and NaN never pass the compare), goes to the exact path, which orders every bit
+  // pattern by its key, so c in-range ids are always written.
+  if (wmax > kSeg || wsum < c) {  // uniform
     select_row_exact(row, V, c, out_id, out_b, s_hist, s_tmp, s_par);
     return;
   }
@@ -614,8 +618,7 @@ __global__ __launch_bounds__(256) void topc_gather_kernel(const int64_t* __restr
 // per pass: the kernel is bound by how many bytes are in flight). BY_ID: the rows are w2[cand[p,
 // k]] (table = w2 [V, r]), and each lane loads the ids of its next round's candidates one round
 // ahead; otherwise table = w2c [rows, c, r], the gathered copy. The winner is tracked by
-// candidate index -- cand is ascending, so the lowest index is the lowest vocabulary id -- and
-// translated to its id once at the end.
+// (value, vocabulary id): equal values go to the lowest id whatever the order of cand.
 template <int R, bool BY_ID>
 __global__ __launch_bounds__(256) void topc_readout_kernel(
     const uint16_t* __restrict__ lat, const float* __restrict__ shares, int nsh,
@@ -670,24 +673,26 @@ __global__ __launch_bounds__(256) void topc_readout_kernel(
   const uint4* wrow = reinterpret_cast<const uint4*>(table + (BY_ID ? 0 : (int64_t)p * c * R));
   const int64_t* crow = cand + (int64_t)p * c;
   float bv = -INFINITY;
-  int bk = INT_MAX;
-  int64_t idn[U];  // BY_ID: the ids of this lane's candidates in the coming round
+  int bid = INT_MAX;  // vocabulary id of the best candidate so far
+  int idn[U];         // BY_ID: the ids of this lane's candidates in the coming round
   if constexpr (BY_ID) {
 #pragma unroll
-    for (int j = 0; j < U; ++j) idn[j] = crow[min((j * 4 + wave) * CPW + sub, c - 1)];
+    for (int j = 0; j < U; ++j) idn[j] = (int)crow[min((j * 4 + wave) * CPW + sub, c - 1)];
   }
   for (int k0 = 0; k0 < c; k0 += CPR) {
     uint4 u[U];
     uint16_t bk16[U];
+    int idc[U];  // this round's ids
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const int k = min(k0 + (j * 4 + wave) * CPW + sub, c - 1);  // past c: repeats, masked
-      u[j] = wrow[(BY_ID ? idn[j] : (int64_t)k) * G + q];
+      idc[j] = BY_ID ? idn[j] : (int)crow[k];
+      u[j] = wrow[(BY_ID ? (int64_t)idn[j] : (int64_t)k) * G + q];
       bk16[j] = bc[k];
     }
     if constexpr (BY_ID) {  // the next round's ids (past c: clamped, unused)
 #pragma unroll
-      for (int j = 0; j < U; ++j) idn[j] = crow[min(k0 + CPR + (j * 4 + wave) * CPW + sub, c - 1)];
+      for (int j = 0; j < U; ++j) idn[j] = (int)crow[min(k0 + CPR + (j * 4 + wave) * CPW + sub, c - 1)];
     }
 #pragma unroll
     for (int j = 0; j < U; ++j) {
@@ -702,23 +707,26 @@ __global__ __launch_bounds__(256) void topc_readout_kernel(
 #pragma unroll
       for (int off = G / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off);
       const int k = k0 + (j * 4 + wave) * CPW + sub;
-      argmax_merge(bv, bk, k < c ? bf16_to_f32(bk16[j]) + d : -INFINITY, k);
+      const bool in = k < c;
+      argmax_merge(bv, bid, in ? bf16_to_f32(bk16[j]) + d : -INFINITY, in ? idc[j] : INT_MAX);
     }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     const float ov = __shfl_xor(bv, off);
-    const int oi = __shfl_xor(bk, off);
-    argmax_merge(bv, bk, ov, oi);
+    const int oi = __shfl_xor(bid, off);
+    argmax_merge(bv, bid, ov, oi);
   }
   if (lane == 0) {
     s_v[wave] = bv;
-    s_i[wave] = bk;
+    s_i[wave] = bid;
   }
   __syncthreads();
   if (tid == 0) {
-    for (int w = 1; w < 4; ++w) argmax_merge(bv, bk, s_v[w], s_i[w]);
-    const int64_t id = crow[bk];
+    for (int w = 1; w < 4; ++w) argmax_merge(bv, bid, s_v[w], s_i[w]);
+    // a row whose every logit is NaN merges nothing: take its first candidate (results for
+    // non-finite inputs are unspecified, but the id stays a candidate's)
+    const int64_t id = bid == INT_MAX ? crow[0] : (int64_t)bid;
     const int n = p / (B - 1), b = 1 + p % (B - 1);
     int64_t* slot = blk + (int64_t)n * B + b;
     if (*slot != id) {

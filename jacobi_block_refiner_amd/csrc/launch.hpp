@@ -58,7 +58,8 @@ hipError_t launch_latent_fused(const uint2* part, int ntiles, int64_t* blk, cons
 // w1p[v, c] = sum_k in_proj[c, 2r + k] * w1[v, k], fp32 [V, r].
 hipError_t launch_fold_embedding(const uint16_t* w1, const uint16_t* in_proj, int r, int64_t V,
                                  float* w1p, hipStream_t s);
-// K5: per (vocab tile, row) partial argmax of base + lat . w2^T; part: [rows, ntiles].
+// K5: per (vocabulary range, row) partial argmax of base + lat . w2^T; part: [ntiles, rows],
+// range-major (part[t * rows + p]).
 hipError_t launch_readout_partial(const uint16_t* lat, const uint16_t* w2, const uint16_t* base,
                                   int64_t ld, int rows, int64_t V, int r, uint2* part,
                                   const int32_t* flags, int pass, hipStream_t s);

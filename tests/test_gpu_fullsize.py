@@ -55,7 +55,8 @@ def _gpu():
     _cache.clear()
 
 
-@pytest.mark.parametrize("wl_id,n_sample", [(2, 1), (3, 3), (5, 2)])
+# 256 blocks: 8 sampled blocks, one in each 512-row chunk of the readout
+@pytest.mark.parametrize("wl_id,n_sample", [(2, 1), (3, 3), (5, 8)])
 def test_one_pass_full_vocab(wl_id, n_sample):
     d = _dev(wl_id)
     inp = d.inp
@@ -77,7 +78,7 @@ def test_one_pass_full_vocab(wl_id, n_sample):
     assert bad == 0
 
 
-@pytest.mark.parametrize("wl_id,n_sample", [(2, 1), (3, 1), (5, 1)])
+@pytest.mark.parametrize("wl_id,n_sample", [(2, 1), (3, 2), (5, 3)])
 def test_step_reaches_fixed_point_and_matches_oracle(wl_id, n_sample):
     d = _dev(wl_id)
     inp, wl = d.inp, d.inp.wl
@@ -160,9 +161,18 @@ def test_topc_full_size():
     dr = draft_rows(got_blk)
     assert all(dr[p] in cc[p] for p in range(rows))
 
-    log("workload 4: step with top-C, K=B-1, then one more pass changes nothing")
+    log("workload 4: the selection with chunk maxima (the form a step runs)")
+    cand2 = torch.empty_like(cand)
+    base_c2 = torch.empty_like(base_c)
+    ws = d.ws(C=C, K=wl.B)
+    xpress.topc_prepare(d.w, d.base, wl.N, C, cand2, base_c2, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(cand2, cand) and torch.equal(base_c2, base_c)  # every row
+    rows_s2 = np.arange(5, rows, 41)
+    assert np.array_equal(cand2.cpu().numpy()[rows_s2], O.topc_select(inp.base[rows_s2], C))
+
+    log("workload 4: step with top-C, K=B-1 as the benchmark runs it, then one more pass")
     K = wl.B - 1
-    ws = d.ws(C=C, K=K + 1)
     blk = torch.zeros(wl.N, wl.B, dtype=torch.int64, device="cuda")
     xpress.jacobi_step(d.w, d.h, d.base, d.anchor, d.am1, blk, K=K, C=C,
                        flags=xpress.INIT_FROM_BASE, ws=ws)
@@ -173,3 +183,16 @@ def test_topc_full_size():
     xpress.readout_argmax_topc(lat2, w2c, base_c, cand, after, changed)
     torch.cuda.synchronize()
     assert int(changed.item()) == 0 and torch.equal(after, blk)
+    got = blk.cpu().numpy()
+    assert all(tok in cc[p] for p, tok in enumerate(draft_rows(got)))
+    blocks = _sample_blocks(wl.N, 3)
+    sub, _ = _subset(inp, blocks)
+    log(f"workload 4: oracle top-C Jacobi on blocks {blocks}")
+    xh_o = O.hidden_cache(sub.h, sub.down_h, sub.down_g, sub.in_proj)
+    cand_o = O.topc_select(sub.base, C)
+    start = O.initial_block(sub.base, sub.blk[:, 0], len(blocks), wl.B)
+    want, _, _, hg = O.jacobi(sub, L, xh_o, start, K=K, stop_at_fixed_point=False, cand=cand_o,
+                              history=True)
+    bad, exempt = end_to_end_ok(got[blocks], want, hg)
+    log(f"workload 4: end-to-end disallowed mismatches {bad}, near-tie row-passes {exempt}")
+    assert bad == 0

@@ -510,6 +510,84 @@ def test_topc_readout_dyadic_exact_and_membership(form, r, C):
         assert got[p] in cand_o[p]
 
 
+@pytest.mark.parametrize("form", ["gathered", "ids"])
+def test_topc_readout_ties_go_to_the_lowest_id_whatever_the_candidate_order(form):
+    """Each row's candidates handed over in a seeded shuffled order (with base_c and the gathered
+    rows permuted alike): the winner is the same lowest-id winner as with ascending candidates
+    (qwen3_xpress page: the candidate set is only indexed, so its order does not matter). The
+    dyadic case plants exact top ties between a low and a high id."""
+    rng = np.random.default_rng(13)
+    N, B, V, r, C = 4, 16, 6000, 256, 96
+    lat, w2, base = _readout_case(8, N, B, r, V)
+    w = _weights_with(w2, r, B, V)
+    rows = N * (B - 1)
+    cand_o = O.topc_select(base, C)
+    perm = np.argsort(rng.random((rows, C)), axis=1)
+    perm[0] = np.arange(C)[::-1]  # fully descending on one row
+    cand_s = np.take_along_axis(cand_o, perm, axis=1)
+    base_c_s = np.take_along_axis(base, cand_s, axis=1)
+    cand = upload.tokens(cand_s)
+    base_c = upload.bf16_tensor(base_c_s)
+    blk = upload.tokens(rng.integers(0, V, (N, B)))
+    log(f"top-C readout {form}, shuffled candidates")
+    if form == "gathered":
+        w2c = upload.bf16_tensor(w2[cand_s])
+        xpress.readout_argmax_topc(upload.bf16_tensor(lat), w2c, base_c, cand, blk)
+    else:
+        xpress.readout_argmax_topc_ids(w, upload.bf16_tensor(lat), base_c, cand, blk)
+    torch.cuda.synchronize()
+    best, _, _ = O.readout_argmax(lat, w2, base, cand=cand_o)
+    best_s, _, _ = O.readout_argmax(lat, w2, base, cand=cand_s)
+    assert np.array_equal(best, best_s)  # the oracle's rule is order-free too
+    got = draft_rows(blk.cpu().numpy())
+    assert np.array_equal(got, best)
+    planted = [p for p in range(0, rows, 3) if best[p] == p]
+    assert len(planted) >= rows // 6  # the planted low ids do win their ties
+
+
+@pytest.mark.parametrize("chunk_maxima", [False, True])
+@pytest.mark.parametrize("V,C", [(5003, 64), (151936, 512)])
+def test_topc_rows_with_fewer_finite_values_than_candidates(V, C, chunk_maxima):
+    """Rows where fewer than C values are finite (the rest -inf, as a vocabulary mask leaves
+    them): the candidate sets are still the C largest under (value desc, id asc) -- -inf below
+    every finite value, ties to the lowest ids -- so every id is in range, and the top-C readout
+    and the step's starting block pick candidates. Inputs that are not finite fall outside the
+    pages' method; this checks that the selection stays exact and in range for them."""
+    rng = np.random.default_rng(14)
+    N, B, r = 2, 3, 64
+    rows = N * (B - 1)
+    base = synth.bf16_round(rng.standard_normal((rows, V)).astype(np.float32))
+    base[0, :] = -np.inf
+    base[0, rng.choice(V, C // 4, replace=False)] = 1.5         # C/4 finite values, tied
+    base[1, :] = -np.inf                                        # no finite value at all
+    base[2, :] = -np.inf
+    keep = rng.choice(V, C - 1, replace=False)
+    base[2, keep] = synth.bf16_round(rng.standard_normal(C - 1).astype(np.float32))
+    base[3, rng.choice(V, V // 2, replace=False)] = -np.inf     # plenty of finite values left
+    w2 = synth.bf16_round(rng.standard_normal((V, r)).astype(np.float32) * 0.1)
+    w = _weights_with(w2, r, B, V)
+    cand = torch.empty(rows, C, dtype=torch.int64, device="cuda")
+    base_c = torch.empty(rows, C, dtype=torch.bfloat16, device="cuda")
+    ws = _select_scratch(rows, V) if chunk_maxima else None
+    log(f"top-C prepare with -inf rows V={V} C={C} chunk_maxima={chunk_maxima}")
+    xpress.topc_prepare(w, upload.base_logits(base), N, C, cand, base_c, None, ws)
+    torch.cuda.synchronize()
+    got = cand.cpu().numpy()
+    assert got.min() >= 0 and got.max() < V
+    want = O.topc_select(base, C)
+    assert np.array_equal(got, want)
+    assert np.array_equal(base_c.float().cpu().numpy(), np.take_along_axis(base, want, axis=1))
+    lat = synth.bf16_round(rng.standard_normal((rows, r)).astype(np.float32))
+    blk = upload.tokens(np.zeros((N, B), np.int64))
+    xpress.readout_argmax_topc_ids(w, upload.bf16_tensor(lat), base_c, cand, blk)
+    torch.cuda.synchronize()
+    best, gap, _ = O.readout_argmax(lat, w2, base, cand=want)
+    got_t = draft_rows(blk.cpu().numpy())
+    assert all(got_t[p] in want[p] for p in range(rows))
+    assert compare_tokens(got_t, best, gap)[0] == 0
+    assert got_t[1] == 0  # every logit -inf: the lowest id
+
+
 @pytest.mark.parametrize("C", [1, 10 ** 6])
 def test_topc_step_limits(C):
     """C = 1 always returns argmax(base); C >= V scores every id, as the full-vocabulary step."""
@@ -533,11 +611,13 @@ def test_topc_step_limits(C):
     assert end_to_end_ok(got, want, hg)[0] == 0
 
 
-@pytest.mark.parametrize("path,M", [("table", 128), ("project", 128), ("table", 1024)])
-def test_topc_step_matches_oracle(path, M):
+@pytest.mark.parametrize("path,M,r", [("table", 128, 64), ("project", 128, 64), ("table", 1024, 64),
+                                      ("table", 512, 256), ("project", 512, 256)])
+def test_topc_step_matches_oracle(path, M, r):
     """With the projected table the top-C readout sums the latent shares itself (no lat); at
-    M = 1024 there are 16 slice shares, two rounds of eight."""
-    inp = strong(synth.make_inputs(replace(synth.WORKLOADS[1], B=8, M=M), N=6, seed=6))
+    M = 1024 there are 16 slice shares, two rounds of eight; r = 256 with M = 512 is the shape of
+    the 32-block top-512 workload."""
+    inp = strong(synth.make_inputs(replace(synth.WORKLOADS[1], B=8, M=M, r=r), N=6, seed=6))
     N, B = inp.blk.shape
     wl = inp.wl
     C = 48
