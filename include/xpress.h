@@ -230,6 +230,24 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
                                  uint32_t flags, int64_t* blk, int32_t* passes_run, void* ws,
                                  size_t ws_bytes, xpress_stream stream);
 
+/* The same draft step as xpress_jacobi_step, for callers that cannot allocate device memory or
+ * hand over a workspace (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): no ws argument, and the call allocates nothing. Its scratch is a static array of
+ * the library on each GPU (64 MiB, created with the library's code object on that GPU and held
+ * until the process ends); the first call on a GPU looks up its address there. Every call on one
+ * GPU shares that array, so calls that overlap on one GPU (concurrent streams or threads) race
+ * and must be serialised by the caller; each call clears what it needs cleared itself, so
+ * nothing carries over from the previous call. A step whose workspace (xpress_workspace_size for
+ * its N, C and K) exceeds 64 MiB returns XPRESS_ERR_WORKSPACE before enqueueing anything: 64 MiB
+ * covers a full-vocabulary step of up to 256 blocks and a top-512 step of up to 64 blocks at
+ * B = 16, r = 256, V = 151936, K = 15. Arguments, results and other errors as in
+ * xpress_jacobi_step. */
+xpress_status xpress_jacobi_step_noalloc(const xpress_weights* w, const xpress_bf16* h,
+                                         const xpress_bf16* base, int64_t base_ld,
+                                         const int64_t* anchor, const int64_t* am1, int32_t N,
+                                         int32_t K, int32_t C, uint32_t flags, int64_t* blk,
+                                         int32_t* passes_run, xpress_stream stream);
+
 /* A draft step recorded once as a HIP graph and replayed with one launch (the pages capture
  * the pass loop in a graph with fixed buffer addresses: qwen3_xpress page, jacobi_refine_greedy;
  * kernels page, module docstring). xpress_jacobi_step_graph checks the arguments exactly as

@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "launch.hpp"
@@ -149,6 +150,38 @@ Layout step_layout(int N, int B, int r, int H, int64_t V, int C, int K) {
 template <typename T>
 T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// Library-owned workspace of the allocation-free step: one array per GPU, in the code object's
+// device globals, held until the process ends. 64 MiB covers a full-vocabulary step of up to 256
+// blocks (43.4 MiB at B = 16, r = 256, V = 151936, K = 15) and a top-512 step of up to 64 blocks
+// (62.9 MiB). In host code the name `scratch` is only a stand-in for the symbol; its device
+// address on each GPU comes from hipGetSymbolAddress (scratch_ptr) and is what the kernels get.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device (the first call
+// on it) with that device current.
+xpress_status scratch_ptr(void** out) {
+  int dev = -1;
+  XP_TRY(hipGetDevice(&dev), "current device");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(XPRESS_ERR_HIP, "device %d outside the %d devices the static scratch supports", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    XP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "static scratch address");
+    if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0)
+      return fail(XPRESS_ERR_HIP, "static scratch address %p is not 256-byte aligned", p);
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return XPRESS_OK;
 }
 
 }  // namespace
@@ -491,6 +524,29 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
   if (passes_run && !last_reduce)
     XP_TRY(xpress::launch_count_passes(pf, K, stop ? 1 : 0, passes_run, s), "count passes");
   return XPRESS_OK;
+}
+
+xpress_status xpress_jacobi_step_noalloc(const xpress_weights* w, const xpress_bf16* h,
+                                         const xpress_bf16* base, int64_t base_ld,
+                                         const int64_t* anchor, const int64_t* am1, int32_t N,
+                                         int32_t K, int32_t C, uint32_t flags, int64_t* blk,
+                                         int32_t* passes_run, xpress_stream stream) {
+  if (w == nullptr) return fail(XPRESS_ERR_ARG, "weights struct is NULL");
+  xpress_status st = check_dims(w->B, w->r, w->V);
+  if (st != XPRESS_OK) return st;
+  if (N < 0 || K < 0 || C < 0) return fail(XPRESS_ERR_ARG, "negative N, K or C");
+  if (N == 0) return XPRESS_OK;
+  const size_t need = step_layout(N, w->B, w->r, w->H, w->V, C, K).total;
+  if (need > kStaticScratchBytes)
+    return fail(XPRESS_ERR_WORKSPACE,
+                "the step needs %zu bytes of scratch (N=%d, C=%d, K=%d), more than the %zu bytes "
+                "of the allocation-free step's static scratch; use xpress_jacobi_step with a "
+                "caller workspace", need, N, C, K, kStaticScratchBytes);
+  void* ws = nullptr;
+  st = scratch_ptr(&ws);
+  if (st != XPRESS_OK) return st;
+  return xpress_jacobi_step(w, h, base, base_ld, anchor, am1, N, K, C, flags, blk, passes_run, ws,
+                            kStaticScratchBytes, stream);
 }
 
 xpress_status xpress_jacobi_step_graph(const xpress_weights* w, const xpress_bf16* h,

@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
             "xpress_readout_argmax_topc_ids": [W, P, P, P, i32, i32, P, P, P],
             "xpress_jacobi_step": [W, P, P, i64, P, P, i32, i32, i32, ctypes.c_uint32, P, P, P,
                                    sz, P],
+            "xpress_jacobi_step_noalloc": [W, P, P, i64, P, P, i32, i32, i32, ctypes.c_uint32,
+                                           P, P, P],
             "xpress_jacobi_step_graph": [W, P, P, i64, P, P, i32, i32, i32, ctypes.c_uint32, P, P,
                                          P, sz, ctypes.POINTER(ctypes.c_void_p)],
             "xpress_graph_launch": [P, P],
@@ -289,6 +291,21 @@ def jacobi_step(w: Weights, h, base, anchor, am1, blk, *, K: int, C: int = 0,
                                     ctypes.c_void_p(base.data_ptr()), base.stride(0), _ptr(anchor),
                                     _ptr(am1), N, K, C, flags, _ptr(blk), _ptr(passes_run),
                                     _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return blk
+
+
+def jacobi_step_noalloc(w: Weights, h, base, anchor, am1, blk, *, K: int, C: int = 0,
+                        flags: int = INIT_FROM_BASE, passes_run=None) -> torch.Tensor:
+    """``jacobi_step`` on the library's own static per-GPU scratch: no workspace argument and no
+    allocation. Calls that overlap on one GPU share that scratch and race."""
+    s = w.struct()
+    _bf16(base, "base")
+    assert base.stride(1) == 1
+    N = blk.shape[0]
+    _check(lib().xpress_jacobi_step_noalloc(ctypes.byref(s), _ptr(_bf16(h, "h")),
+                                            ctypes.c_void_p(base.data_ptr()), base.stride(0),
+                                            _ptr(anchor), _ptr(am1), N, K, C, flags, _ptr(blk),
+                                            _ptr(passes_run), _stream()))
     return blk
 
 
