@@ -144,9 +144,12 @@ def main() -> int:
     rows = wl.rows
     xh = torch.empty(wl.N, wl.B, wl.r, dtype=torch.float32, device=dev)
     xpress.hidden_cache(w, h, xh, ws)
-    lat = torch.empty(wl.N, wl.B - 1, wl.r, dtype=torch.bfloat16, device=dev)
+    # the latent layout the step keeps: fragment order for the full-vocabulary readout,
+    # row-major for the top-C readout
+    lay = xpress.LAT_ROWS if wl.C > 0 else xpress.LAT_FRAGMENTS
+    lat = xpress.lat_buffer(wl.N, wl.B, wl.r, lay, dev)
     blk2 = blk.clone()
-    xpress.latent_pass(w, blk2, am1, xh, lat, ws)
+    xpress.latent_pass(w, blk2, am1, xh, lat, ws, layout=lay)
     ntiles = xpress.readout_tiles(wl.V, rows)
     part = torch.empty(ntiles, rows, 2, dtype=torch.int32, device=dev)
 
@@ -174,10 +177,10 @@ def main() -> int:
         fn_reduce = None
         readout_pass = fn_readout
     else:
-        fn_readout = lambda: xpress.readout_partials(w, lat, base, part)
+        fn_readout = lambda: xpress.readout_partials(w, lat, base, part, layout=lay)
         fn_reduce = lambda: xpress.argmax_reduce(part, blk2)
-        readout_pass = lambda: xpress.readout_argmax(w, lat, base, blk2, ws)
-    fn_latent = lambda: xpress.latent_pass(w, blk2, am1, xh, lat, ws)
+        readout_pass = lambda: xpress.readout_argmax(w, lat, base, blk2, ws, layout=lay)
+    fn_latent = lambda: xpress.latent_pass(w, blk2, am1, xh, lat, ws, layout=lay)
     for f in (fn_readout, fn_reduce, fn_latent):
         if f is not None:
             f()
@@ -191,7 +194,7 @@ def main() -> int:
 
     def loop():
         for _ in range(K):
-            xpress.latent_pass(w, blk2, am1, xh, lat, ws)
+            xpress.latent_pass(w, blk2, am1, xh, lat, ws, layout=lay)
             readout_pass()
 
     loop()

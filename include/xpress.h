@@ -96,6 +96,17 @@ typedef struct {
                                           agree with the NULL path within fp32 rounding        */
 } xpress_weights;
 
+/* Layouts of the latent rows lat (N*(B-1) readout rows of r channels, bf16):
+ *   XPRESS_LAT_ROWS       row-major [N*(B-1), r];
+ *   XPRESS_LAT_FRAGMENTS  the order in which the full-vocabulary readout's matrix core takes them
+ *                         (the layout a draft step keeps): rows in tiles of 32; for tile T,
+ *                         16-channel group s and lane l = 32*h + (p % 32), the 8 channels
+ *                         16*s + 8*h .. +7 of row p = 32*T + (p % 32) are the 16 bytes at byte
+ *                         offset ((T*(r/16) + s)*64 + l)*16. The buffer holds ceil(N*(B-1)/32)
+ *                         whole tiles (the rows past N*(B-1) are never written or used). */
+#define XPRESS_LAT_ROWS 0u
+#define XPRESS_LAT_FRAGMENTS 1u
+
 /* Flags of xpress_jacobi_step. */
 #define XPRESS_INIT_FROM_BASE 1u      /* blk[:,0] = anchor, blk[:,1:] = argmax(base) first    */
 #define XPRESS_STOP_AT_FIXED_POINT 2u /* passes after the first pass that changes no slot
@@ -143,21 +154,24 @@ xpress_status xpress_initial_block(const xpress_bf16* base, int64_t base_ld,
  * _refine_latent): reads blk, never writes it. Token ids outside [0, V) contribute a zero
  * embedding.
  * blk: [N, B]; am1: [N] (token before each anchor); xh: [N, B, r] fp32 from xpress_hidden_cache;
- * lat: [N, B-1, r] bf16 (written; row n*(B-1)+b-1 is slot b). ws: scratch of ws_bytes bytes
- * (a workspace sized by xpress_workspace_size for at least N blocks is enough). */
+ * lat: [N, B-1, r] bf16 (written; row n*(B-1)+b-1 is slot b) in lat_layout (XPRESS_LAT_ROWS or
+ * XPRESS_LAT_FRAGMENTS; other values are XPRESS_ERR_ARG). ws: scratch of ws_bytes bytes (a
+ * workspace sized by xpress_workspace_size for at least N blocks is enough). */
 xpress_status xpress_latent_pass(const xpress_weights* w, const int64_t* blk, const int64_t* am1,
-                                 const float* xh, int32_t N, xpress_bf16* lat, void* ws,
-                                 size_t ws_bytes, xpress_stream stream);
+                                 const float* xh, int32_t N, xpress_bf16* lat,
+                                 uint32_t lat_layout, void* ws, size_t ws_bytes,
+                                 xpress_stream stream);
 
 /* Full-vocabulary readout and argmax (kernels page, fused_add_argmax_to_blk; qwen3_xpress page,
  * refine_bias): blk[n, b] = argmax_v (base[p, v] + lat[p] . w2[v]) for p = n*(B-1)+b-1, written in
  * place for slots 1..B-1. The [N*(B-1), V] logits are never stored.
- * lat: [N*(B-1), r] bf16; base: [N*(B-1), V] bf16 stride base_ld; blk: [N, B] in/out.
- * changed (nullable): set to 1 if any slot took a new value (never cleared by this call). */
+ * lat: [N*(B-1), r] bf16 in lat_layout; base: [N*(B-1), V] bf16 stride base_ld; blk: [N, B]
+ * in/out. changed (nullable): set to 1 if any slot took a new value (never cleared by this
+ * call). */
 xpress_status xpress_readout_argmax(const xpress_weights* w, const xpress_bf16* lat,
-                                    const xpress_bf16* base, int64_t base_ld, int32_t N,
-                                    int64_t* blk, int32_t* changed, void* ws, size_t ws_bytes,
-                                    xpress_stream stream);
+                                    uint32_t lat_layout, const xpress_bf16* base,
+                                    int64_t base_ld, int32_t N, int64_t* blk, int32_t* changed,
+                                    void* ws, size_t ws_bytes, xpress_stream stream);
 
 /* The two stages of xpress_readout_argmax, for callers that reduce the per-range winners
  * themselves (for example across GPUs that each hold a slice of the vocabulary) and for timing
@@ -171,13 +185,14 @@ xpress_status xpress_readout_argmax(const xpress_weights* w, const xpress_bf16* 
  *   including) floor(S*(t+1) / ntiles), the last clipped to V. rows < 1 is XPRESS_ERR_ARG.
  * xpress_readout_partials: part[t * N*(B-1) + p] = {bits of the fp32 maximum of base + lat . w2
  *   over range t of row p, the lowest vocabulary id attaining it}. part: [ntiles, N*(B-1)] pairs
- *   of uint32, range-major (caller-owned, 8 bytes each).
+ *   of uint32, range-major (caller-owned, 8 bytes each). lat in lat_layout.
  * xpress_argmax_reduce: blk[n, b] = the id of the largest pair of row p = n*(B-1)+b-1 (ties:
  *   lowest id), written in place; `changed` as in xpress_readout_argmax. */
 xpress_status xpress_readout_tiles(int64_t V, int32_t rows, int32_t* ntiles);
 xpress_status xpress_readout_partials(const xpress_weights* w, const xpress_bf16* lat,
-                                      const xpress_bf16* base, int64_t base_ld, int32_t N,
-                                      uint32_t* part, xpress_stream stream);
+                                      uint32_t lat_layout, const xpress_bf16* base,
+                                      int64_t base_ld, int32_t N, uint32_t* part,
+                                      xpress_stream stream);
 xpress_status xpress_argmax_reduce(const uint32_t* part, int32_t ntiles, int32_t N, int32_t B,
                                    int64_t* blk, int32_t* changed, xpress_stream stream);
 

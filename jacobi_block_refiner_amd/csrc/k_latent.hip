@@ -238,7 +238,7 @@ template <int R, int G>
 __global__ __launch_bounds__(256) void latent_down_kernel(
     const uint16_t* __restrict__ s16, const float* __restrict__ u32,
     const uint16_t* __restrict__ w_down, int M, int B, int nrows, uint16_t* __restrict__ lat,
-    const int32_t* __restrict__ flags, int pass) {
+    const int32_t* __restrict__ flags, int pass, int lat_frag) {
   if (pass_skipped(flags, pass)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, q4 = lane >> 4;
@@ -276,9 +276,11 @@ __global__ __launch_bounds__(256) void latent_down_kernel(
     for (int v = 0; v < 4; ++v) {
       const int r = r0 + 16 * g + 4 * q4 + v;  // row = 16 * block + slot
       const int n = r >> 4, slot = r & 15;
-      if (r < nrows && slot >= 1 && slot < B)
-        lat[((int64_t)n * (B - 1) + slot - 1) * R + c] =
+      if (r < nrows && slot >= 1 && slot < B) {
+        const int p = n * (B - 1) + slot - 1;
+        lat[lat_frag ? lat_frag_offset<R>(p, c) : (int64_t)p * R + c] =
             f32_to_bf16(u32[(int64_t)r * R + c] + acc[g][v]);
+      }
     }
 }
 
@@ -483,7 +485,7 @@ template <int R>
 __global__ __launch_bounds__(256) void latent_sum_kernel(const float* __restrict__ dpart, int B,
                                                          int G, uint16_t* __restrict__ lat,
                                                          const int32_t* __restrict__ flags,
-                                                         int pass, int prev) {
+                                                         int pass, int prev, int lat_frag) {
   if (prev ? pass_skipped(flags, pass - 1) : pass_skipped(flags, pass)) return;
   constexpr int QR = R / 4;
   constexpr int RPW = 256 / QR;
@@ -509,7 +511,8 @@ __global__ __launch_bounds__(256) void latent_sum_kernel(const float* __restrict
   uint2 o;
   o.x = pack_bf16x2(acc.x, acc.y);
   o.y = pack_bf16x2(acc.z, acc.w);
-  *reinterpret_cast<uint2*>(lat + ((int64_t)n * (B - 1) + b - 1) * R + 4 * q) = o;
+  const int p = n * (B - 1) + b - 1;
+  *reinterpret_cast<uint2*>(lat + (lat_frag ? lat_frag_offset<R>(p, 4 * q) : (int64_t)p * R + 4 * q)) = o;
 }
 
 template <int R>
@@ -517,8 +520,9 @@ hipError_t launch_r(const uint2* part, int ntiles, int64_t* blk, const int64_t* 
                     const float* xh, const uint16_t* w1, const uint16_t* in_proj,
                     const uint16_t* mix_L, const uint16_t* w_gate, const uint16_t* w_up,
                     const uint16_t* w_down, int N, int B, int M, int64_t V, uint16_t* lat,
-                    void* scratch, int32_t* flags, int pass, hipStream_t s) {
+                    void* scratch, int32_t* flags, int pass, hipStream_t s, bool lat_frag) {
   const int nrows = N * 16;
+  const int lf = lat_frag ? 1 : 0;
   float* u32 = static_cast<float*>(scratch);
   uint16_t* u16 = reinterpret_cast<uint16_t*>(u32 + (size_t)nrows * R);
   uint16_t* s16 = u16 + (size_t)nrows * R;
@@ -531,12 +535,12 @@ hipError_t launch_r(const uint2* part, int ntiles, int64_t* blk, const int64_t* 
     hipLaunchKernelGGL((latent_gate_kernel<R, 4>), g2, dim3(256), 0, s, u16, w_gate, w_up, M,
                        nrows, s16, flags, pass);
     hipLaunchKernelGGL((latent_down_kernel<R, 4>), g3, dim3(256), 0, s, s16, u32, w_down, M, B,
-                       nrows, lat, flags, pass);
+                       nrows, lat, flags, pass, lf);
   } else {
     hipLaunchKernelGGL((latent_gate_kernel<R, 1>), g2, dim3(256), 0, s, u16, w_gate, w_up, M,
                        nrows, s16, flags, pass);
     hipLaunchKernelGGL((latent_down_kernel<R, 1>), g3, dim3(256), 0, s, s16, u32, w_down, M, B,
-                       nrows, lat, flags, pass);
+                       nrows, lat, flags, pass, lf);
   }
   return hipGetLastError();
 }
@@ -546,7 +550,8 @@ hipError_t launch_fused_r(const uint2* part, int ntiles, int64_t* blk, const int
                           const float* xh, const float* w1p, const uint16_t* mix_L,
                           const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                           int N, int B, int M, int64_t V, uint16_t* lat, float* dpart,
-                          int32_t* flags, int pass, hipStream_t s, bool with_sum) {
+                          int32_t* flags, int pass, hipStream_t s, bool with_sum,
+                          bool lat_frag) {
   const int G = M / 64;
   hipLaunchKernelGGL(latent_share_kernel<R>, dim3(N, G), dim3(256), 0, s, part, ntiles,
                      N * (B - 1), blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, B, M, V, dpart,
@@ -554,7 +559,7 @@ hipError_t launch_fused_r(const uint2* part, int ntiles, int64_t* blk, const int
   if (!with_sum) return hipGetLastError();
   constexpr int RPW = 256 / (R / 4);
   hipLaunchKernelGGL(latent_sum_kernel<R>, dim3(N, (B - 1 + RPW - 1) / RPW), dim3(256), 0, s,
-                     dpart, B, G, lat, flags, pass, part != nullptr ? 1 : 0);
+                     dpart, B, G, lat, flags, pass, part != nullptr ? 1 : 0, lat_frag ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -569,11 +574,11 @@ hipError_t launch_latent_fused(const uint2* part, int ntiles, int64_t* blk, cons
                                const uint16_t* w_gate, const uint16_t* w_up,
                                const uint16_t* w_down, int N, int B, int r, int M, int64_t V,
                                uint16_t* lat, float* dpart, int32_t* flags, int pass,
-                               hipStream_t s, bool with_sum) {
+                               hipStream_t s, bool with_sum, bool lat_frag) {
   switch (r) {
-    case 64: return launch_fused_r<64>(part, ntiles, blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, dpart, flags, pass, s, with_sum);
-    case 128: return launch_fused_r<128>(part, ntiles, blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, dpart, flags, pass, s, with_sum);
-    case 256: return launch_fused_r<256>(part, ntiles, blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, dpart, flags, pass, s, with_sum);
+    case 64: return launch_fused_r<64>(part, ntiles, blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, dpart, flags, pass, s, with_sum, lat_frag);
+    case 128: return launch_fused_r<128>(part, ntiles, blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, dpart, flags, pass, s, with_sum, lat_frag);
+    case 256: return launch_fused_r<256>(part, ntiles, blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, dpart, flags, pass, s, with_sum, lat_frag);
     default: return hipErrorInvalidValue;
   }
 }
@@ -599,11 +604,12 @@ hipError_t launch_latent(const uint2* part, int ntiles, int64_t* blk, const int6
                          const float* xh, const uint16_t* w1, const uint16_t* in_proj,
                          const uint16_t* mix_L, const uint16_t* w_gate, const uint16_t* w_up,
                          const uint16_t* w_down, int N, int B, int r, int M, int64_t V,
-                         uint16_t* lat, void* scratch, int32_t* flags, int pass, hipStream_t s) {
+                         uint16_t* lat, void* scratch, int32_t* flags, int pass, hipStream_t s,
+                         bool lat_frag) {
   switch (r) {
-    case 64: return launch_r<64>(part, ntiles, blk, am1, xh, w1, in_proj, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, scratch, flags, pass, s);
-    case 128: return launch_r<128>(part, ntiles, blk, am1, xh, w1, in_proj, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, scratch, flags, pass, s);
-    case 256: return launch_r<256>(part, ntiles, blk, am1, xh, w1, in_proj, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, scratch, flags, pass, s);
+    case 64: return launch_r<64>(part, ntiles, blk, am1, xh, w1, in_proj, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, scratch, flags, pass, s, lat_frag);
+    case 128: return launch_r<128>(part, ntiles, blk, am1, xh, w1, in_proj, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, scratch, flags, pass, s, lat_frag);
+    case 256: return launch_r<256>(part, ntiles, blk, am1, xh, w1, in_proj, mix_L, w_gate, w_up, w_down, N, B, M, V, lat, scratch, flags, pass, s, lat_frag);
     default: return hipErrorInvalidValue;
   }
 }

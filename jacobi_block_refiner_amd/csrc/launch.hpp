@@ -38,12 +38,15 @@ hipError_t launch_initial_block(const uint16_t* base, int64_t ld, const int64_t*
 size_t latent_scratch_bytes(int N, int r, int M);
 // Steps 1-5 of the latent. With part != nullptr (inside a step, pass >= 1) the mix kernel first
 // reduces the previous pass's range-major partials into blk for its block and raises
-// flags[pass-1] on a change; blk is then written. Otherwise blk is only read.
+// flags[pass-1] on a change; blk is then written. Otherwise blk is only read. lat is row-major
+// [N*(B-1), r], or with lat_frag in the readout's fragment order (lat_frag_offset; the buffer
+// then holds ceil(N*(B-1)/32) whole 32-row tiles).
 hipError_t launch_latent(const uint2* part, int ntiles, int64_t* blk, const int64_t* am1,
                          const float* xh, const uint16_t* w1, const uint16_t* in_proj,
                          const uint16_t* mix_L, const uint16_t* w_gate, const uint16_t* w_up,
                          const uint16_t* w_down, int N, int B, int r, int M, int64_t V,
-                         uint16_t* lat, void* scratch, int32_t* flags, int pass, hipStream_t s);
+                         uint16_t* lat, void* scratch, int32_t* flags, int pass, hipStream_t s,
+                         bool lat_frag = false);
 // K4 from the projected embedding table w1p (launch_fold_embedding), two launches: the
 // per-(block, 64-unit slice) shares of the latent, then their sum into lat (skipped with
 // with_sum = false, for a consumer that sums the shares itself). dpart: [N, M/64, 16,
@@ -54,15 +57,16 @@ hipError_t launch_latent_fused(const uint2* part, int ntiles, int64_t* blk, cons
                                const uint16_t* w_gate, const uint16_t* w_up,
                                const uint16_t* w_down, int N, int B, int r, int M, int64_t V,
                                uint16_t* lat, float* dpart, int32_t* flags, int pass,
-                               hipStream_t s, bool with_sum = true);
+                               hipStream_t s, bool with_sum = true, bool lat_frag = false);
 // w1p[v, c] = sum_k in_proj[c, 2r + k] * w1[v, k], fp32 [V, r].
 hipError_t launch_fold_embedding(const uint16_t* w1, const uint16_t* in_proj, int r, int64_t V,
                                  float* w1p, hipStream_t s);
 // K5: per (vocabulary range, row) partial argmax of base + lat . w2^T; part: [ntiles, rows],
-// range-major (part[t * rows + p]).
+// range-major (part[t * rows + p]). lat row-major, or with lat_frag in fragment order.
 hipError_t launch_readout_partial(const uint16_t* lat, const uint16_t* w2, const uint16_t* base,
                                   int64_t ld, int rows, int64_t V, int r, uint2* part,
-                                  const int32_t* flags, int pass, hipStream_t s);
+                                  const int32_t* flags, int pass, hipStream_t s,
+                                  bool lat_frag = false);
 // K6: per-row reduce of the partials into blk[n, 1 + p % (B-1)].
 // With passes_run (nullable; the last pass of a step, pass = K-1), also writes the number of
 // passes that ran, as launch_count_passes would.

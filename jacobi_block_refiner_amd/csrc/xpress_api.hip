@@ -93,6 +93,13 @@ xpress_status check_weights(const xpress_weights* w, bool need_hidden, bool need
   return XPRESS_OK;
 }
 
+xpress_status check_layout(uint32_t lat_layout) {
+  if (lat_layout != XPRESS_LAT_ROWS && lat_layout != XPRESS_LAT_FRAGMENTS)
+    return fail(XPRESS_ERR_ARG, "lat_layout=%u is neither XPRESS_LAT_ROWS nor XPRESS_LAT_FRAGMENTS",
+                lat_layout);
+  return XPRESS_OK;
+}
+
 xpress_status check_base(const xpress_bf16* base, int64_t ld, int64_t V) {
   XP_PTR(base);
   if (ld < V || ld % 8) return fail(XPRESS_ERR_ARG, "base_ld=%lld must be >= V=%lld and a multiple of 8",
@@ -135,7 +142,7 @@ Layout step_layout(int N, int B, int r, int H, int64_t V, int C, int K) {
   (void)H;
   L.hdg = take(xpress::hidden_scratch_bytes_any_h(N * B, r));
   L.xh = take((size_t)N * B * r * sizeof(float));
-  L.lat = take(rows * r * 2);
+  L.lat = take((rows + 31) / 32 * 32 * (size_t)r * 2);  // whole 32-row tiles (fragment order)
   L.lscr = take(latent_bytes(N, r, kMaxM));
   // sized for the largest range count (the count at one row chunk)
   L.part = take(C > 0 ? 0 : rows * (size_t)xpress::readout_tiles(V, 1) * sizeof(uint2));
@@ -268,10 +275,14 @@ xpress_status xpress_initial_block(const xpress_bf16* base, int64_t base_ld, con
 }
 
 xpress_status xpress_latent_pass(const xpress_weights* w, const int64_t* blk, const int64_t* am1,
-                                 const float* xh, int32_t N, xpress_bf16* lat, void* ws,
-                                 size_t ws_bytes, xpress_stream stream) {
+                                 const float* xh, int32_t N, xpress_bf16* lat,
+                                 uint32_t lat_layout, void* ws, size_t ws_bytes,
+                                 xpress_stream stream) {
   xpress_status st = check_weights(w, false, true, false);
   if (st != XPRESS_OK) return st;
+  st = check_layout(lat_layout);
+  if (st != XPRESS_OK) return st;
+  const bool frag = lat_layout == XPRESS_LAT_FRAGMENTS;
   if (N < 0) return fail(XPRESS_ERR_ARG, "N=%d < 0", N);
   if (N == 0) return XPRESS_OK;
   XP_PTR(blk);
@@ -286,7 +297,8 @@ xpress_status xpress_latent_pass(const xpress_weights* w, const int64_t* blk, co
       return fail(XPRESS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed for N=%d", ws_bytes, need, N);
     XP_TRY(xpress::launch_latent_fused(nullptr, 0, const_cast<int64_t*>(blk), am1, xh, w->w1p,
                                        w->mix_L, w->w_gate, w->w_up, w->w_down, N, w->B, w->r,
-                                       w->M, w->V, lat, static_cast<float*>(ws), nullptr, 0, s),
+                                       w->M, w->V, lat, static_cast<float*>(ws), nullptr, 0, s,
+                                       true, frag),
            "latent");
     return XPRESS_OK;
   }
@@ -295,16 +307,18 @@ xpress_status xpress_latent_pass(const xpress_weights* w, const int64_t* blk, co
     return fail(XPRESS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed for N=%d", ws_bytes, need, N);
   XP_TRY(xpress::launch_latent(nullptr, 0, const_cast<int64_t*>(blk), am1, xh, w->w1, w->in_proj,
                                w->mix_L, w->w_gate, w->w_up, w->w_down, N, w->B, w->r, w->M, w->V,
-                               lat, ws, nullptr, 0, s),
+                               lat, ws, nullptr, 0, s, frag),
          "latent");
   return XPRESS_OK;
 }
 
 xpress_status xpress_readout_argmax(const xpress_weights* w, const xpress_bf16* lat,
-                                    const xpress_bf16* base, int64_t base_ld, int32_t N,
-                                    int64_t* blk, int32_t* changed, void* ws, size_t ws_bytes,
-                                    xpress_stream stream) {
+                                    uint32_t lat_layout, const xpress_bf16* base,
+                                    int64_t base_ld, int32_t N, int64_t* blk, int32_t* changed,
+                                    void* ws, size_t ws_bytes, xpress_stream stream) {
   xpress_status st = check_weights(w, false, false, true);
+  if (st != XPRESS_OK) return st;
+  st = check_layout(lat_layout);
   if (st != XPRESS_OK) return st;
   if (N < 0) return fail(XPRESS_ERR_ARG, "N=%d < 0", N);
   if (N == 0) return XPRESS_OK;
@@ -320,7 +334,8 @@ xpress_status xpress_readout_argmax(const xpress_weights* w, const xpress_bf16* 
     return fail(XPRESS_ERR_WORKSPACE, "workspace %zu bytes < %zu needed for N=%d", ws_bytes, need, N);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   uint2* part = static_cast<uint2*>(ws);
-  XP_TRY(xpress::launch_readout_partial(lat, w->w2, base, base_ld, rows, w->V, w->r, part, nullptr, 0, s),
+  XP_TRY(xpress::launch_readout_partial(lat, w->w2, base, base_ld, rows, w->V, w->r, part, nullptr, 0, s,
+                                        lat_layout == XPRESS_LAT_FRAGMENTS),
          "readout");
   XP_TRY(xpress::launch_argmax_reduce(part, ntiles, rows, w->B, blk, changed, nullptr, 0, s),
          "argmax reduce");
@@ -337,9 +352,12 @@ xpress_status xpress_readout_tiles(int64_t V, int32_t rows, int32_t* ntiles) {
 }
 
 xpress_status xpress_readout_partials(const xpress_weights* w, const xpress_bf16* lat,
-                                      const xpress_bf16* base, int64_t base_ld, int32_t N,
-                                      uint32_t* part, xpress_stream stream) {
+                                      uint32_t lat_layout, const xpress_bf16* base,
+                                      int64_t base_ld, int32_t N, uint32_t* part,
+                                      xpress_stream stream) {
   xpress_status st = check_weights(w, false, false, true);
+  if (st != XPRESS_OK) return st;
+  st = check_layout(lat_layout);
   if (st != XPRESS_OK) return st;
   if (N < 0) return fail(XPRESS_ERR_ARG, "N=%d < 0", N);
   if (N == 0) return XPRESS_OK;
@@ -349,7 +367,8 @@ xpress_status xpress_readout_partials(const xpress_weights* w, const xpress_bf16
   XP_PTR(part);
   XP_TRY(xpress::launch_readout_partial(lat, w->w2, base, base_ld, N * (w->B - 1), w->V, w->r,
                                         reinterpret_cast<uint2*>(part), nullptr, 0,
-                                        reinterpret_cast<hipStream_t>(stream)),
+                                        reinterpret_cast<hipStream_t>(stream),
+                                        lat_layout == XPRESS_LAT_FRAGMENTS),
          "readout");
   return XPRESS_OK;
 }
@@ -491,19 +510,21 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
   uint2* part = at<uint2>(ws, L.part);
   const int ntiles = xpress::readout_tiles(V, rows);
   // Full vocabulary: the argmax reduce of pass p-1 runs inside pass p's first latent kernel (each
-  // block finishes its own rows); only the last pass's reduce is a launch of its own.
+  // block finishes its own rows); only the last pass's reduce is a launch of its own. lat is kept
+  // in the readout's fragment order (coalesced loads of every workgroup's lat fragments).
+  const bool lat_frag = c == 0;
   for (int p = 0; p < K; ++p) {
     const uint2* prev = (c == 0 && p > 0) ? part : nullptr;
     // with candidates, the top-C readout sums the table path's latent shares itself
     if (fused)
       XP_TRY(xpress::launch_latent_fused(prev, ntiles, blk, am1, xh, w->w1p, w->mix_L, w->w_gate,
                                          w->w_up, w->w_down, N, B, r, w->M, V, lat,
-                                         static_cast<float*>(lscr), pf, p, s, c == 0),
+                                         static_cast<float*>(lscr), pf, p, s, c == 0, lat_frag),
              "latent");
     else
       XP_TRY(xpress::launch_latent(prev, ntiles, blk, am1, xh, w->w1, w->in_proj, w->mix_L,
                                    w->w_gate, w->w_up, w->w_down, N, B, r, w->M, V, lat, lscr, pf,
-                                   p, s),
+                                   p, s, lat_frag),
              "latent");
     if (c > 0) {
       XP_TRY(xpress::launch_topc_readout(lat, fused ? static_cast<const float*>(lscr) : nullptr,
@@ -511,7 +532,8 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
                                          nullptr, pf, p, s),
              "top-C readout");
     } else {
-      XP_TRY(xpress::launch_readout_partial(lat, w->w2, base, base_ld, rows, V, r, part, pf, p, s),
+      XP_TRY(xpress::launch_readout_partial(lat, w->w2, base, base_ld, rows, V, r, part, pf, p, s,
+                                            lat_frag),
              "readout");
     }
   }

@@ -70,6 +70,18 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// Element offset of lat[p, c] (readout row p, channel c) in the fragment order that a step's
+// full-vocabulary readout loads with one contiguous 1 KiB read per wave instruction: row tile
+// T = p / 32 holds, for each 16-channel k-step s and lane l = 32*half + p%32, the 8 channels
+// 16s + 8*half .. +7 of row p as one 16-byte chunk at chunk index (T*(R/16) + s)*64 + l -- the
+// B-operand fragment of v_mfma_f32_32x32x16_bf16 that lane l holds for k-step s. A buffer of
+// ceil(rows/32) whole tiles holds it.
+template <int R>
+__device__ __forceinline__ int64_t lat_frag_offset(int p, int c) {
+  const int T = p >> 5, lr = p & 31, q = c >> 3;
+  return ((int64_t)(T * (R / 16) + (q >> 1)) * 64 + (q & 1) * 32 + lr) * 8 + (c & 7);
+}
+
 // Skip test of the fixed-point early exit: pass p >= 1 is skipped once pass p-1 changed nothing.
 // flags == nullptr disables it.
 __device__ __forceinline__ bool pass_skipped(const int32_t* flags, int pass) {

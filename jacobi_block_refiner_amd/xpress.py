@@ -18,6 +18,7 @@ LIB_PATH = PKG / "libxpress.so"
 HEADER = PKG.parent / "include" / "xpress.h"
 
 OK, ERR_ARG, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3
+LAT_ROWS, LAT_FRAGMENTS = 0, 1
 INIT_FROM_BASE = 1
 STOP_AT_FIXED_POINT = 2
 
@@ -64,10 +65,10 @@ def lib() -> ctypes.CDLL:
             "xpress_fold_embedding": [W, P, P],
             "xpress_hidden_cache": [W, P, i32, P, P, sz, P],
             "xpress_initial_block": [P, i64, P, i32, i32, i64, P, P],
-            "xpress_latent_pass": [W, P, P, P, i32, P, P, sz, P],
-            "xpress_readout_argmax": [W, P, P, i64, i32, P, P, P, sz, P],
+            "xpress_latent_pass": [W, P, P, P, i32, P, ctypes.c_uint32, P, sz, P],
+            "xpress_readout_argmax": [W, P, ctypes.c_uint32, P, i64, i32, P, P, P, sz, P],
             "xpress_readout_tiles": [i64, i32, ctypes.POINTER(i32)],
-            "xpress_readout_partials": [W, P, P, i64, i32, P, P],
+            "xpress_readout_partials": [W, P, ctypes.c_uint32, P, i64, i32, P, P],
             "xpress_argmax_reduce": [P, i32, i32, i32, P, P, P],
             "xpress_topc_prepare": [W, P, i64, i32, i32, P, P, P, P, sz, P],
             "xpress_readout_argmax_topc": [P, P, P, P, i32, i32, i32, i32, P, P, P],
@@ -204,22 +205,31 @@ def initial_block(base: torch.Tensor, anchor: torch.Tensor, blk: torch.Tensor) -
     return blk
 
 
-def latent_pass(w: Weights, blk, am1, xh, lat, ws: torch.Tensor) -> torch.Tensor:
+def lat_buffer(N: int, B: int, r: int, layout: int = LAT_ROWS, device="cuda") -> torch.Tensor:
+    """A latent buffer for N blocks in `layout` (fragment order: whole 32-row tiles)."""
+    rows = N * (B - 1)
+    if layout == LAT_FRAGMENTS:
+        rows = (rows + 31) // 32 * 32
+    return torch.empty(rows, r, dtype=torch.bfloat16, device=device)
+
+
+def latent_pass(w: Weights, blk, am1, xh, lat, ws: torch.Tensor, layout: int = LAT_ROWS) -> torch.Tensor:
     s = w.struct()
     N = blk.shape[0]
     _check(lib().xpress_latent_pass(ctypes.byref(s), _ptr(blk), _ptr(am1), _ptr(xh), N,
-                                    _ptr(lat), _ptr(ws), ws.numel() * ws.element_size(),
+                                    _ptr(lat), layout, _ptr(ws), ws.numel() * ws.element_size(),
                                     _stream()))
     return lat
 
 
-def readout_argmax(w: Weights, lat, base, blk, ws, changed=None) -> torch.Tensor:
+def readout_argmax(w: Weights, lat, base, blk, ws, changed=None, layout: int = LAT_ROWS) -> torch.Tensor:
     s = w.struct()
     _bf16(base, "base")
     assert base.stride(1) == 1
     N = blk.shape[0]
-    _check(lib().xpress_readout_argmax(ctypes.byref(s), _ptr(lat), ctypes.c_void_p(base.data_ptr()),
-                                       base.stride(0), N, _ptr(blk), _ptr(changed), _ptr(ws),
+    _check(lib().xpress_readout_argmax(ctypes.byref(s), _ptr(lat), layout,
+                                       ctypes.c_void_p(base.data_ptr()), base.stride(0), N,
+                                       _ptr(blk), _ptr(changed), _ptr(ws),
                                        ws.numel() * ws.element_size(), _stream()))
     return blk
 
@@ -230,15 +240,16 @@ def readout_tiles(V: int, rows: int) -> int:
     return int(out.value)
 
 
-def readout_partials(w: Weights, lat, base, part: torch.Tensor) -> torch.Tensor:
+def readout_partials(w: Weights, lat, base, part: torch.Tensor, layout: int = LAT_ROWS) -> torch.Tensor:
     """part: int32/uint32-compatible tensor [ntiles, rows, 2] (value bits, id), range-major."""
     s = w.struct()
     _bf16(base, "base")
     assert base.stride(1) == 1
-    rows = lat.numel() // lat.shape[-1]
+    rows = part.shape[1]
     N = rows // (w.dims["B"] - 1)
-    _check(lib().xpress_readout_partials(ctypes.byref(s), _ptr(lat), ctypes.c_void_p(base.data_ptr()),
-                                         base.stride(0), N, _ptr(part), _stream()))
+    _check(lib().xpress_readout_partials(ctypes.byref(s), _ptr(lat), layout,
+                                         ctypes.c_void_p(base.data_ptr()), base.stride(0), N,
+                                         _ptr(part), _stream()))
     return part
 
 

@@ -113,3 +113,22 @@ def end_to_end_ok(got: np.ndarray, want: np.ndarray, hist_gap: np.ndarray,
     allowed[:, 1:] = np.logical_or.accumulate(near, axis=1)
     bad = (got != want) & ~allowed
     return int(bad.sum()), int((hist_gap < near_tie).sum())
+
+
+def lat_pack_fragments(lat: np.ndarray) -> np.ndarray:
+    """Row-major lat [rows, r] -> the readout's fragment order (XPRESS_LAT_FRAGMENTS), as a
+    [ceil(rows/32)*32, r] array (rows past the end are zero): tile T, 16-channel group s, lane
+    l = 32*h + i holds channels 16s + 8h .. +7 of row 32T + i. A pure permutation of the values."""
+    rows, r = lat.shape
+    nt = (rows + 31) // 32
+    pad = np.zeros((nt * 32, r), dtype=lat.dtype)
+    pad[:rows] = lat
+    # [T, i, s, h, e] -> [T, s, h, i, e]
+    return np.ascontiguousarray(pad.reshape(nt, 32, r // 16, 2, 8).transpose(0, 2, 3, 1, 4)).reshape(nt * 32, r)
+
+
+def lat_unpack_fragments(frag: np.ndarray, rows: int) -> np.ndarray:
+    """Inverse of lat_pack_fragments: the first `rows` rows, row-major."""
+    n32, r = frag.shape
+    nt = n32 // 32
+    return np.ascontiguousarray(frag.reshape(nt, r // 16, 2, 32, 8).transpose(0, 3, 1, 2, 4)).reshape(nt * 32, r)[:rows]

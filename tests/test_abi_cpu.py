@@ -42,7 +42,7 @@ def test_bad_shapes_are_rejected(B, r, V):
 
 def test_null_weights_and_pointers_are_rejected():
     L = xpress.lib()
-    st = L.xpress_latent_pass(None, None, None, None, 4, None, None, 0, None)
+    st = L.xpress_latent_pass(None, None, None, None, 4, None, 0, None, 0, None)
     assert st == xpress.ERR_ARG and b"NULL" in L.xpress_last_error()
     w = xpress._Weights(B=16, r=256, H=4096, M=512, V=151936)
     st = L.xpress_jacobi_step(ctypes.byref(w), None, None, 151936, None, None, 4, 15, 0, 1, None,
@@ -58,7 +58,7 @@ def test_n_zero_is_a_noop_and_unknown_flags_are_rejected():
     w = xpress._Weights(B=16, r=256, H=4096, M=512, V=151936, w1=fake, down_h=fake,
                         down_g=fake, in_proj=fake, mix_L=fake, w_gate=fake, w_up=fake,
                         w_down=fake, w2=fake)
-    assert L.xpress_latent_pass(ctypes.byref(w), fake, fake, fake, 0, fake, fake, 0, None) == xpress.OK
+    assert L.xpress_latent_pass(ctypes.byref(w), fake, fake, fake, 0, fake, 0, fake, 0, None) == xpress.OK
     st = L.xpress_jacobi_step(ctypes.byref(w), fake, fake, 151936, fake, fake, 4, 15, 0, 0x10,
                               fake, None, fake, 1 << 30, None)
     assert st == xpress.ERR_ARG and b"flag" in L.xpress_last_error()
@@ -70,14 +70,17 @@ def test_small_workspace_and_bad_stride_are_rejected():
     w = xpress._Weights(B=16, r=256, H=4096, M=512, V=151936, w1=fake, down_h=fake,
                         down_g=fake, in_proj=fake, mix_L=fake, w_gate=fake, w_up=fake,
                         w_down=fake, w2=fake)
-    st = L.xpress_readout_argmax(ctypes.byref(w), fake, fake, 151936, 4, fake, None, fake, 16,
+    st = L.xpress_readout_argmax(ctypes.byref(w), fake, 0, fake, 151936, 4, fake, None, fake, 16,
                                  None)
     assert st == xpress.ERR_WORKSPACE
-    st = L.xpress_readout_argmax(ctypes.byref(w), fake, fake, 151937, 4, fake, None, fake,
+    st = L.xpress_readout_argmax(ctypes.byref(w), fake, 0, fake, 151937, 4, fake, None, fake,
                                  1 << 30, None)
     assert st == xpress.ERR_ARG
+    st = L.xpress_readout_argmax(ctypes.byref(w), fake, 2, fake, 151936, 4, fake, None, fake,
+                                 1 << 30, None)
+    assert st == xpress.ERR_ARG and b"lat_layout" in L.xpress_last_error()
     misaligned = ctypes.c_void_p((1 << 20) + 2)
-    st = L.xpress_readout_argmax(ctypes.byref(w), misaligned, fake, 151936, 4, fake, None, fake,
+    st = L.xpress_readout_argmax(ctypes.byref(w), misaligned, 0, fake, 151936, 4, fake, None, fake,
                                  1 << 30, None)
     assert st == xpress.ERR_ARG and b"aligned" in L.xpress_last_error()
 
@@ -96,12 +99,14 @@ def test_fold_embedding_and_table_arguments_are_checked():
     assert L.xpress_fold_embedding(ctypes.byref(bad), fake, None) == xpress.ERR_ARG
     # a misaligned projected table is rejected before anything is enqueued
     w.w1p = (1 << 20) + 8
-    st = L.xpress_latent_pass(ctypes.byref(w), fake, fake, fake, 4, fake, fake, 1 << 30, None)
+    st = L.xpress_latent_pass(ctypes.byref(w), fake, fake, fake, 4, fake, 0, fake, 1 << 30, None)
     assert st == xpress.ERR_ARG and b"w1p" in L.xpress_last_error()
     # with the table, the latent scratch holds the M/64 slice shares of every block
     w.w1p = 1 << 20
-    st = L.xpress_latent_pass(ctypes.byref(w), fake, fake, fake, 4, fake, fake, 1024, None)
+    st = L.xpress_latent_pass(ctypes.byref(w), fake, fake, fake, 4, fake, 0, fake, 1024, None)
     assert st == xpress.ERR_WORKSPACE
+    st = L.xpress_latent_pass(ctypes.byref(w), fake, fake, fake, 4, fake, 7, fake, 1 << 30, None)
+    assert st == xpress.ERR_ARG and b"lat_layout" in L.xpress_last_error()
 
 
 def test_workspace_for_n_max_fits_every_smaller_n():

@@ -9,7 +9,8 @@ import torch
 from jacobi_block_refiner_amd import synth, upload, xpress
 from oracle import oracle as O
 from tests.gpu_helpers import (LAT_RTOL, NEAR_TIE, Dev, compare_tokens, draft_rows, end_to_end_ok,
-                               lat_rel_err, lat_to_f64, log, oracle_mixer, strong)
+                               lat_pack_fragments, lat_rel_err, lat_to_f64,
+                               lat_unpack_fragments, log, oracle_mixer, strong)
 
 pytestmark = pytest.mark.gpu
 
@@ -83,9 +84,11 @@ def test_initial_block_exact(V):
 @pytest.mark.parametrize("r,V,N", [(64, 5003, 3), (256, 5003, 5), (256, 8192, 3), (128, 700, 2),
                                    (256, 151936, 1), (128, 60001, 2), (64, 40000, 1),
                                    (256, 5003, 20), (256, 8192, 35), (128, 3001, 35)])
-def test_readout_argmax_dyadic_exact(r, V, N):
+@pytest.mark.parametrize("layout", ["rows", "fragments"])
+def test_readout_argmax_dyadic_exact(r, V, N, layout):
     """Every fp32 partial sum is exact, so the GPU must match the oracle on every row, ties
-    included (lowest id), with no near-tie exemption."""
+    included (lowest id), with no near-tie exemption. lat is given row-major or in the fragment
+    order a step keeps it in (a permutation of the same values)."""
     B = 16
     lat, w2, base = _readout_case(2, N, B, r, V)
     w = _weights_with(w2, r, B, V)
@@ -94,8 +97,12 @@ def test_readout_argmax_dyadic_exact(r, V, N):
     blk = upload.tokens(blk0)
     changed = torch.zeros(1, dtype=torch.int32, device="cuda")
     ws = xpress.alloc_workspace(N, B, r, V, 0, 1)
-    log(f"readout dyadic r={r} V={V} N={N}")
-    xpress.readout_argmax(w, upload.bf16_tensor(lat), upload.base_logits(base), blk, ws, changed)
+    log(f"readout dyadic r={r} V={V} N={N} lat {layout}")
+    if layout == "rows":
+        lat_d, lay = upload.bf16_tensor(lat), xpress.LAT_ROWS
+    else:
+        lat_d, lay = upload.bf16_tensor(lat_pack_fragments(lat)), xpress.LAT_FRAGMENTS
+    xpress.readout_argmax(w, lat_d, upload.base_logits(base), blk, ws, changed, layout=lay)
     torch.cuda.synchronize()
     best, gap, _ = O.readout_argmax(lat, w2, base)
     got = blk.cpu().numpy()
@@ -267,6 +274,26 @@ def test_latent_parity(wl_id, N, over, path):
     err = lat_rel_err(lat_to_f64(lat), want)
     log(f"latent {path} wl{wl_id} N={N} {over}: row-relative error {err:.2e}")
     assert err < LAT_RTOL
+
+
+@pytest.mark.parametrize("path", ["table", "project"])
+@pytest.mark.parametrize("N,over", [(3, {"V": 4096}), (37, {"V": 3000}), (130, {"V": 3000})])
+def test_latent_fragment_order_is_the_same_values(path, N, over):
+    """The latent written in the readout's fragment order holds exactly the values of the
+    row-major latent, permuted (the order a step keeps lat in); 3 and 37 blocks leave a partial
+    last 32-row tile, 130 blocks run the three-kernel path."""
+    inp, xh = _latent_case(3 if N == 3 else 1, N, **({} if N == 3 else {"B": 16, "r": 256, "M": 512}), **over)
+    d = _dev(inp, path)
+    wl = inp.wl
+    blk, xh_d = upload.tokens(inp.blk), torch.from_numpy(xh).cuda()
+    lat_r = xpress.lat_buffer(N, wl.B, wl.r, xpress.LAT_ROWS)
+    lat_f = xpress.lat_buffer(N, wl.B, wl.r, xpress.LAT_FRAGMENTS)
+    xpress.latent_pass(d.w, blk, d.am1, xh_d, lat_r, d.ws())
+    xpress.latent_pass(d.w, blk, d.am1, xh_d, lat_f, d.ws(), layout=xpress.LAT_FRAGMENTS)
+    torch.cuda.synchronize()
+    rows = N * (wl.B - 1)
+    got = lat_unpack_fragments(lat_f.view(torch.int16).cpu().numpy(), rows)
+    assert np.array_equal(got, lat_r.view(torch.int16).cpu().numpy())
 
 
 @pytest.mark.parametrize("path", ["table", "project"])
