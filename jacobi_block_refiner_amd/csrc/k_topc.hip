@@ -186,7 +186,22 @@ __device__ void select_row_exact(const uint16_t* __restrict__ row, int64_t V, in
 // runs on the buffer: threshold by radix select, the boundary ties by id rank, and each winner
 // written at its rank by id (ascending id order).
 constexpr int kBuf = 2048;
-constexpr int kEq = 512;
+
+// hist[bin] += 1 for every lane with `valid`, one LDS atomic per distinct bin in the wave: the
+// lanes of the wave's smallest pending lane's bin are counted together (ballot) and leave the
+// loop. Keys near the top of a row share a handful of high bytes, and plain per-lane atomics on
+// the same bin serialize; the loop runs once per distinct bin (wave-uniform).
+__device__ __forceinline__ void hist_add_aggregated(uint32_t* hist, int bin, bool valid) {
+  const int lane = threadIdx.x & 63;
+  uint64_t pending = __ballot(valid);
+  while (pending) {
+    const int leader = __ffsll((unsigned long long)pending) - 1;
+    const int lb = __shfl(bin, leader);
+    const uint64_t same = __ballot(bin == lb) & pending;
+    if (lane == leader) atomicAdd(&hist[lb], (uint32_t)__popcll(same));
+    pending &= ~same;
+  }
+}
 __device__ __forceinline__ uint32_t radix_kth(const uint32_t* keys, int n, int k, uint32_t* s_hist,
                                               uint32_t* s_par, uint32_t* above_out) {
   // keys: 17-bit (key + 1, 0 = empty); returns the k-th largest non-empty key (as key + 1) and
@@ -198,9 +213,9 @@ __device__ __forceinline__ uint32_t radix_kth(const uint32_t* keys, int n, int k
   __shared__ int s_tmp[4];
   s_hist[tid] = 0;
   __syncthreads();
-  for (int j = tid; j < n; j += 256) {
-    const uint32_t k1 = keys[j];
-    if (k1) atomicAdd(&s_hist[(k1 - 1) >> 8], 1u);
+  for (int j0 = 0; j0 < n; j0 += 256) {  // uniform trip count (n is a multiple of 256)
+    const uint32_t k1 = keys[j0 + tid];
+    hist_add_aggregated(s_hist, (int)((k1 - 1) >> 8) & 255, k1 != 0);
   }
   __syncthreads();
   int total;
@@ -249,11 +264,9 @@ __device__ __forceinline__ void topc_select_row(int p, const uint16_t* __restric
   __shared__ uint32_t s_par[4];
   __shared__ uint32_t s_key[kBuf];  // key + 1 (0: empty)
   __shared__ int s_id[kBuf];
-  __shared__ int s_eq[kEq];         // ids of the boundary ties
-  __shared__ __align__(16) int s_sel[1024];  // ids of the winners
-  __shared__ int s_cnt[4];
-  constexpr int kHC = 1024;         // chunk-list capacity per wave
-  __shared__ int s_hc[4][kHC];      // chunks whose maximum can hold an answer, per wave
+  __shared__ uint16_t s_bits[kBuf];  // the buffered values' bf16 bits
+  constexpr int kHC = 4096;          // chunk-list capacity
+  __shared__ int s_hc[kHC];          // chunks whose maximum can hold an answer, ascending
   const int tid = threadIdx.x, lane = tid & 63;
   const uint16_t* row = base + (int64_t)p * ld;
   int64_t* out_id = cand + (int64_t)p * c;
@@ -351,180 +364,129 @@ __device__ __forceinline__ void topc_select_row(int p, const uint16_t* __restric
   }
   for (int j = tid; j < kBuf; j += 256) s_key[j] = 0;
   __syncthreads();
-  // 3. every element with value >= v0 into the buffer. Each wave appends to its own quarter of
-  // it (kBuf / 4 slots) with a wave-uniform running count: the compare's lane mask is the ballot,
-  // so no atomics; unused slots stay empty (key 0). A quarter that would overflow sends the row to
-  // the exact path.
-  constexpr int kSeg = kBuf / 4;
-  const int wave = tid >> 6;
-  int wcnt = 0;  // wave-uniform
-  // With chunk maxima: (3a) each wave lists the chunks whose maximum is >= v0 (8 maxima per
-  // 16-byte read), then (3b) reads only those chunks, one per lane, and appends their elements
-  // >= v0 as below. A list that would overflow sends the row to the full pass instead.
-  bool full_pass = cmax_row == nullptr;
-  if (!full_pass) {
-    int hc = 0;  // wave-uniform (lane 0, which runs every iteration any lane runs, holds it)
-    const uint4* cm4 = reinterpret_cast<const uint4*>(cmax_row);
-    const int64_t n8 = nchunk8 / 8;
-    for (int64_t g0 = tid; g0 < n8; g0 += 256 * kLB) {
-      uint4 m8[kLB];
-#pragma unroll
-      for (int u = 0; u < kLB; ++u) {
-        const int64_t g = g0 + 256 * u;
-        m8[u] = g < n8 ? cm4[g] : make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
-      }
-#pragma unroll
-      for (int u = 0; u < kLB; ++u) {
-        const int64_t g = g0 + 256 * u;
-        const uint32_t w[4] = {m8[u].x, m8[u].y, m8[u].z, m8[u].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t b = (e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16);
-          const bool hit = __uint_as_float(b) >= v0;
-          const uint64_t m = __ballot(hit);
-          if (m) {
-            const int pos = hc + __popcll(m & ((1ull << lane) - 1));
-            if (hit && pos < kHC) s_hc[wave][pos] = (int)(g * 8 + e);
-            hc += __popcll(m);
-          }
-        }
-      }
-    }
-    if (lane == 0) s_cnt[wave] = hc;
-    __syncthreads();
-    hc = s_cnt[wave];  // every lane: the wave's count
-    full_pass = max(max(s_cnt[0], s_cnt[1]), max(s_cnt[2], s_cnt[3])) > kHC;  // uniform
-    if (!full_pass) {
-      for (int i0 = 0; i0 < hc; i0 += 64) {  // wave-uniform bound
-        const bool has = i0 + lane < hc;
-        const int64_t q = has ? s_hc[wave][i0 + lane] : nchunk;  // past the row: all -inf
-        float x[8];
-        widen(q, has ? row4[q] : make_uint4(0, 0, 0, 0), x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bool hit = x[e] >= v0;
-          const uint64_t m = __ballot(hit);
-          if (m) {
-            const int pos = wcnt + __popcll(m & ((1ull << lane) - 1));
-            if (hit && pos < kSeg) {
-              s_key[wave * kSeg + pos] = key1_of(x[e]);
-              s_id[wave * kSeg + pos] = (int)(q * 8 + e);
-            }
-            wcnt += __popcll(m);
-          }
-        }
-      }
-    }
-    __syncthreads();  // s_cnt is reused below
-  }
-  if (full_pass)
-  for (int64_t q0 = tid; q0 < nchunk; q0 += 256 * kLB) {
-    uint4 raw[kLB];
-    load_batch(q0, raw);
-#pragma unroll
-    for (int u = 0; u < kLB; ++u) {
-      const int64_t q = q0 + 256 * u;
-      float x[8];
-      widen(q, raw[u], x);  // past the row: -inf, no hit
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const bool hit = x[e] >= v0;
-        const uint64_t m = __ballot(hit);
-        if (m) {
-          const int pos = wcnt + __popcll(m & ((1ull << lane) - 1));
-          if (hit && pos < kSeg) {
-            s_key[wave * kSeg + pos] = key1_of(x[e]);
-            s_id[wave * kSeg + pos] = (int)(q * 8 + e);
-          }
-          wcnt += __popcll(m);
-        }
-      }
-    }
-  }
-  if (lane == 0) s_cnt[wave] = wcnt;
-  __syncthreads();
-  const int wmax = max(max(s_cnt[0], s_cnt[1]), max(s_cnt[2], s_cnt[3]));
-  const int wsum = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
-  // A quarter that overflowed, or fewer than c buffered elements (a row with fewer than c finite
-  // values: -inf and NaN never pass the compare), goes to the exact path, which orders every bit
-  // pattern by its key, so c in-range ids are always written.
-  if (wmax > kSeg || wsum < c) {  // uniform
+  // 3. Every element with value >= v0 into the buffer, in ascending id order; without chunk
+  // maxima (no workspace) the exact whole-row path runs instead.
+  if (cmax_row == nullptr) {
     select_row_exact(row, V, c, out_id, out_b, s_hist, s_tmp, s_par);
     return;
   }
-  // 4. exact selection on the buffer: threshold T (c-th largest), every key above it, and the
-  // need_eq lowest ids among the keys equal to it (the boundary ties, compacted first)
+  // 3a. The chunks whose maximum reaches v0, listed in ascending order: in round u, thread tid
+  // takes the 8 chunk maxima of group g0 + 256u + tid (the kLB groups' 16-byte reads are issued
+  // first); a block-wide exclusive scan of the hit counts places its hits after those of the
+  // lower groups. A list that would overflow sends the row to the exact path.
+  const int64_t n8 = nchunk8 / 8;
+  const uint4* cm4 = reinterpret_cast<const uint4*>(cmax_row);
+  int nhc = 0;  // uniform
+  for (int64_t g0 = 0; g0 < n8; g0 += 256 * kLB) {
+    uint4 m8[kLB];
+#pragma unroll
+    for (int u = 0; u < kLB; ++u) {
+      const int64_t g = g0 + 256 * u + tid;
+      m8[u] = g < n8 ? cm4[g] : make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
+    }
+#pragma unroll
+    for (int u = 0; u < kLB; ++u) {
+      if (g0 + 256 * u >= n8) break;  // uniform
+      const int64_t g = g0 + 256 * u + tid;
+      const uint32_t w[4] = {m8[u].x, m8[u].y, m8[u].z, m8[u].w};
+      uint32_t hm = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t b = (e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16);
+        hm |= (__uint_as_float(b) >= v0 ? 1u : 0u) << e;
+      }
+      const int cnt = __popc(hm);
+      int tot;
+      int pos = nhc + block_exclusive_scan(cnt, s_tmp, tot);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if ((hm >> e) & 1u) {
+          if (pos < kHC) s_hc[pos] = (int)(g * 8 + e);
+          ++pos;
+        }
+      nhc += tot;
+    }
+  }
+  if (nhc > kHC) {  // uniform
+    select_row_exact(row, V, c, out_id, out_b, s_hist, s_tmp, s_par);
+    return;
+  }
+  __syncthreads();  // the list is complete
+  // 3b. The listed chunks' elements >= v0 appended in list order (ascending ids): per round,
+  // thread tid reads chunk tid of the round (up to four rounds' reads issued together), and a
+  // block-wide scan places its hits. More than kBuf of them, or fewer than c, sends the row to the
+  // exact path.
+  int nbuf = 0;  // uniform
+  for (int i0 = 0; i0 < nhc; i0 += 4 * 256) {
+    uint4 raw[4];
+    int64_t qs[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + 256 * u + tid;
+      qs[u] = i < nhc ? s_hc[i] : nchunk;  // past the list: a chunk past the row, all -inf
+      raw[u] = i < nhc ? row4[qs[u]] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (i0 + 256 * u >= nhc) break;  // uniform
+      float x[8];
+      widen(qs[u], raw[u], x);
+      uint32_t hm = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hm |= (x[e] >= v0 ? 1u : 0u) << e;
+      int tot;
+      int pos = nbuf + block_exclusive_scan(__popc(hm), s_tmp, tot);
+      const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if ((hm >> e) & 1u) {
+          if (pos < kBuf) {
+            s_key[pos] = key1_of(x[e]);
+            s_id[pos] = (int)(qs[u] * 8 + e);
+            s_bits[pos] = (uint16_t)((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
+          }
+          ++pos;
+        }
+      nbuf += tot;
+    }
+  }
+  // -inf and NaN never pass the compare, so a row with fewer than c finite values has fewer than
+  // c buffered elements; the exact path orders every bit pattern by its key
+  if (nbuf > kBuf || nbuf < c) {  // uniform
+    select_row_exact(row, V, c, out_id, out_b, s_hist, s_tmp, s_par);
+    return;
+  }
+  __syncthreads();
+  // 4. The threshold T (c-th largest key of the buffer; empty slots are 0), then one ordered
+  // compaction: thread tid owns buffer slots 8*tid .. 8*tid+7; every key above T is taken, and of
+  // the keys equal to T the first need_eq in buffer order, the lowest ids. Written in buffer order:
+  // ascending ids.
   const uint32_t T = radix_kth(s_key, kBuf, c, s_hist, s_par, &above);
   const int need_eq = c - (int)above;
+  uint32_t k8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) k8[e] = s_key[8 * tid + e];
   int n_eq = 0;
-  for (int j = tid; j < kBuf; j += 256) n_eq += s_key[j] == T;
-  int eq_total;
-  int epos = block_exclusive_scan(n_eq, s_tmp, eq_total);
-  for (int j = tid; j < kBuf; j += 256)
-    if (s_key[j] == T) {
-      if (epos < kEq) s_eq[epos] = s_id[j];
-      ++epos;
-    }
-  __syncthreads();
-  int n_sel = 0;
-  for (int j = tid; j < kBuf; j += 256) {
-    const uint32_t k1 = s_key[j];
-    bool sel = k1 > T;
-    if (k1 == T) {
-      const int id = s_id[j];
-      int lower = 0;
-      if (eq_total <= kEq) {
-        for (int i2 = 0; i2 < eq_total; ++i2) lower += s_eq[i2] < id;
-      } else {
-        for (int i2 = 0; i2 < kBuf; ++i2) lower += s_key[i2] == T && s_id[i2] < id;
-      }
-      sel = lower < need_eq;
-    }
-    n_sel += sel;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) n_eq += k8[e] == T;
+  int eq_tot;
+  int eq_rank = block_exclusive_scan(n_eq, s_tmp, eq_tot);
+  uint32_t sm = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    bool take = k8[e] > T;
+    if (k8[e] == T) take = eq_rank++ < need_eq;
+    sm |= (take ? 1u : 0u) << e;
   }
-  int sel_total;
-  int spos = block_exclusive_scan(n_sel, s_tmp, sel_total);
-  for (int j = tid; j < kBuf; j += 256) {
-    const uint32_t k1 = s_key[j];
-    bool sel = k1 > T;
-    if (k1 == T) {
-      const int id = s_id[j];
-      int lower = 0;
-      if (eq_total <= kEq) {
-        for (int i2 = 0; i2 < eq_total; ++i2) lower += s_eq[i2] < id;
-      } else {
-        for (int i2 = 0; i2 < kBuf; ++i2) lower += s_key[i2] == T && s_id[i2] < id;
-      }
-      sel = lower < need_eq;
+  int sel_tot;
+  int pos = block_exclusive_scan(__popc(sm), s_tmp, sel_tot);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if ((sm >> e) & 1u) {
+      out_id[pos] = s_id[8 * tid + e];
+      out_b[pos] = s_bits[8 * tid + e];
+      ++pos;
     }
-    if (sel) s_sel[spos++] = s_id[j];
-  }
-  __syncthreads();
-  // 5. the winners in ascending id order: a bitonic sort of s_sel in LDS, padded to a power of
-  // two with INT_MAX (the winners' ids are distinct)
-  int P = 1;
-  while (P < c) P <<= 1;
-  for (int j = c + tid; j < P; j += 256) s_sel[j] = INT_MAX;
-  __syncthreads();
-  for (int k = 2; k <= P; k <<= 1)
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < P; i += 256) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const int a = s_sel[i], b = s_sel[ixj];
-          if ((a > b) == ((i & k) == 0)) {
-            s_sel[i] = b;
-            s_sel[ixj] = a;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  for (int k = tid; k < c; k += 256) {
-    const int id = s_sel[k];
-    out_id[k] = id;
-    out_b[k] = row[id];
-  }
 }
 
 // Draft row p, by one workgroup: the row's candidate set; with blk given, also the row's starting
