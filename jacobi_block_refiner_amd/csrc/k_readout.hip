@@ -49,16 +49,6 @@ constexpr int kMaxRanges = 256;     // vocabulary ranges per row chunk (partials
 // its lanes fetch whichever global chunks belong there.
 __device__ __forceinline__ int w2_row_id(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
 
-// One 1 KiB copy: this lane's 16 bytes at gbase + off (a scalar base pointer and a per-lane
-// 32-bit byte offset) to LDS byte address lds_base + 16 * lane. Written as inline assembly so
-// the compiler's wait-count bookkeeping stays out of it (the kernel waits for the copies itself,
-// with vmcnt, before the barrier that publishes a stage).
-__device__ __forceinline__ void lds_copy16(const void* gbase, uint32_t off, uint32_t lds_base) {
-  // one wait state between the M0 write and the copy that reads it
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds_base), "v"(off), "s"(gbase) : "memory");
-}
-
 template <int R, int kNW, int RW, int NS, int TR>
 __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
     const uint16_t* __restrict__ lat, const uint16_t* __restrict__ w2,

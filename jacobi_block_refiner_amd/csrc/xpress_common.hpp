@@ -82,6 +82,17 @@ __device__ __forceinline__ int64_t lat_frag_offset(int p, int c) {
   return ((int64_t)(T * (R / 16) + (q >> 1)) * 64 + (q & 1) * 32 + lr) * 8 + (c & 7);
 }
 
+// One 1 KiB copy from global memory straight into LDS (global_load_lds_dwordx4: no registers):
+// this lane's 16 bytes at gbase + off (a scalar base pointer and a per-lane 32-bit byte offset)
+// to LDS byte address lds_base + 16 * lane. Written as inline assembly so the compiler's
+// wait-count bookkeeping stays out of it: the caller waits for the copies itself, with vmcnt,
+// before the barrier that publishes them.
+__device__ __forceinline__ void lds_copy16(const void* gbase, uint32_t off, uint32_t lds_base) {
+  // one wait state between the M0 write and the copy that reads it
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_base), "v"(off), "s"(gbase) : "memory", "m0");
+}
+
 // Skip test of the fixed-point early exit: pass p >= 1 is skipped once pass p-1 changed nothing.
 // flags == nullptr disables it.
 __device__ __forceinline__ bool pass_skipped(const int32_t* flags, int pass) {
