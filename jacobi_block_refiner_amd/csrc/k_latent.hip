@@ -107,8 +107,10 @@ __global__ __launch_bounds__(256) void latent_mix_kernel(
     float* __restrict__ u32, uint16_t* __restrict__ u16, int32_t* __restrict__ flags, int pass) {
   // fused: runs when the previous pass ran; plain: when this pass runs
   if (part ? pass_skipped(flags, pass - 1) : pass_skipped(flags, pass)) return;
+  constexpr int EP = R + 8;  // bf16 row pitch of s_e (a 16-byte pad per row)
   __shared__ int64_t s_tok[16];
   __shared__ float s_x[16][65];
+  __shared__ __align__(16) uint16_t s_e[16][EP];
   const int n = blockIdx.x, c0 = blockIdx.y * 64, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
 
@@ -134,21 +136,33 @@ __global__ __launch_bounds__(256) void latent_mix_kernel(
   __syncthreads();
 
   // steps 1-2: x[slot, c] = xh[slot, c] + sum_k P_e[c, k] w1[tok(slot), k]; wave w computes the
-  // 16 x 16 tile of channels c0 + 16w .. +15 (A: the 16 slots' embeddings, B: P_e rows)
+  // 16 x 16 tile of channels c0 + 16w .. +15 (A: the 16 slots' embeddings, B: P_e rows). The 16
+  // embedding rows are read once per workgroup into LDS (every wave multiplies all of them).
   {
-    const int64_t tok = l16 < B ? s_tok[l16] : -1;
-    const bool live = tok >= 0 && tok < V;
-    const uint4* erow = reinterpret_cast<const uint4*>(w1 + (live ? tok : 0) * R);
+    constexpr int RC = R / 8, NCH = 16 * RC, PER = (NCH + 255) / 256;
+    uint4 ev[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = min(tid + 256 * i, NCH - 1), slot = idx / RC;
+      const int64_t tok = slot < B ? s_tok[slot] : -1;
+      const bool live = tok >= 0 && tok < V;  // slots past B and ids outside [0, V): zero
+      ev[i] = *reinterpret_cast<const uint4*>(w1 + (live ? tok : 0) * R + 8 * (idx % RC));
+      if (!live) ev[i] = make_uint4(0, 0, 0, 0);
+    }
     const int c = c0 + 16 * wave + l16;
     const uint4* prow = reinterpret_cast<const uint4*>(in_proj + (int64_t)c * 3 * R + 2 * R);
     bf16x8 a[R / 32], b[R / 32];
 #pragma unroll
-    for (int s2 = 0; s2 < R / 32; ++s2) {
-      uint4 e = erow[4 * s2 + q4];
-      if (!live) e = make_uint4(0, 0, 0, 0);
-      a[s2] = as_bf16x8(e);
-      b[s2] = as_bf16x8(prow[4 * s2 + q4]);
+    for (int s2 = 0; s2 < R / 32; ++s2) b[s2] = as_bf16x8(prow[4 * s2 + q4]);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + 256 * i;
+      if (idx < NCH) *reinterpret_cast<uint4*>(&s_e[idx / RC][8 * (idx % RC)]) = ev[i];
     }
+    __syncthreads();
+#pragma unroll
+    for (int s2 = 0; s2 < R / 32; ++s2)
+      a[s2] = as_bf16x8(*reinterpret_cast<const uint4*>(&s_e[l16][32 * s2 + 8 * q4]));
     float h[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -184,14 +198,41 @@ __global__ __launch_bounds__(256) void latent_mix_kernel(
   }
 }
 
+// Rows r0 .. r0+nr-1 of a bf16 matrix with `ld` elements per row, columns k0 .. k0+KW-1, copied
+// into LDS rows of pitch P elements (a 16-byte pad per row keeps the 16 rows of an MFMA fragment
+// read on distinct banks). Rows past nrows repeat the last one (their results are not stored).
+// Called by all 256 threads; the caller synchronises before reading.
+template <int NR, int KW, int P>
+__device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ src, int64_t ld, int r0,
+                                           int nrows, int k0, uint16_t (*dst)[P]) {
+  constexpr int RC = KW / 8;        // 16-byte chunks per row
+  constexpr int NCH = NR * RC;
+  constexpr int PER = (NCH + 255) / 256;
+  uint4 v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {  // all loads before any store
+    const int idx = min((int)threadIdx.x + 256 * i, NCH - 1);
+    const int r = min(r0 + idx / RC, nrows - 1);
+    v[i] = *reinterpret_cast<const uint4*>(src + (int64_t)r * ld + k0 + 8 * (idx % RC));
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int idx = (int)threadIdx.x + 256 * i;
+    if (idx < NCH) *reinterpret_cast<uint4*>(&dst[idx / RC][8 * (idx % RC)]) = v[i];
+  }
+}
+
 // Step 4 for rows r0..r0+16*G-1 (whole blocks, 16 rows each) and hidden units h0..h0+63; wave w
-// owns units h0 + 16w .. +15.
+// owns units h0 + 16w .. +15. The rows of u are read once per workgroup into LDS (every wave
+// multiplies all of them) and each wave keeps its own units' gate and up rows in registers.
 template <int R, int G>
 __global__ __launch_bounds__(256) void latent_gate_kernel(
     const uint16_t* __restrict__ u16, const uint16_t* __restrict__ w_gate,
     const uint16_t* __restrict__ w_up, int M, int nrows, uint16_t* __restrict__ s16,
     const int32_t* __restrict__ flags, int pass) {
   if (pass_skipped(flags, pass)) return;
+  constexpr int AP = R + 8;
+  __shared__ __align__(16) uint16_t s_a[16 * G][AP];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, q4 = lane >> 4;
   const int r0 = blockIdx.x * 16 * G;
@@ -202,23 +243,21 @@ __global__ __launch_bounds__(256) void latent_gate_kernel(
 #pragma unroll
   for (int g = 0; g < G; ++g) ag[g] = au[g] = f32x4{0, 0, 0, 0};
   // all operands are loaded before the first MFMA, so their latencies overlap
-  bf16x8 bg[R / 32], bu[R / 32], a[G][R / 32];
+  bf16x8 bg[R / 32], bu[R / 32];
 #pragma unroll
   for (int s = 0; s < R / 32; ++s) {
     bg[s] = as_bf16x8(grow[4 * s + q4]);
     bu[s] = as_bf16x8(urow[4 * s + q4]);
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int r = min(r0 + 16 * g + l16, nrows - 1);
-      a[g][s] = as_bf16x8(reinterpret_cast<const uint4*>(u16 + (int64_t)r * R)[4 * s + q4]);
-    }
   }
+  stage_rows<16 * G, R, AP>(u16, R, r0, nrows, 0, s_a);
+  __syncthreads();
 #pragma unroll
   for (int s = 0; s < R / 32; ++s)
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      ag[g] = mfma16x16x32(a[g][s], bg[s], ag[g]);
-      au[g] = mfma16x16x32(a[g][s], bu[s], au[g]);
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&s_a[16 * g + l16][32 * s + 8 * q4]));
+      ag[g] = mfma16x16x32(a, bg[s], ag[g]);
+      au[g] = mfma16x16x32(a, bu[s], au[g]);
     }
 #pragma unroll
   for (int g = 0; g < G; ++g)
@@ -234,12 +273,17 @@ __global__ __launch_bounds__(256) void latent_gate_kernel(
 }
 
 // Step 5 for rows r0..r0+16*G-1 and channels c0..c0+63; wave w owns channels c0 + 16w .. +15.
+// The k range (the M hidden units) goes in chunks of 256: the chunk's rows of s are read once per
+// workgroup into LDS, while each wave's w_down rows for the chunk are in registers.
 template <int R, int G>
 __global__ __launch_bounds__(256) void latent_down_kernel(
     const uint16_t* __restrict__ s16, const float* __restrict__ u32,
     const uint16_t* __restrict__ w_down, int M, int B, int nrows, uint16_t* __restrict__ lat,
     const int32_t* __restrict__ flags, int pass, int lat_frag) {
   if (pass_skipped(flags, pass)) return;
+  constexpr int KW = 256;           // hidden units per chunk (M is 64 .. 1024, a power of two)
+  constexpr int AP = KW + 8;
+  __shared__ __align__(16) uint16_t s_a[16 * G][AP];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, q4 = lane >> 4;
   const int r0 = blockIdx.x * 16 * G;
@@ -248,27 +292,30 @@ __global__ __launch_bounds__(256) void latent_down_kernel(
   f32x4 acc[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) acc[g] = f32x4{0, 0, 0, 0};
-  // k in chunks of KC MFMA steps (M/32 >= 2): a chunk's loads are all issued before its MFMAs;
-  // indexes past the end are clamped and their MFMAs skipped
-  constexpr int KC = G == 1 ? 16 : 8;
-  const int ns = M / 32;
-  for (int s0 = 0; s0 < ns; s0 += KC) {
-    bf16x8 b[KC], a[G][KC];
+  for (int k0 = 0; k0 < M; k0 += KW) {
+    // this chunk's k steps (M = 64 or 128: one partial chunk); indexes past M are clamped and
+    // their MFMAs skipped
+    const int ns = min(KW, M - k0) / 32;
+    bf16x8 b[KW / 32];
 #pragma unroll
-    for (int i = 0; i < KC; ++i) {
-      const int s = min(s0 + i, ns - 1);
-      b[i] = as_bf16x8(drow[4 * s + q4]);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const int r = min(r0 + 16 * g + l16, nrows - 1);
-        a[g][i] = as_bf16x8(reinterpret_cast<const uint4*>(s16 + (int64_t)r * M)[4 * s + q4]);
-      }
+    for (int i = 0; i < KW / 32; ++i) b[i] = as_bf16x8(drow[(k0 >> 3) + 4 * min(i, ns - 1) + q4]);
+    if (k0 > 0) __syncthreads();  // the previous chunk's fragments have been read
+    if (M - k0 >= KW) {
+      stage_rows<16 * G, KW, AP>(s16, M, r0, nrows, k0, s_a);
+    } else {
+      // M = 64 or 128: the whole k range is narrower than a chunk
+      if (M - k0 == 128) stage_rows<16 * G, 128, AP>(s16, M, r0, nrows, k0, s_a);
+      else stage_rows<16 * G, 64, AP>(s16, M, r0, nrows, k0, s_a);
     }
+    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < KC; ++i)
-      if (s0 + i < ns)
+    for (int i = 0; i < KW / 32; ++i)
+      if (i < ns)
 #pragma unroll
-        for (int g = 0; g < G; ++g) acc[g] = mfma16x16x32(a[g][i], b[i], acc[g]);
+        for (int g = 0; g < G; ++g) {
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&s_a[16 * g + l16][32 * i + 8 * q4]));
+          acc[g] = mfma16x16x32(a, b[i], acc[g]);
+        }
   }
 #pragma unroll
   for (int g = 0; g < G; ++g)
@@ -283,7 +330,6 @@ __global__ __launch_bounds__(256) void latent_down_kernel(
       }
     }
 }
-
 
 // Embedding table with the embedding block of in_proj applied (done once per weight set; the
 // pass then gathers rows instead of projecting them):
