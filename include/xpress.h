@@ -88,10 +88,12 @@ typedef struct {
   const float* w1p;           /* [V, r]   OPTIONAL (NULL: not used), fp32: the embedding table with
                                           in_proj's embedding block applied,
                                           w1p[v, c] = sum_k in_proj[c, 2r+k] * w1[v, k]
-                                          (xpress_fold_embedding). When given and N <= 96,
+                                          (xpress_fold_embedding). When given and
+                                          N * M/64 <= 256 (one workgroup per block and 64-unit
+                                          slice, one round on the 256 CUs: N <= 32 at M = 512),
                                           the latent stage gathers its rows instead of
                                           projecting w1's rows every pass and runs as two
-                                          launches instead of three (from 97 blocks on the
+                                          launches instead of three (beyond that the
                                           three-kernel path is faster and is used); results
                                           agree with the NULL path within fp32 rounding        */
 } xpress_weights;

@@ -107,20 +107,26 @@ xpress_status check_base(const xpress_bf16* base, int64_t ld, int64_t V) {
   return XPRESS_OK;
 }
 
-// Whether the latent stage runs from the projected embedding table (share + sum kernels). Per
-// pass: 11 against 16 us at 32 blocks, equal at 64 and 96; from there on the three-kernel path
-// wins (34 against 37 us at 127 blocks, 46 against 50 at 256: the fp32 shares of the down
-// product, G copies of lat, then cost more than the projection they replace) and is taken even
-// when the table is given. The results agree within fp32 rounding either way.
-constexpr int kTableMaxN = 96;
-bool use_table(const xpress_weights* w, int N) { return w->w1p != nullptr && N <= kTableMaxN; }
+// Whether the latent stage runs from the projected embedding table (share + sum kernels): while
+// its N * M/64 share workgroups (one per block and 64-unit slice) fit in one round on the 256
+// CUs. Whole steps at M = 512: the table path is faster up to 32 blocks (16.4k against 15.4k
+// passes/s at 32, 18.9k against 17.4k at 24, 35.0k against 29.6k at 1); from 33 blocks on (264
+// workgroups, a second round) the three-kernel path is (14.9k against 14.4k at 33, 12.1k against
+// 11.9k at 36, 9.4k against 9.1k at 48, 6.2k against 6.0k at 96) and is taken even when the table
+// is given. The results agree within fp32 rounding either way.
+constexpr int kTableMaxWorkgroups = 256;
+bool table_fits(int N, int M) { return (int64_t)N * (M / 64) <= kTableMaxWorkgroups; }
+bool use_table(const xpress_weights* w, int N) { return w->w1p != nullptr && table_fits(N, w->M); }
 
-// Scratch of the latent stage: the three-kernel path's, or the larger projected-table path's
-// (slice shares) when N is small enough for that path to run.
-size_t latent_bytes(int N, int r, int M) {
-  const size_t a = xpress::latent_scratch_bytes(N, r, M);
-  const size_t b = N <= kTableMaxN ? xpress::latent_fused_scratch_bytes(N, r, M) : 0;
-  return a > b ? a : b;
+// Scratch of the latent stage for any M: the three-kernel path's, or the projected-table path's
+// (slice shares) where some M lets that path run.
+size_t latent_bytes(int N, int r) {
+  size_t t = xpress::latent_scratch_bytes(N, r, kMaxM);
+  for (int M = 64; M <= kMaxM; M *= 2) {
+    const size_t b = table_fits(N, M) ? xpress::latent_fused_scratch_bytes(N, r, M) : 0;
+    t = b > t ? b : t;
+  }
+  return t;
 }
 
 // Workspace regions of a call with N blocks.
@@ -143,7 +149,7 @@ Layout step_layout(int N, int B, int r, int H, int64_t V, int C, int K) {
   L.hdg = take(xpress::hidden_scratch_bytes_any_h(N * B, r));
   L.xh = take((size_t)N * B * r * sizeof(float));
   L.lat = take((rows + 31) / 32 * 32 * (size_t)r * 2);  // whole 32-row tiles (fragment order)
-  L.lscr = take(latent_bytes(N, r, kMaxM));
+  L.lscr = take(latent_bytes(N, r));
   // sized for the largest range count (the count at one row chunk)
   L.part = take(C > 0 ? 0 : rows * (size_t)xpress::readout_tiles(V, 1) * sizeof(uint2));
   L.flags = take((size_t)(K + 1) * sizeof(int32_t));
@@ -203,12 +209,16 @@ xpress_status xpress_workspace_size(int32_t n_max, int32_t B, int32_t r, int64_t
   if (n_max < 0 || C < 0 || k_max < 0) return fail(XPRESS_ERR_ARG, "negative n_max, C or k_max");
   xpress_status st = check_dims(B, r, V);
   if (st != XPRESS_OK) return st;
-  // every region grows with N, except the latent scratch, which the table path enlarges up to
-  // kTableMaxN blocks: the largest layout of any N <= n_max is at n_max or at kTableMaxN
+  // every region grows with N, except the latent scratch, whose table-path part peaks where
+  // N * M/64 reaches the workgroup bound for one of the M values: the largest layout of any
+  // N <= n_max is at n_max or at one of those N
   size_t t = step_layout(n_max, B, r, kMaxH, V, C, k_max).total;
-  if (n_max > kTableMaxN) {
-    const size_t u = step_layout(kTableMaxN, B, r, kMaxH, V, C, k_max).total;
-    t = u > t ? u : t;
+  for (int M = 64; M <= kMaxM; M *= 2) {
+    const int n = kTableMaxWorkgroups / (M / 64);
+    if (n < n_max) {
+      const size_t u = step_layout(n, B, r, kMaxH, V, C, k_max).total;
+      t = u > t ? u : t;
+    }
   }
   *bytes = t;
   return XPRESS_OK;

@@ -111,10 +111,11 @@ def test_fold_embedding_and_table_arguments_are_checked():
 
 def test_workspace_for_n_max_fits_every_smaller_n():
     """A workspace sized for n_max covers every N <= n_max (the table path's latent scratch makes
-    the size non-monotone in N where that path stops, after 96 blocks)."""
-    for n_max in (96, 97, 128, 160, 256):
+    the size non-monotone in N where that path stops: N * M/64 = 256 share workgroups, i.e.
+    after 16, 32, 64, 128 or 256 blocks depending on M)."""
+    for n_max in (15, 16, 17, 31, 32, 33, 64, 65, 96, 128, 160, 256, 257):
         big = xpress.workspace_size(n_max, 16, 256, 151936, 0, 15)
-        for n in (1, 32, 96, 97, 127, 128, n_max):
+        for n in (1, 16, 17, 32, 33, 64, 65, 96, 128, 129, 256, n_max):
             if n <= n_max:
                 assert xpress.workspace_size(n, 16, 256, 151936, 0, 15) <= big, (n, n_max)
 
