@@ -225,6 +225,16 @@ def main() -> int:
     flops = 2.0 * rows * (wl.C if wl.C > 0 else wl.V) * wl.r
     achieved_gbs = alg_bytes / (readout_us * 1e-6) / 1e9
     mfma_tflops = flops / (readout_us * 1e-6) / 1e12
+    # The readout's arithmetic intensity caps its MFMA fraction at the HBM peak: a kernel that
+    # streamed its bytes at 8 TB/s would reach (flops / bytes) * 8 TB/s of bf16 MFMA work.
+    mfma_cap = flops / alg_bytes * HBM_PEAK_GBS * 1e9 / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    # Latent bytes per pass, each operand once: gate, up and down weights, the folded mixer, xh,
+    # the 16 gathered rows per block (projected fp32 table rows on the two-launch path, bf16 w1
+    # rows plus in_proj's embedding block on the three-launch one) and lat written.
+    table_path = wl.N * (wl.M // 64) <= 256
+    latent_bytes = (3 * wl.M * wl.r * 2 + wl.B * wl.B * wl.r * 2 + wl.N * wl.B * wl.r * 4
+                    + (wl.N * wl.B * wl.r * 4 if table_path else wl.N * wl.B * wl.r * 2 + wl.r * wl.r * 2)
+                    + rows * wl.r * 2)
     traffic = traffic_record(kname, wl.name)
 
     out = {
@@ -260,8 +270,12 @@ def main() -> int:
             "loop_only_passes_per_s": round(K / (loop_us * 1e-6), 1),
             "readout_tflops": round(mfma_tflops, 1),
             "readout_frac_of_bf16_mfma_peak": round(mfma_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "readout_mfma_frac_cap_at_hbm_peak": round(mfma_cap, 4),
             "argmax_reduce_us": round(reduce_us, 2),
             "latent_us": round(latent_us, 2),
+            "latent_path": "table (2 launches)" if table_path else "projection (3 launches)",
+            "latent_algorithmic_bytes": latent_bytes,
+            "latent_frac_of_hbm_peak": round(latent_bytes / (latent_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "pass_loop_us_per_pass": round(loop_us / K, 2),
             "draft_checksum": int(np.sum(draft * (np.arange(draft.size).reshape(draft.shape) + 1)) % (1 << 61)),
         },
