@@ -97,6 +97,12 @@ __device__ __forceinline__ void block_tokens_finish(bool has_part, const uint2 (
   }
 }
 
+// The mixer rows of wave w in latent_mix_kernel: w, 15-w, w+4 and 11-w, two pairs (b, 15-b) of
+// 17 taps each (row b has the b+1 taps j <= b), so every wave loads and multiplies 34 taps per
+// channel.
+constexpr int mix_row(int w, int k) { return k == 0 ? w : k == 1 ? 15 - w : k == 2 ? w + 4 : 11 - w; }
+constexpr int mix_tap0(int w, int k) { return k == 0 ? 0 : mix_tap0(w, k - 1) + mix_row(w, k - 1) + 1; }
+
 // Steps 1-3 for one block and 64 channels (blockIdx.y); 4 waves. With `part` given (inside a
 // step), the block first finishes the previous pass (block_tokens_*); slice 0 writes blk.
 template <int R>
@@ -115,22 +121,27 @@ __global__ __launch_bounds__(256) void latent_mix_kernel(
   const int lane = tid & 63, wave = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
 
   // The previous pass's partials first (they head the dependency chain), then the mixer taps of
-  // this thread's channel c0 + lane for slots 4*wave .. 4*wave+3 (independent of the tokens):
+  // this thread's channel c0 + lane for the wave's rows (mix_row; independent of the tokens):
   // mix_L is [B, B, r], channel innermost, so a tap is one coalesced 2-byte load across the wave.
-  // Taps past B or above the diagonal are not used.
+  // Rows past B are zeroed after the mixer. The wave index is uniform, so each wave runs its own
+  // copy of the tap loads and the mixer, with every index known at compile time.
   uint2 qp[16];
   if (part) block_tokens_load(part, ntiles, rows, n, B, qp);
-  uint16_t tap[4][16];
-  {
-    const int bb = min(4 * wave, B - 1);
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int b = min(bb + k, B - 1), jj = min(j, B - 1);
-        tap[k][j] = mix_L[(int64_t)(b * B + jj) * R + c0 + lane];
-      }
-  }
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  uint16_t tap[34];
+  auto load_taps = [&](auto wc) __attribute__((always_inline)) {
+    constexpr int W = decltype(wc)::value;
+    static_for<0, 4>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int K = decltype(kc)::value, b = mix_row(W, K), e0 = mix_tap0(W, K);
+      static_for<0, b + 1>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        tap[e0 + j] = mix_L[(int64_t)(min(b, B - 1) * B + min(j, B - 1)) * R + c0 + lane];
+      });
+    });
+  };
+  static_for<0, 4>([&](auto wc) __attribute__((always_inline)) {
+    if (wave_s == decltype(wc)::value) load_taps(wc);
+  });
 
   block_tokens_finish(part != nullptr, qp, blk, am1, n, B, blockIdx.y == 0, flags, pass, s_tok);
   __syncthreads();
@@ -177,24 +188,31 @@ __global__ __launch_bounds__(256) void latent_mix_kernel(
   }
   __syncthreads();
 
-  // step 3: u[b, c] = sum_{j<=b} L[b, j, c] x[j, c]; thread -> channel c0 + lane, slots
-  // 4*wave .. 4*wave+3
+  // step 3: u[b, c] = sum_{j<=b} L[b, j, c] x[j, c]; thread -> channel c0 + lane, the wave's
+  // rows mix_row(wave, 0..3)
   {
     float x[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) x[j] = s_x[j][lane];
     float* o32 = u32 + (int64_t)n * 16 * R + c0 + lane;
     uint16_t* o16 = u16 + (int64_t)n * 16 * R + c0 + lane;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int b = 4 * wave + k;
-      float u = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        u = (j <= b && b < B) ? fmaf(bf16_to_f32(tap[k][j]), x[j], u) : u;
-      o32[(int64_t)b * R] = u;
-      o16[(int64_t)b * R] = f32_to_bf16(u);
-    }
+    auto mix = [&](auto wc) __attribute__((always_inline)) {
+      constexpr int W = decltype(wc)::value;
+      static_for<0, 4>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int K = decltype(kc)::value, b = mix_row(W, K), e0 = mix_tap0(W, K);
+        float u = 0.f;
+        static_for<0, b + 1>([&](auto jc) __attribute__((always_inline)) {
+          constexpr int j = decltype(jc)::value;
+          u = fmaf(bf16_to_f32(tap[e0 + j]), x[j], u);
+        });
+        u = b < B ? u : 0.f;
+        o32[(int64_t)b * R] = u;
+        o16[(int64_t)b * R] = f32_to_bf16(u);
+      });
+    };
+    static_for<0, 4>([&](auto wc) __attribute__((always_inline)) {
+      if (wave_s == decltype(wc)::value) mix(wc);
+    });
   }
 }
 
