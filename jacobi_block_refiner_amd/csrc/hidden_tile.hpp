@@ -19,16 +19,23 @@ constexpr int kMaxSplits = 8;     // split-K slices at most
 // readout kernel: D[row = 8*(v/4) + 4*(l/32) + v%4][col = l%32]). Up to kDepth k chunks are loaded
 // into registers ahead of the one being multiplied out of LDS: the operands are first touches
 // from HBM, so the slice's loads must be in flight together rather than one chunk at a time.
-constexpr int kDepth = 8;
+// The GEMM's own launch takes 8 (10 us at 32 x 16 slots against 25 one chunk at a time); inside
+// a start-of-step launch, whose other workgroups need few registers, 4 keeps the launch at four
+// workgroups per CU.
+struct GemmLds {
+  u32x4 a[kTM * kLQ];
+  u32x4 b[kTN * kLQ];
+};
 
+template <int kDepth>
 __device__ __forceinline__ void hidden_gemm_tile(const uint16_t* __restrict__ h,
                                                  const uint16_t* __restrict__ down_h,
                                                  const uint16_t* __restrict__ down_g, int NB,
                                                  int H, int r, int kslice,
                                                  float* __restrict__ part, int bx, int by,
-                                                 int ks) {
-  __shared__ u32x4 s_a[kTM * kLQ];
-  __shared__ u32x4 s_b[kTN * kLQ];
+                                                 int ks, GemmLds& lds) {
+  u32x4* s_a = lds.a;
+  u32x4* s_b = lds.b;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int m0 = bx * kTM, n0 = by * kTN;

@@ -24,7 +24,8 @@ __global__ __launch_bounds__(256) void hidden_gemm_kernel(const uint16_t* __rest
                                                           const uint16_t* __restrict__ down_g,
                                                           int NB, int H, int r, int kslice,
                                                           float* __restrict__ part) {
-  hidden_gemm_tile(h, down_h, down_g, NB, H, r, kslice, part, blockIdx.x, blockIdx.y, blockIdx.z);
+  __shared__ GemmLds lds;
+  hidden_gemm_tile<8>(h, down_h, down_g, NB, H, r, kslice, part, blockIdx.x, blockIdx.y, blockIdx.z, lds);
 }
 
 // The start of a step in one launch: workgroups [0, g1) are the hidden GEMM's tiles (mt x nt
@@ -40,8 +41,9 @@ __global__ __launch_bounds__(256) void step_start_kernel(
   const int i = blockIdx.x;
   if (zero_flags && i == 0)
     for (int q = threadIdx.x; q < nzero; q += blockDim.x) zero_flags[q] = 0;
+  __shared__ GemmLds lds;
   if (i < g1)
-    hidden_gemm_tile(h, down_h, down_g, NB, H, r, kslice, part, i % mt, (i / mt) % nt, i / (mt * nt));
+    hidden_gemm_tile<4>(h, down_h, down_g, NB, H, r, kslice, part, i % mt, (i / mt) % nt, i / (mt * nt), lds);
   else
     initial_block_row(base, ld, anchor, B, V, blk, i - g1);
 }

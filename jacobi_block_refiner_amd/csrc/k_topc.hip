@@ -203,14 +203,13 @@ __device__ __forceinline__ void hist_add_aggregated(uint32_t* hist, int bin, boo
   }
 }
 __device__ __forceinline__ uint32_t radix_kth(const uint32_t* keys, int n, int k, uint32_t* s_hist,
-                                              uint32_t* s_par, uint32_t* above_out) {
+                                              uint32_t* s_par, int* s_tmp, uint32_t* above_out) {
   // keys: 17-bit (key + 1, 0 = empty); returns the k-th largest non-empty key (as key + 1) and
   // sets *above_out = number of keys strictly above it. Whole workgroup (256 threads). Two
   // histogram levels over the 16-bit key (high byte, then low byte inside the boundary bin); the
   // boundary bin is found by a parallel scan over the bins in descending order: thread t owns bin
   // 255 - t, and the bin whose [count above, count above + own count) holds k - 1 is the one.
   const int tid = threadIdx.x;
-  __shared__ int s_tmp[4];
   s_hist[tid] = 0;
   __syncthreads();
   for (int j0 = 0; j0 < n; j0 += 256) {  // uniform trip count (n is a multiple of 256)
@@ -254,19 +253,33 @@ __device__ __forceinline__ uint32_t radix_kth(const uint32_t* keys, int n, int k
   return t;
 }
 
+// LDS of one row's selection (the caller's, so that a launch with other work can overlay it).
+constexpr int kHC = 4096;  // chunk-list capacity
+struct SelLds {
+  uint32_t hist[512];
+  int tmp[4];
+  uint32_t par[4];
+  int tmp_r[4];        // radix_kth's scan
+  uint32_t key[kBuf];  // key + 1 (0: empty)
+  int id[kBuf];
+  uint16_t bits[kBuf];  // the buffered values' bf16 bits
+  int hc[kHC];          // chunks whose maximum can hold an answer, ascending
+  float bv[4];          // the starting block's per-wave winners
+  int bi[4];
+};
+
 __device__ __forceinline__ void topc_select_row(int p, const uint16_t* __restrict__ base,
                                                 int64_t ld, int64_t V, int c,
                                                 int64_t* __restrict__ cand,
                                                 uint16_t* __restrict__ base_c,
-                                                uint16_t* __restrict__ cmax) {
-  __shared__ uint32_t s_hist[512];
-  __shared__ int s_tmp[4];
-  __shared__ uint32_t s_par[4];
-  __shared__ uint32_t s_key[kBuf];  // key + 1 (0: empty)
-  __shared__ int s_id[kBuf];
-  __shared__ uint16_t s_bits[kBuf];  // the buffered values' bf16 bits
-  constexpr int kHC = 4096;          // chunk-list capacity
-  __shared__ int s_hc[kHC];          // chunks whose maximum can hold an answer, ascending
+                                                uint16_t* __restrict__ cmax, SelLds& L) {
+  uint32_t* s_hist = L.hist;
+  int* s_tmp = L.tmp;
+  uint32_t* s_par = L.par;
+  uint32_t* s_key = L.key;
+  int* s_id = L.id;
+  uint16_t* s_bits = L.bits;
+  int* s_hc = L.hc;
   const int tid = threadIdx.x, lane = tid & 63;
   const uint16_t* row = base + (int64_t)p * ld;
   int64_t* out_id = cand + (int64_t)p * c;
@@ -353,7 +366,7 @@ __device__ __forceinline__ void topc_select_row(int p, const uint16_t* __restric
   int ngm_total;
   (void)block_exclusive_scan(ngm, s_tmp, ngm_total);
   uint32_t above;
-  const uint32_t t0 = ngm_total >= c ? radix_kth(s_key, kBuf, c, s_hist, s_par, &above) : 1u;
+  const uint32_t t0 = ngm_total >= c ? radix_kth(s_key, kBuf, c, s_hist, s_par, L.tmp_r, &above) : 1u;
   // the smallest fp32 value with key >= t0 - 1 (any finite value when t0 <= 1: the key's bf16
   // bits, inverse of order_key, would not be a finite value then)
   float v0 = -3.4028235e38f;
@@ -461,7 +474,7 @@ __device__ __forceinline__ void topc_select_row(int p, const uint16_t* __restric
   // compaction: thread tid owns buffer slots 8*tid .. 8*tid+7; every key above T is taken, and of
   // the keys equal to T the first need_eq in buffer order, the lowest ids. Written in buffer order:
   // ascending ids.
-  const uint32_t T = radix_kth(s_key, kBuf, c, s_hist, s_par, &above);
+  const uint32_t T = radix_kth(s_key, kBuf, c, s_hist, s_par, L.tmp_r, &above);
   const int need_eq = c - (int)above;
   uint32_t k8[8];
 #pragma unroll
@@ -500,13 +513,13 @@ __device__ __forceinline__ void topc_select_block(int p, const uint16_t* __restr
                                                   uint16_t* __restrict__ base_c,
                                                   const int64_t* __restrict__ anchor,
                                                   int64_t* __restrict__ blk, int B,
-                                                  uint16_t* __restrict__ cmax) {
-  topc_select_row(p, base, ld, V, c, cand, base_c, cmax);
+                                                  uint16_t* __restrict__ cmax, SelLds& L) {
+  topc_select_row(p, base, ld, V, c, cand, base_c, cmax, L);
   if (!blk) return;
   // the block's first row also stores the anchor in slot 0
   if (p % (B - 1) == 0 && threadIdx.x == 0) blk[(int64_t)(p / (B - 1)) * B] = anchor[p / (B - 1)];
-  __shared__ float s_bv[4];
-  __shared__ int s_bi[4];
+  float* s_bv = L.bv;
+  int* s_bi = L.bi;
   __threadfence_block();
   __syncthreads();  // the row's candidates and values are written (by this workgroup)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -540,12 +553,15 @@ __global__ __launch_bounds__(256) void topc_select_kernel(const uint16_t* __rest
                                                           const int64_t* __restrict__ anchor,
                                                           int64_t* __restrict__ blk, int B,
                                                           uint16_t* __restrict__ cmax) {
-  topc_select_block(blockIdx.x, base, ld, V, c, cand, base_c, anchor, blk, B, cmax);
+  __shared__ SelLds lds;
+  topc_select_block(blockIdx.x, base, ld, V, c, cand, base_c, anchor, blk, B, cmax, lds);
 }
 
 // The start of a top-C step in one launch: workgroups [0, g1) are the hidden GEMM's tiles (mt x
 // nt tiles per split, split-major), the rest the draft rows' selection. The two are independent;
-// the GEMM is latency-bound and hides behind the selection.
+// the GEMM is latency-bound and hides behind the selection. The two roles overlay one LDS area
+// and the GEMM keeps 4 k chunks in flight, so a CU holds three of these workgroups and the whole
+// launch (256 tiles + 480 rows at 32 blocks) runs in one round.
 __global__ __launch_bounds__(256) void topc_start_kernel(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ down_h,
     const uint16_t* __restrict__ down_g, int NB, int H, int r, int kslice,
@@ -556,10 +572,14 @@ __global__ __launch_bounds__(256) void topc_start_kernel(
   const int i = blockIdx.x;
   if (zero_flags && i == 0)  // the step's pass flags (read only by later launches)
     for (int q = threadIdx.x; q < nzero; q += blockDim.x) zero_flags[q] = 0;
+  __shared__ union {
+    GemmLds gemm;
+    SelLds sel;
+  } lds;
   if (i < g1)
-    hidden_gemm_tile(h, down_h, down_g, NB, H, r, kslice, part, i % mt, (i / mt) % nt, i / (mt * nt));
+    hidden_gemm_tile<4>(h, down_h, down_g, NB, H, r, kslice, part, i % mt, (i / mt) % nt, i / (mt * nt), lds.gemm);
   else
-    topc_select_block(i - g1, base, ld, V, c, cand, base_c, anchor, blk, B, cmax);
+    topc_select_block(i - g1, base, ld, V, c, cand, base_c, anchor, blk, B, cmax, lds.sel);
 }
 
 __global__ __launch_bounds__(256) void topc_gather_kernel(const int64_t* __restrict__ cand,
