@@ -383,10 +383,11 @@ __device__ __forceinline__ void topc_select_row(int p, const uint16_t* __restric
     select_row_exact(row, V, c, out_id, out_b, s_hist, s_tmp, s_par);
     return;
   }
-  // 3a. The chunks whose maximum reaches v0, listed in ascending order: in round u, thread tid
-  // takes the 8 chunk maxima of group g0 + 256u + tid (the kLB groups' 16-byte reads are issued
-  // first); a block-wide exclusive scan of the hit counts places its hits after those of the
-  // lower groups. A list that would overflow sends the row to the exact path.
+  // 3a. The chunks whose maximum reaches v0, listed in ascending order: per round, thread tid takes
+  // the kLB consecutive groups of 8 chunk maxima g0 + kLB*tid .. +kLB-1 (128 contiguous bytes,
+  // all read before any is used); one block-wide exclusive scan of the threads' hit counts places
+  // each thread's hits, in ascending order, after those of the lower threads (two rounds per row
+  // of 151936 ids). A list that would overflow sends the row to the exact path.
   const int64_t n8 = nchunk8 / 8;
   const uint4* cm4 = reinterpret_cast<const uint4*>(cmax_row);
   int nhc = 0;  // uniform
@@ -394,31 +395,29 @@ __device__ __forceinline__ void topc_select_row(int p, const uint16_t* __restric
     uint4 m8[kLB];
 #pragma unroll
     for (int u = 0; u < kLB; ++u) {
-      const int64_t g = g0 + 256 * u + tid;
+      const int64_t g = g0 + kLB * tid + u;
       m8[u] = g < n8 ? cm4[g] : make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
     }
+    uint64_t hm = 0;  // bit 8u + e: chunk 8 (g0 + kLB*tid + u) + e reaches v0
 #pragma unroll
     for (int u = 0; u < kLB; ++u) {
-      if (g0 + 256 * u >= n8) break;  // uniform
-      const int64_t g = g0 + 256 * u + tid;
       const uint32_t w[4] = {m8[u].x, m8[u].y, m8[u].z, m8[u].w};
-      uint32_t hm = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t b = (e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16);
-        hm |= (__uint_as_float(b) >= v0 ? 1u : 0u) << e;
+        const uint32_t bv = (e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16);
+        hm |= (uint64_t)(__uint_as_float(bv) >= v0 ? 1u : 0u) << (8 * u + e);
       }
-      const int cnt = __popc(hm);
-      int tot;
-      int pos = nhc + block_exclusive_scan(cnt, s_tmp, tot);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if ((hm >> e) & 1u) {
-          if (pos < kHC) s_hc[pos] = (int)(g * 8 + e);
-          ++pos;
-        }
-      nhc += tot;
     }
+    int tot;
+    int pos = nhc + block_exclusive_scan(__popcll(hm), s_tmp, tot);
+    const int64_t c0 = (g0 + kLB * tid) * 8;
+    while (hm) {  // the thread's hits in ascending order
+      const int bit = __ffsll((unsigned long long)hm) - 1;
+      if (pos < kHC) s_hc[pos] = (int)(c0 + bit);
+      ++pos;
+      hm &= hm - 1;
+    }
+    nhc += tot;
   }
   if (nhc > kHC) {  // uniform
     select_row_exact(row, V, c, out_id, out_b, s_hist, s_tmp, s_par);
