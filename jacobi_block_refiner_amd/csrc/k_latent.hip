@@ -400,8 +400,10 @@ __global__ __launch_bounds__(256) void fold_embedding_kernel(const uint16_t* __r
 //   4. share_g = w_down[:, units] . s (+ u for g = 0), written to dpart for slots 1..B-1.
 // latent_sum_kernel then adds the G shares of each slot in slice order into lat (bf16): a fixed
 // summation order, and the kernel boundary orders the shares' stores before their loads.
-// Every workgroup of a block computes the same u (same inputs, same arithmetic).
-template <int R>
+// Every workgroup of a block computes the same u (same inputs, same arithmetic). A slice is UPW
+// = 64 units (waves 0-3 take 16 each) or, with few blocks, 32 (waves 0-1; twice the workgroups,
+// each with half the gate, up and down weights to load).
+template <int R, int UPW>
 __global__ __launch_bounds__(256) void latent_share_kernel(
     const uint2* __restrict__ part, int ntiles, int rows, int64_t* __restrict__ blk,
     const int64_t* __restrict__ am1, const float* __restrict__ xh, const float* __restrict__ w1p,
@@ -413,7 +415,9 @@ __global__ __launch_bounds__(256) void latent_share_kernel(
   constexpr int KS = R / 32;  // k steps of the gate/up products
   constexpr int DT = R / 64;  // 16-channel output tiles of the down product per wave
   constexpr int UP = R + 8;   // bf16 row pitch of s_u (one 16-byte pad per row)
-  constexpr int SP = 64 + 8;  // bf16 row pitch of s_s
+  constexpr int SP = UPW + 8;  // bf16 row pitch of s_s
+  constexpr int UW = UPW / 16;  // waves with units
+  constexpr int DK = UPW / 32;  // k steps of the down product
   __shared__ int64_t s_tok[16];
   __shared__ float s_u32[16][R];
   __shared__ __align__(16) uint16_t s_u[16][UP];
@@ -429,9 +433,9 @@ __global__ __launch_bounds__(256) void latent_share_kernel(
   // loads that do not depend on the tokens: the slice's gate/up rows, xh and the taps.
   uint2 qp[16];
   if (part) block_tokens_load(part, ntiles, rows, n, B, qp);
-  const int m = g * 64 + wave * 16 + l16;
+  const int m = g * UPW + min(wave, UW - 1) * 16 + l16;
   bf16x8 gB[KS], uB[KS];
-  {
+  if (wave < UW) {  // uniform
     const uint4* grow = reinterpret_cast<const uint4*>(w_gate + (int64_t)m * R);
     const uint4* urow = reinterpret_cast<const uint4*>(w_up + (int64_t)m * R);
 #pragma unroll
@@ -492,18 +496,18 @@ __global__ __launch_bounds__(256) void latent_share_kernel(
     }
   }
   // the slice's w_down columns, needed after the gate products
-  bf16x8 dB[DT][2];
+  bf16x8 dB[DT][DK];
 #pragma unroll
   for (int it = 0; it < DT; ++it) {
     const int i = (wave * DT + it) * 16 + l16;
-    const uint4* drow = reinterpret_cast<const uint4*>(w_down + (int64_t)i * M + g * 64);
+    const uint4* drow = reinterpret_cast<const uint4*>(w_down + (int64_t)i * M + g * UPW);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) dB[it][ks] = as_bf16x8(drow[4 * ks + q4]);
+    for (int ks = 0; ks < DK; ++ks) dB[it][ks] = as_bf16x8(drow[4 * ks + q4]);
   }
   __syncthreads();
 
-  // step 3: units g*64 + 16*wave .. +15 for the 16 slot rows
-  {
+  // step 3: units g*UPW + 16*wave .. +15 for the 16 slot rows
+  if (wave < UW) {  // uniform
     f32x4 ag = {0, 0, 0, 0}, au = {0, 0, 0, 0};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -523,16 +527,16 @@ __global__ __launch_bounds__(256) void latent_share_kernel(
   // step 4: this slice's share of w_down . s for channels (wave*DT + it)*16 + l16; slice 0's
   // share carries the residual u
   {
-    bf16x8 a[2];
+    bf16x8 a[DK];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < DK; ++ks)
       a[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(&s_s[l16][32 * ks + 8 * q4]));
     float* dp = dpart + ((int64_t)n * G + g) * 16 * R;
 #pragma unroll
     for (int it = 0; it < DT; ++it) {
       f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) acc = mfma16x16x32(a[ks], dB[it][ks], acc);
+      for (int ks = 0; ks < DK; ++ks) acc = mfma16x16x32(a[ks], dB[it][ks], acc);
       const int i = (wave * DT + it) * 16 + l16;
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -616,10 +620,15 @@ hipError_t launch_fused_r(const uint2* part, int ntiles, int64_t* blk, const int
                           int N, int B, int M, int64_t V, uint16_t* lat, float* dpart,
                           int32_t* flags, int pass, hipStream_t s, bool with_sum,
                           bool lat_frag) {
-  const int G = M / 64;
-  hipLaunchKernelGGL(latent_share_kernel<R>, dim3(N, G), dim3(256), 0, s, part, ntiles,
-                     N * (B - 1), blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, B, M, V, dpart,
-                     flags, pass);
+  const int G = share_slices(N, M);
+  if (G == M / 32)
+    hipLaunchKernelGGL((latent_share_kernel<R, 32>), dim3(N, G), dim3(256), 0, s, part, ntiles,
+                       N * (B - 1), blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, B, M, V, dpart,
+                       flags, pass);
+  else
+    hipLaunchKernelGGL((latent_share_kernel<R, 64>), dim3(N, G), dim3(256), 0, s, part, ntiles,
+                       N * (B - 1), blk, am1, xh, w1p, mix_L, w_gate, w_up, w_down, B, M, V, dpart,
+                       flags, pass);
   if (!with_sum) return hipGetLastError();
   constexpr int RPW = 256 / (R / 4);
   hipLaunchKernelGGL(latent_sum_kernel<R>, dim3(N, (B - 1 + RPW - 1) / RPW), dim3(256), 0, s,
@@ -629,8 +638,12 @@ hipError_t launch_fused_r(const uint2* part, int ntiles, int64_t* blk, const int
 
 }  // namespace
 
+// Slices of the share kernel per block: 32-unit slices while their N * M/32 workgroups fit one
+// round on the 256 CUs (N <= 16 at M = 512), else 64-unit ones.
+int share_slices(int N, int M) { return (int64_t)N * (M / 32) <= 256 ? M / 32 : M / 64; }
+
 size_t latent_fused_scratch_bytes(int N, int r, int M) {
-  return (size_t)N * (M / 64) * 16 * r * sizeof(float);
+  return (size_t)N * share_slices(N, M) * 16 * r * sizeof(float);
 }
 
 hipError_t launch_latent_fused(const uint2* part, int ntiles, int64_t* blk, const int64_t* am1,

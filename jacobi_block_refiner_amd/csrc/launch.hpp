@@ -51,6 +51,7 @@ hipError_t launch_latent(const uint2* part, int ntiles, int64_t* blk, const int6
 // per-(block, 64-unit slice) shares of the latent, then their sum into lat (skipped with
 // with_sum = false, for a consumer that sums the shares itself). dpart: [N, M/64, 16,
 // r] fp32 shares (latent_fused_scratch_bytes). part / blk / flags as in launch_latent.
+int share_slices(int N, int M);  // latent share workgroups per block (table path)
 size_t latent_fused_scratch_bytes(int N, int r, int M);
 hipError_t launch_latent_fused(const uint2* part, int ntiles, int64_t* blk, const int64_t* am1,
                                const float* xh, const float* w1p, const uint16_t* mix_L,

@@ -209,16 +209,13 @@ xpress_status xpress_workspace_size(int32_t n_max, int32_t B, int32_t r, int64_t
   if (n_max < 0 || C < 0 || k_max < 0) return fail(XPRESS_ERR_ARG, "negative n_max, C or k_max");
   xpress_status st = check_dims(B, r, V);
   if (st != XPRESS_OK) return st;
-  // every region grows with N, except the latent scratch, whose table-path part peaks where
-  // N * M/64 reaches the workgroup bound for one of the M values: the largest layout of any
-  // N <= n_max is at n_max or at one of those N
+  // every region grows with N, except the latent scratch, whose table-path part peaks where the
+  // share workgroups N * slices reach their bound of 256, at a power of two N: the largest
+  // layout of any N <= n_max is at n_max or at one of those N
   size_t t = step_layout(n_max, B, r, kMaxH, V, C, k_max).total;
-  for (int M = 64; M <= kMaxM; M *= 2) {
-    const int n = kTableMaxWorkgroups / (M / 64);
-    if (n < n_max) {
-      const size_t u = step_layout(n, B, r, kMaxH, V, C, k_max).total;
-      t = u > t ? u : t;
-    }
+  for (int n = 1; n <= kTableMaxWorkgroups && n < n_max; n *= 2) {
+    const size_t u = step_layout(n, B, r, kMaxH, V, C, k_max).total;
+    t = u > t ? u : t;
   }
   *bytes = t;
   return XPRESS_OK;
@@ -538,7 +535,7 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
              "latent");
     if (c > 0) {
       XP_TRY(xpress::launch_topc_readout(lat, fused ? static_cast<const float*>(lscr) : nullptr,
-                                         w->M / 64, w->w2, true, base_c, cand, rows, B, r, c, blk,
+                                         xpress::share_slices(N, w->M), w->w2, true, base_c, cand, rows, B, r, c, blk,
                                          nullptr, pf, p, s),
              "top-C readout");
     } else {
