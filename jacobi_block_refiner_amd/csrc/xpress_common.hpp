@@ -90,7 +90,7 @@ __device__ __forceinline__ int64_t lat_frag_offset(int p, int c) {
 __device__ __forceinline__ void lds_copy16(const void* gbase, uint32_t off, uint32_t lds_base) {
   // one wait state between the M0 write and the copy that reads it
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds_base), "v"(off), "s"(gbase) : "memory", "m0");
+               :: "s"(lds_base), "v"(off), "s"(gbase) : "memory");
 }
 
 // Skip test of the fixed-point early exit: pass p >= 1 is skipped once pass p-1 changed nothing.
