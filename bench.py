@@ -276,6 +276,7 @@ def main() -> int:
             "latent_path": "table (2 launches)" if table_path else "projection (3 launches)",
             "latent_algorithmic_bytes": latent_bytes,
             "latent_frac_of_hbm_peak": round(latent_bytes / (latent_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "latent_share_of_pass": round(latent_us / (loop_us / K), 4),
             "pass_loop_us_per_pass": round(loop_us / K, 2),
             "draft_checksum": int(np.sum(draft * (np.arange(draft.size).reshape(draft.shape) + 1)) % (1 << 61)),
         },
