@@ -266,6 +266,14 @@ def test_fold_embedding_matches_oracle_projection(r, V):
                                          (1, 33, {"B": 16, "r": 256, "M": 512, "V": 3000}),
                                          (1, 96, {"B": 16, "r": 256, "M": 512, "V": 3000}),
                                          (1, 130, {"B": 16, "r": 256, "M": 512, "V": 3000}),
+                                         # the slice width follows N * M/32 <= 256 (32 units) and the
+                                         # path N * M/64 <= 256: M = 1024 at 12 blocks takes 64-unit
+                                         # slices on the table path, M = 256 at 20 and 40 blocks 32-
+                                         # and 64-unit ones, at 65 blocks the three-kernel path
+                                         (3, 12, {"V": 2048, "M": 1024}),
+                                         (1, 20, {"B": 16, "r": 256, "M": 256, "V": 3000}),
+                                         (1, 40, {"B": 16, "r": 256, "M": 256, "V": 3000}),
+                                         (1, 65, {"B": 16, "r": 256, "M": 256, "V": 3000}),
                                          (1, 129, {"B": 5, "r": 128, "M": 128, "V": 1000})])
 def test_latent_parity(wl_id, N, over, path):
     inp, xh = _latent_case(wl_id, N, **over)
