@@ -394,8 +394,9 @@ __global__ __launch_bounds__(256) void fold_embedding_kernel(const uint16_t* __r
 // of latent_share_kernel takes block n and the 64 SwiGLU units g*64 .. g*64+63 (G = M/64
 // workgroups per block):
 //   0. the block's tokens (block_tokens_*; inside a step this finishes the previous pass);
-//   1. x[b, c] = xh[b, c] + w1p[tok(b), c]            thread c < r, all 16 slots in registers;
-//   2. u[b, c] = sum_{j<=b} L[b, j, c] x[j, c]          same thread, taps in registers;
+//   1. x[b, c] = xh[b, c] + w1p[tok(b), c]            16-byte rows into LDS;
+//   2. u[b, c] = sum_{j<=b} L[b, j, c] x[j, c]          lane l: channels CL*l .. +CL-1 (CL = r/64)
+//                                                       of the wave's rows mix_row(wave, 0..3);
 //   3. a = w_gate[units] . u, e = w_up[units] . u,  s = silu(a) * e   (16x16x32 MFMAs);
 //   4. share_g = w_down[:, units] . s (+ u for g = 0), written to dpart for slots 1..B-1.
 // latent_sum_kernel then adds the G shares of each slot in slice order into lat (bf16): a fixed
@@ -418,15 +419,18 @@ __global__ __launch_bounds__(256) void latent_share_kernel(
   constexpr int SP = UPW + 8;  // bf16 row pitch of s_s
   constexpr int UW = UPW / 16;  // waves with units
   constexpr int DK = UPW / 32;  // k steps of the down product
+  constexpr int CL = R / 64;    // mixer channels per lane
+  constexpr int CW = (CL + 1) / 2;  // 32-bit words of a lane's CL taps
+  constexpr int QR = R / 4;     // float4 per x row
+  constexpr int NXI = 16 * QR / 256;  // float4 of the x tile per thread
   __shared__ int64_t s_tok[16];
-  __shared__ float s_u32[16][R];
+  __shared__ __align__(16) float s_x[16][R];
+  __shared__ __align__(16) float s_u32[16][R];
   __shared__ __align__(16) uint16_t s_u[16][UP];
   __shared__ __align__(16) uint16_t s_s[16][SP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, q4 = lane >> 4;
   const int n = blockIdx.x, g = blockIdx.y, G = gridDim.y;
-  const bool chan = tid < R;  // thread tid owns channel tid in steps 1-2
-  const int c = min(tid, R - 1);
 
   // The previous pass's partials head the dependency chain (partials -> tokens -> w1p rows), so
   // their loads are issued first (1% faster steps than issuing them after the others); then the
@@ -446,54 +450,109 @@ __global__ __launch_bounds__(256) void latent_share_kernel(
   }
   // Every load below is unconditional, at an index clamped into range, and a select drops what
   // is not wanted: a load under a condition becomes a branch with its own wait, one memory
-  // round trip at a time.
-  float x[16];
+  // round trip at a time. xh: thread tid takes the float4 tid + 256 i of the [16, r] x tile.
+  float4 xv[NXI];
 #pragma unroll
-  for (int b = 0; b < 16; ++b) x[b] = xh[((int64_t)n * B + min(b, B - 1)) * R + c];
-  // taps L[b, j, c] for j <= b (mix_L is [B, B, r], channel innermost: one coalesced 2-byte load
-  // across the wave per tap); slots b >= B are zeroed after the mixer
-  uint16_t tap[136];
-#pragma unroll
-  for (int b = 0, k = 0; b < 16; ++b)
-#pragma unroll
-    for (int j = 0; j <= b; ++j, ++k)
-      tap[k] = mix_L[((int64_t)min(b, B - 1) * B + min(j, B - 1)) * R + c];
+  for (int i = 0; i < NXI; ++i) {
+    const int idx = tid + 256 * i, b = idx / QR;
+    xv[i] = *reinterpret_cast<const float4*>(xh + ((int64_t)n * B + min(b, B - 1)) * R + 4 * (idx % QR));
+  }
+  // taps L[b, j, c] of the lane's CL channels for the wave's rows mix_row(wave, 0..3), j <= b
+  // (mix_L is [B, B, r], channel innermost: one coalesced 2*CL-byte load per tap across the
+  // wave). The wave index is uniform, so each wave runs its own copy of the loads and of the
+  // mixer, with every index known at compile time. Rows b >= B are zeroed after the mixer.
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t tap[34][CW];
+  auto load_taps = [&](auto wc) __attribute__((always_inline)) {
+    constexpr int W = decltype(wc)::value;
+    static_for<0, 4>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int K = decltype(kc)::value, b = mix_row(W, K), e0 = mix_tap0(W, K);
+      static_for<0, b + 1>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        const uint16_t* t = mix_L + (int64_t)(min(b, B - 1) * B + min(j, B - 1)) * R + CL * lane;
+        if constexpr (CL == 4) {
+          const uint2 v = *reinterpret_cast<const uint2*>(t);
+          tap[e0 + j][0] = v.x;
+          tap[e0 + j][1] = v.y;
+        } else if constexpr (CL == 2) {
+          tap[e0 + j][0] = *reinterpret_cast<const uint32_t*>(t);
+        } else {
+          tap[e0 + j][0] = *t;
+        }
+      });
+    });
+  };
+  static_for<0, 4>([&](auto wc) __attribute__((always_inline)) {
+    if (wave_s == decltype(wc)::value) load_taps(wc);
+  });
 
   block_tokens_finish(part != nullptr, qp, blk, am1, n, B, g == 0, flags, pass, s_tok);
   __syncthreads();
 
-  // steps 1-2
+  // step 1: the x tile into LDS
   {
-    float e[16];
-    bool ok[16];
+    float4 e[NXI];
+    bool ok[NXI];
 #pragma unroll
-    for (int b = 0; b < 16; ++b) {
+    for (int i = 0; i < NXI; ++i) {
+      const int idx = tid + 256 * i, b = idx / QR;
       const int64_t t = s_tok[b];
-      ok[b] = b < B && t >= 0 && t < V;  // slots past B and ids outside [0, V): zero
-      e[b] = w1p[(ok[b] ? t : 0) * R + c];
+      ok[i] = b < B && t >= 0 && t < V;  // slots past B and ids outside [0, V): zero
+      e[i] = *reinterpret_cast<const float4*>(w1p + (ok[i] ? t : 0) * R + 4 * (idx % QR));
     }
-    // all 16 rows in flight before the first is used (otherwise each load sinks into the branch
-    // on b < B next to its use)
-    asm volatile("" : "+v"(e[0]), "+v"(e[1]), "+v"(e[2]), "+v"(e[3]), "+v"(e[4]), "+v"(e[5]),
-                 "+v"(e[6]), "+v"(e[7]), "+v"(e[8]), "+v"(e[9]), "+v"(e[10]), "+v"(e[11]),
-                 "+v"(e[12]), "+v"(e[13]), "+v"(e[14]), "+v"(e[15]));
 #pragma unroll
-    for (int b = 0; b < 16; ++b) x[b] = b < B ? x[b] + (ok[b] ? e[b] : 0.f) : 0.f;
-    float u[16];
-#pragma unroll
-    for (int b = 0, k = 0; b < 16; ++b) {
-      float acc = 0.f;
-#pragma unroll
-      for (int j = 0; j <= b; ++j, ++k) acc = fmaf(bf16_to_f32(tap[k]), x[j], acc);
-      u[b] = b < B ? acc : 0.f;
+    for (int i = 0; i < NXI; ++i) {
+      const int idx = tid + 256 * i, b = idx / QR;
+      const bool live = b < B;
+      float4 x;
+      x.x = live ? xv[i].x + (ok[i] ? e[i].x : 0.f) : 0.f;
+      x.y = live ? xv[i].y + (ok[i] ? e[i].y : 0.f) : 0.f;
+      x.z = live ? xv[i].z + (ok[i] ? e[i].z : 0.f) : 0.f;
+      x.w = live ? xv[i].w + (ok[i] ? e[i].w : 0.f) : 0.f;
+      *reinterpret_cast<float4*>(&s_x[b][4 * (idx % QR)]) = x;
     }
-    if (chan) {
+  }
+  __syncthreads();
+  // step 2: the mixer rows of the wave, lane channels CL*lane .. +CL-1
+  {
+    float x[16][CL];
 #pragma unroll
-      for (int b = 0; b < 16; ++b) {
-        s_u32[b][c] = u[b];
-        s_u[b][c] = f32_to_bf16(u[b]);
+    for (int j = 0; j < 16; ++j) {
+      if constexpr (CL == 4) {
+        const float4 v = *reinterpret_cast<const float4*>(&s_x[j][4 * lane]);
+        x[j][0] = v.x; x[j][1] = v.y; x[j][2] = v.z; x[j][3] = v.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < CL; ++e) x[j][e] = s_x[j][CL * lane + e];
       }
     }
+    auto mix = [&](auto wc) __attribute__((always_inline)) {
+      constexpr int W = decltype(wc)::value;
+      static_for<0, 4>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int K = decltype(kc)::value, b = mix_row(W, K), e0 = mix_tap0(W, K);
+        float u[CL];
+#pragma unroll
+        for (int e = 0; e < CL; ++e) u[e] = 0.f;
+        static_for<0, b + 1>([&](auto jc) __attribute__((always_inline)) {
+          constexpr int j = decltype(jc)::value;
+#pragma unroll
+          for (int e = 0; e < CL; ++e) {
+            const uint32_t w = tap[e0 + j][e / 2];
+            const float l = __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+            u[e] = fmaf(l, x[j][e], u[e]);
+          }
+        });
+#pragma unroll
+        for (int e = 0; e < CL; ++e) {
+          u[e] = b < B ? u[e] : 0.f;
+          s_u32[b][CL * lane + e] = u[e];
+          s_u[b][CL * lane + e] = f32_to_bf16(u[e]);
+        }
+      });
+    };
+    static_for<0, 4>([&](auto wc) __attribute__((always_inline)) {
+      if (wave_s == decltype(wc)::value) mix(wc);
+    });
   }
   // the slice's w_down columns, needed after the gate products
   bf16x8 dB[DT][DK];

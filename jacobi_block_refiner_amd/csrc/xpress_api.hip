@@ -82,7 +82,7 @@ xpress_status check_weights(const xpress_weights* w, bool need_hidden, bool need
       return fail(XPRESS_ERR_ARG, "M=%d not in {64,128,256,512,1024}", M);
     XP_PTR(w->w1);
     XP_PTR(w->in_proj);
-    if (w->mix_L == nullptr) return fail(XPRESS_ERR_ARG, "w->mix_L is NULL");
+    XP_PTR(w->mix_L);
     XP_PTR(w->w_gate);
     XP_PTR(w->w_up);
     XP_PTR(w->w_down);
