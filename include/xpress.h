@@ -32,8 +32,8 @@
  *   - N == 0 is a no-op that returns XPRESS_OK.
  *   - Supported shapes on the GPU path: r in {64, 128, 256}; 2 <= B <= 16; M in
  *     {64, 128, 256, 512, 1024}; H a multiple of 64 in [64, 16384]; V >= 1 and V*r < 2^31; all
- *     pointers 16-byte aligned and base_ld a multiple of 8 elements. Other values are
- *     XPRESS_ERR_ARG.
+ *     pointers 16-byte aligned and base_ld a multiple of 8 elements, V <= base_ld <= 2^27.
+ *     Other values are XPRESS_ERR_ARG.
  *   - Capacity: a workspace sized by xpress_workspace_size(n_max, ...) serves every N <= n_max;
  *     a call whose N needs more than ws_bytes (N beyond the n_max the workspace was sized for,
  *     among other cases) returns XPRESS_ERR_WORKSPACE before enqueueing anything. That one

@@ -134,12 +134,16 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
   const bool active = wave * RW < TR && row0 + wave * RW * 32 < rows;
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)&s_stage[0][0];
-  // Per-lane byte offsets of the copies, relative to the step's w2 tile and to the chunk's base
-  // rows at the step's first id (loop-invariant; the step only moves the scalar base pointers).
-  // In the last step of the vocabulary, ids past V are clamped instead (w2 row V-1, the padded
-  // row's last chunk). Copy instruction ins, lane j of the w2 tile carries chunk j % RQ of A-row
-  // (j / RQ) * NI + ins.
+  // Per-lane byte offsets of the copies, relative to the step's w2 tile and to the first base row
+  // of the copy instruction at the step's first id (loop-invariant; the step only moves the
+  // scalar base pointers). A base copy instruction covers 16 rows, and its first row's offset
+  // from the chunk (rowb, uniform) is added to the scalar pointer, so a lane offset spans at most
+  // 15 rows: 32 bits hold it for any base_ld <= 2^27. In the last step of the vocabulary, ids
+  // past V are clamped instead (w2 row V-1, the padded row's last chunk). Copy instruction ins,
+  // lane j of the w2 tile carries chunk j % RQ of A-row (j / RQ) * NI + ins.
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   uint32_t offw[WI], offb[BI];
+  int64_t rowb[BI];
 #pragma unroll
   for (int q = 0; q < WI; ++q) {
     const int ins = (wave + q * kNW) % NI;
@@ -148,9 +152,12 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
   }
 #pragma unroll
   for (int q = 0; q < BI; ++q) {
-    const int p = ((wave + q * kNW) % NBI) * 64 + lane;  // base chunk position
+    const int ins = (wave_s + q * kNW) % NBI;
+    const int r_ins = min(row0 + 16 * ins, rows - 1) - row0;  // the instruction's first row
+    rowb[q] = (int64_t)r_ins * ld * 2;
+    const int p = ins * 64 + lane;  // base chunk position
     const int rr = p >> 2, c = (p & 3) ^ ((rr >> 2) & 3);
-    offb[q] = (uint32_t)(((int64_t)(min(row0 + rr, rows - 1) - row0) * ld + 8 * c) * 2);
+    offb[q] = (uint32_t)(((int64_t)(min(row0 + rr, rows - 1) - row0 - r_ins) * ld + 8 * c) * 2);
   }
   const uint16_t* base_rc = base + (int64_t)row0 * ld;
   // The lane id, recomputed where it is used: the clamped offsets of the vocabulary's last step
@@ -164,7 +171,6 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
   // Issue the copies of step t into stage st. The LDS destinations are scalar (the wave index is
   // uniform), and one uniform branch per step picks the clamped offsets of the vocabulary's last
   // step, so the common path is the copies alone.
-  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   auto copy_step = [&](int t, int st) __attribute__((always_inline)) {
     const uint32_t sbase = lds0 + (uint32_t)st * (SCH * 16);
     const uint16_t* gw = w2 + (int64_t)t * 32 * R;
@@ -181,11 +187,12 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
 #pragma unroll
       for (int q = 0; q < BI; ++q) {
         const int ins = (wave_s + q * kNW) % NBI;
+        const int r_ins = min(row0 + 16 * ins, rows - 1) - row0;
         const int p = ins * 64 + opaque_lane_id();
         const int rr = p >> 2, c = (p & 3) ^ ((rr >> 2) & 3);
-        const uint32_t off = (uint32_t)(((int64_t)(min(row0 + rr, rows - 1) - row0) * ld +
+        const uint32_t off = (uint32_t)(((int64_t)(min(row0 + rr, rows - 1) - row0 - r_ins) * ld +
                                          8 * (min(4 * t + c, last_chunk) - 4 * t)) * 2);
-        lds_copy16(gb, off, sbase + (WCH + ins * 64) * 16);
+        lds_copy16(reinterpret_cast<const char*>(gb) + rowb[q], off, sbase + (WCH + ins * 64) * 16);
       }
     } else {
 #pragma unroll
@@ -193,7 +200,8 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
         lds_copy16(gw, offw[q], sbase + ((wave_s + q * kNW) % NI) * WP * 16);
 #pragma unroll
       for (int q = 0; q < BI; ++q)
-        lds_copy16(gb, offb[q], sbase + (WCH + ((wave_s + q * kNW) % NBI) * 64) * 16);
+        lds_copy16(reinterpret_cast<const char*>(gb) + rowb[q], offb[q],
+                   sbase + (WCH + ((wave_s + q * kNW) % NBI) * 64) * 16);
     }
   };
 

@@ -42,6 +42,9 @@ xpress_status hip_check(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The readout's base copies address 16 rows from one scalar pointer with 32-bit lane offsets.
+constexpr int64_t kMaxBaseLd = (int64_t)1 << 27;
+
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 xpress_status check_ptr(const void* p, const char* name) {
@@ -102,8 +105,9 @@ xpress_status check_layout(uint32_t lat_layout) {
 
 xpress_status check_base(const xpress_bf16* base, int64_t ld, int64_t V) {
   XP_PTR(base);
-  if (ld < V || ld % 8) return fail(XPRESS_ERR_ARG, "base_ld=%lld must be >= V=%lld and a multiple of 8",
-                                    (long long)ld, (long long)V);
+  if (ld < V || ld % 8 || ld > kMaxBaseLd)
+    return fail(XPRESS_ERR_ARG, "base_ld=%lld must be >= V=%lld, a multiple of 8 and at most 2^27",
+                (long long)ld, (long long)V);
   return XPRESS_OK;
 }
 

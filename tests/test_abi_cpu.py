@@ -83,6 +83,11 @@ def test_small_workspace_and_bad_stride_are_rejected():
     st = L.xpress_readout_argmax(ctypes.byref(w), misaligned, 0, fake, 151936, 4, fake, None, fake,
                                  1 << 30, None)
     assert st == xpress.ERR_ARG and b"aligned" in L.xpress_last_error()
+    # a base row stride past 2^27 elements is refused (the readout's 32-bit copy offsets)
+    for ld in ((1 << 27) + 8, 1 << 28):
+        st = L.xpress_readout_argmax(ctypes.byref(w), fake, 0, fake, ld, 4, fake, None, fake,
+                                     1 << 30, None)
+        assert st == xpress.ERR_ARG and b"base_ld" in L.xpress_last_error()
 
 
 def test_fold_embedding_and_table_arguments_are_checked():

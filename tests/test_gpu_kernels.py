@@ -150,6 +150,36 @@ def test_readout_partials_per_range_and_reduce(r, V, N):
     assert torch.equal(blk_two, blk_one)
 
 
+# A base row stride of 2^23 elements: a 512-row chunk (32 blocks) spans 8 GB of base and a
+# 256-row chunk (17 blocks) 4.3 GB, beyond what a 32-bit byte offset from one pointer reaches; a
+# single request's 32-row chunk stays below it
+@pytest.mark.parametrize("N", [1, 17, 32])
+def test_readout_and_starting_block_with_a_large_base_stride(N):
+    B, r, V, LD = 16, 256, 5003, 1 << 23
+    lat, w2, base = _readout_case(11, N, B, r, V)
+    w = _weights_with(w2, r, B, V)
+    dense = upload.base_logits(base)
+    log(f"readout with base_ld = 2^23, N={N}")
+    big = torch.empty((dense.shape[0], LD), dtype=torch.bfloat16, device="cuda")
+    big[:, :8 * -(-V // 8)].zero_()  # the row padding up to a multiple of 8 ids
+    view = big[:, :V]
+    view.copy_(dense)
+    assert view.stride(0) == LD
+    ws = xpress.alloc_workspace(N, B, r, V, 0, 1)
+    blk_big = torch.zeros(N, B, dtype=torch.int64, device="cuda")
+    xpress.readout_argmax(w, upload.bf16_tensor(lat), view, blk_big, ws)
+    anchor = upload.tokens(np.arange(N))
+    start = torch.zeros(N, B, dtype=torch.int64, device="cuda")
+    xpress.initial_block(view, anchor, start)
+    torch.cuda.synchronize()
+    best, _, _ = O.readout_argmax(lat, w2, base)
+    assert np.array_equal(draft_rows(blk_big.cpu().numpy()), best)
+    want = O.initial_block(base, np.arange(N), N, B)
+    assert np.array_equal(start.cpu().numpy(), want)
+    del big, view
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("V", [1, 7, 31, 33])
 def test_readout_argmax_small_vocabulary(V):
     """A vocabulary of fewer ids than one 32-id step (or just past it): the single partial step's
