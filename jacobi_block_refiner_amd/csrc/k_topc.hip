@@ -254,40 +254,57 @@ __device__ __forceinline__ uint32_t radix_kth(const uint32_t* keys, int n, int k
 }
 
 // LDS of one row's selection (the caller's, so that a launch with other work can overlay it).
-constexpr int kHC = 4096;  // chunk-list capacity
-struct SelLds {
-  uint32_t hist[512];
+// The chunk maxima of a row of up to kCmaxLds chunks (153,600 ids) stay in LDS from the first pass
+// to the chunk list, where the buffer's ids and values later go; longer rows keep them in the
+// caller's global buffer. The chunk list holds at most kBuf chunks: each listed chunk holds an
+// element of the buffer, so a longer list would overflow the buffer anyway.
+constexpr int kCmaxLds = 19200;
+struct alignas(16) SelLds {
+  uint32_t hist[256];
   int tmp[4];
   uint32_t par[4];
   int tmp_r[4];        // radix_kth's scan
   uint32_t key[kBuf];  // key + 1 (0: empty)
-  int id[kBuf];
-  uint16_t bits[kBuf];  // the buffered values' bf16 bits
-  int hc[kHC];          // chunks whose maximum can hold an answer, ascending
-  float bv[4];          // the starting block's per-wave winners
+  union alignas(16) Shared {
+    struct {
+      int id[kBuf];
+      uint16_t bits[kBuf];  // the buffered values' bf16 bits
+    } buf;
+    uint16_t cmax[kCmaxLds];  // bf16 bits of the chunk maxima (first pass to chunk list)
+  } u;
+  uint16_t hc[kBuf];    // chunks whose maximum can hold an answer, ascending
+  uint32_t bk[4];       // the starting block's per-wave winners (key + 1, id)
   int bi[4];
+  float bv[4];
 };
 
-__device__ __forceinline__ void topc_select_row(int p, const uint16_t* __restrict__ base,
+// Returns whether the buffered path ran; then, with start_slot given, the row's best id (largest
+// value, lowest id) has been written there from the buffer.
+__device__ __forceinline__ bool topc_select_row(int p, const uint16_t* __restrict__ base,
                                                 int64_t ld, int64_t V, int c,
                                                 int64_t* __restrict__ cand,
                                                 uint16_t* __restrict__ base_c,
-                                                uint16_t* __restrict__ cmax, SelLds& L) {
+                                                uint16_t* __restrict__ cmax, SelLds& L,
+                                                int64_t* __restrict__ start_slot) {
   uint32_t* s_hist = L.hist;
   int* s_tmp = L.tmp;
   uint32_t* s_par = L.par;
   uint32_t* s_key = L.key;
-  int* s_id = L.id;
-  uint16_t* s_bits = L.bits;
-  int* s_hc = L.hc;
+  int* s_id = L.u.buf.id;
+  uint16_t* s_bits = L.u.buf.bits;
+  uint16_t* s_hc = L.hc;
   const int tid = threadIdx.x, lane = tid & 63;
   const uint16_t* row = base + (int64_t)p * ld;
   int64_t* out_id = cand + (int64_t)p * c;
   uint16_t* out_b = base_c + (int64_t)p * c;
   const int64_t nchunk = (V + 7) / 8;
-  if (c > 1024 || nchunk > (int64_t)256 * 1024) {
+  const int64_t nchunk8 = (nchunk + 7) / 8 * 8;
+  const bool cm_lds = nchunk8 <= kCmaxLds;  // the chunk maxima in LDS (else in `cmax`)
+  // the chunk list holds 16-bit chunk indexes; without chunk maxima (a long row and no
+  // workspace) the exact whole-row path runs
+  if (c > 1024 || nchunk > 65536 || (!cm_lds && cmax == nullptr)) {
     select_row_exact(row, V, c, out_id, out_b, s_hist, s_tmp, s_par);
-    return;
+    return false;
   }
   // The two passes over the row load kLB chunks per thread before using any of them, so enough
   // bytes are in flight to stream the row (one chunk at a time is latency-bound). Rows are padded
@@ -320,10 +337,10 @@ __device__ __forceinline__ void topc_select_row(int p, const uint16_t* __restric
   auto key1_of = [](float v) __attribute__((always_inline)) {
     return order_key(__float_as_uint(v) >> 16) + 1;
   };
-  // chunk maxima (bf16 bits), written by pass 1 when a buffer is given, read back by pass 3 so
-  // that it re-reads only the chunks that can hold an answer
-  const int64_t nchunk8 = (nchunk + 7) / 8 * 8;
-  uint16_t* cmax_row = cmax ? cmax + (int64_t)p * nchunk8 : nullptr;
+  // chunk maxima (bf16 bits), written by pass 1 and read back by pass 3 so that it re-reads only
+  // the chunks that can hold an answer
+  uint16_t* cmax_row = cm_lds ? nullptr : cmax + (int64_t)p * nchunk8;
+  uint16_t* s_cm = L.u.cmax;
   // 1. group maxima: thread tid visits chunks tid + 256 i; groups of gv visits (<= 8 groups)
   const int nv_max = (int)((nchunk + 255) / 256);
   const int gv = (nv_max + 7) / 8;
@@ -341,7 +358,11 @@ __device__ __forceinline__ void topc_select_row(int p, const uint16_t* __restric
           widen(q, raw[u], x);
           const float cm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                                  fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-          if (cmax_row) cmax_row[q] = (uint16_t)(__float_as_uint(cm) >> 16);  // -inf: 0xff80
+          const uint16_t cb = (uint16_t)(__float_as_uint(cm) >> 16);  // -inf: 0xff80
+          if (cm_lds)
+            s_cm[q] = cb;
+          else
+            cmax_row[q] = cb;
           gm = fmaxf(gm, cm);
           if (++inside == gv) {
             s_key[tid * 8 + g] = gm > -INFINITY ? key1_of(gm) : 0u;
@@ -354,8 +375,12 @@ __device__ __forceinline__ void topc_select_row(int p, const uint16_t* __restric
     }
     if (inside) s_key[tid * 8 + g++] = gm > -INFINITY ? key1_of(gm) : 0u;
     for (; g < 8; ++g) s_key[tid * 8 + g] = 0;
-    if (cmax_row)  // the padding up to a multiple of 8 chunk maxima: -inf
-      for (int64_t q = nchunk + tid; q < nchunk8; q += 256) cmax_row[q] = 0xff80u;
+    for (int64_t q = nchunk + tid; q < nchunk8; q += 256) {  // padding to 8 chunk maxima: -inf
+      if (cm_lds)
+        s_cm[q] = 0xff80u;
+      else
+        cmax_row[q] = 0xff80u;
+    }
   }
   __threadfence_block();
   __syncthreads();
@@ -377,12 +402,7 @@ __device__ __forceinline__ void topc_select_row(int p, const uint16_t* __restric
   }
   for (int j = tid; j < kBuf; j += 256) s_key[j] = 0;
   __syncthreads();
-  // 3. Every element with value >= v0 into the buffer, in ascending id order; without chunk
-  // maxima (no workspace) the exact whole-row path runs instead.
-  if (cmax_row == nullptr) {
-    select_row_exact(row, V, c, out_id, out_b, s_hist, s_tmp, s_par);
-    return;
-  }
+  // 3. Every element with value >= v0 into the buffer, in ascending id order.
   // 3a. The chunks whose maximum reaches v0, listed in ascending order: per round, thread tid takes
   // the kLB consecutive groups of 8 chunk maxima g0 + kLB*tid .. +kLB-1 (128 contiguous bytes,
   // all read before any is used); one block-wide exclusive scan of the threads' hit counts places
@@ -390,13 +410,17 @@ __device__ __forceinline__ void topc_select_row(int p, const uint16_t* __restric
   // of 151936 ids). A list that would overflow sends the row to the exact path.
   const int64_t n8 = nchunk8 / 8;
   const uint4* cm4 = reinterpret_cast<const uint4*>(cmax_row);
+  const uint4* s_cm4 = reinterpret_cast<const uint4*>(s_cm);
   int nhc = 0;  // uniform
   for (int64_t g0 = 0; g0 < n8; g0 += 256 * kLB) {
     uint4 m8[kLB];
 #pragma unroll
     for (int u = 0; u < kLB; ++u) {
       const int64_t g = g0 + kLB * tid + u;
-      m8[u] = g < n8 ? cm4[g] : make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
+      const bool in = g < n8;
+      const int64_t gc = in ? g : 0;
+      m8[u] = cm_lds ? s_cm4[gc] : cm4[gc];
+      if (!in) m8[u] = make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
     }
     uint64_t hm = 0;  // bit 8u + e: chunk 8 (g0 + kLB*tid + u) + e reaches v0
 #pragma unroll
@@ -413,17 +437,18 @@ __device__ __forceinline__ void topc_select_row(int p, const uint16_t* __restric
     const int64_t c0 = (g0 + kLB * tid) * 8;
     while (hm) {  // the thread's hits in ascending order
       const int bit = __ffsll((unsigned long long)hm) - 1;
-      if (pos < kHC) s_hc[pos] = (int)(c0 + bit);
+      if (pos < kBuf) s_hc[pos] = (uint16_t)(c0 + bit);
       ++pos;
       hm &= hm - 1;
     }
     nhc += tot;
   }
-  if (nhc > kHC) {  // uniform
+  if (nhc > kBuf) {  // uniform
     select_row_exact(row, V, c, out_id, out_b, s_hist, s_tmp, s_par);
-    return;
+    return false;
   }
-  __syncthreads();  // the list is complete
+  __syncthreads();  // the list is complete (and the chunk maxima, which share LDS with the
+                    // buffer's ids and values, are no longer read)
   // 3b. The listed chunks' elements >= v0 appended in list order (ascending ids): per round,
   // thread tid reads chunk tid of the round (up to four rounds' reads issued together), and a
   // block-wide scan places its hits. More than kBuf of them, or fewer than c, sends the row to the
@@ -466,7 +491,7 @@ __device__ __forceinline__ void topc_select_row(int p, const uint16_t* __restric
   // c buffered elements; the exact path orders every bit pattern by its key
   if (nbuf > kBuf || nbuf < c) {  // uniform
     select_row_exact(row, V, c, out_id, out_b, s_hist, s_tmp, s_par);
-    return;
+    return false;
   }
   __syncthreads();
   // 4. The threshold T (c-th largest key of the buffer; empty slots are 0), then one ordered
@@ -499,6 +524,41 @@ __device__ __forceinline__ void topc_select_row(int p, const uint16_t* __restric
       out_b[pos] = s_bits[8 * tid + e];
       ++pos;
     }
+  if (start_slot) {  // uniform: the best buffered element (largest key, lowest id)
+    const int wave = tid >> 6;
+    uint32_t bk = 0;
+    int bid = INT_MAX;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int id = s_id[8 * tid + e];
+      const bool take = k8[e] > bk || (k8[e] != 0 && k8[e] == bk && id < bid);
+      bk = take ? k8[e] : bk;
+      bid = take ? id : bid;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const uint32_t ok = (uint32_t)__shfl_xor((int)bk, off);
+      const int oi = __shfl_xor(bid, off);
+      const bool take = ok > bk || (ok != 0 && ok == bk && oi < bid);
+      bk = take ? ok : bk;
+      bid = take ? oi : bid;
+    }
+    if (lane == 0) {
+      L.bk[wave] = bk;
+      L.bi[wave] = bid;
+    }
+    __syncthreads();
+    if (tid == 0) {
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        const bool take = L.bk[w] > bk || (L.bk[w] != 0 && L.bk[w] == bk && L.bi[w] < bid);
+        bk = take ? L.bk[w] : bk;
+        bid = take ? L.bi[w] : bid;
+      }
+      *start_slot = bid;
+    }
+  }
+  return true;
 }
 
 // Draft row p, by one workgroup: the row's candidate set; with blk given, also the row's starting
@@ -513,10 +573,13 @@ __device__ __forceinline__ void topc_select_block(int p, const uint16_t* __restr
                                                   const int64_t* __restrict__ anchor,
                                                   int64_t* __restrict__ blk, int B,
                                                   uint16_t* __restrict__ cmax, SelLds& L) {
-  topc_select_row(p, base, ld, V, c, cand, base_c, cmax, L);
+  int64_t* slot = blk ? blk + (int64_t)(p / (B - 1)) * B + 1 + p % (B - 1) : nullptr;
+  const bool buffered = topc_select_row(p, base, ld, V, c, cand, base_c, cmax, L, slot);
   if (!blk) return;
   // the block's first row also stores the anchor in slot 0
   if (p % (B - 1) == 0 && threadIdx.x == 0) blk[(int64_t)(p / (B - 1)) * B] = anchor[p / (B - 1)];
+  if (buffered) return;  // uniform: the starting token is written
+  // the exact path: the best of the candidates it wrote
   float* s_bv = L.bv;
   int* s_bi = L.bi;
   __threadfence_block();
@@ -541,7 +604,7 @@ __device__ __forceinline__ void topc_select_block(int p, const uint16_t* __restr
   if (tid == 0) {
 #pragma unroll
     for (int w = 1; w < 4; ++w) argmax_merge(bv, bi, s_bv[w], s_bi[w]);
-    blk[(int64_t)(p / (B - 1)) * B + 1 + p % (B - 1)] = bi;
+    *slot = bi;
   }
 }
 

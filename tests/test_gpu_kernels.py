@@ -480,14 +480,16 @@ def test_step_fixed_k_runs_every_pass_and_is_deterministic():
 # top-C
 
 def _select_scratch(rows, V):
-    """Scratch for the selection's chunk maxima (rows x 8-aligned chunk count, 2 bytes each): with
-    it, the second pass re-reads only the chunks that can hold an answer."""
+    """Scratch for the selection's chunk maxima (rows x 8-aligned chunk count, 2 bytes each). Rows
+    of up to 153,600 ids keep them in LDS; longer rows need this buffer for the second pass to
+    re-read only the chunks that can hold an answer (without it they take the exact path)."""
     nchunk8 = ((V + 7) // 8 + 7) // 8 * 8
     return torch.empty(rows * nchunk8 * 2, dtype=torch.uint8, device="cuda")
 
 
 @pytest.mark.parametrize("chunk_maxima", [False, True])
-@pytest.mark.parametrize("C,V", [(64, 5003), (512, 8192), (700, 700), (1, 3000), (5, 7), (40, 33)])
+@pytest.mark.parametrize("C,V", [(64, 5003), (512, 8192), (700, 700), (1, 3000), (5, 7), (40, 33),
+                                 (512, 153600), (64, 153608), (512, 200003)])
 def test_topc_prepare_exact(C, V, chunk_maxima):
     rng = np.random.default_rng(6)
     N, B, r = 3, 16, 64
@@ -512,7 +514,7 @@ def test_topc_prepare_exact(C, V, chunk_maxima):
 
 
 @pytest.mark.parametrize("chunk_maxima", [False, True])
-@pytest.mark.parametrize("C,V", [(512, 8192), (64, 5003), (1024, 20000)])
+@pytest.mark.parametrize("C,V", [(512, 8192), (64, 5003), (1024, 20000), (512, 160000)])
 def test_topc_prepare_adversarial_rows(C, V, chunk_maxima):
     """Rows that defeat a per-thread shortlist (sorted rows, the answer concentrated in the ids one
     thread visits, very few distinct values) must still give the exact candidate sets."""
