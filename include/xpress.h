@@ -205,10 +205,12 @@ xpress_status xpress_argmax_reduce(const uint32_t* part, int32_t ntiles, int32_t
  * xpress_readout_argmax_topc_ids, which reads the rows from w2 through cand).
  * cand: [N*(B-1), c] int64; base_c: [N*(B-1), c] bf16; w2c: [N*(B-1), c, r] bf16 (written;
  * nullable, else 16-byte aligned).
- * ws (optional, may be NULL): device scratch; when it is 16-byte aligned and holds at least
- * N*(B-1) * 8*ceil(ceil(V/8)/8) * 2 bytes, the selection keeps per-chunk maxima there and its
- * second pass over base reads only the chunks that can hold an answer (same result, less
- * traffic); otherwise it reads base twice. xpress_jacobi_step's workspace includes this. */
+ * ws (optional, may be NULL): device scratch for rows of more than 153,600 ids (rows up to that
+ * length keep the selection's per-chunk maxima in LDS and ignore ws). For rows of 153,601 to
+ * 524,288 ids, when ws is 16-byte aligned and holds at least N*(B-1) * 8*ceil(ceil(V/8)/8) * 2
+ * bytes, the selection keeps per-chunk maxima there and its second pass over base reads only the
+ * chunks that can hold an answer; otherwise (and for longer rows) it reads base three times. The
+ * result is the same either way. xpress_jacobi_step's workspace includes this. */
 xpress_status xpress_topc_prepare(const xpress_weights* w, const xpress_bf16* base,
                                   int64_t base_ld, int32_t N, int32_t C, int64_t* cand,
                                   xpress_bf16* base_c, xpress_bf16* w2c, void* ws,
@@ -256,8 +258,8 @@ xpress_status xpress_jacobi_step(const xpress_weights* w, const xpress_bf16* h,
  * and must be serialised by the caller; each call clears what it needs cleared itself, so
  * nothing carries over from the previous call. A step whose workspace (xpress_workspace_size for
  * its N, C and K) exceeds 64 MiB returns XPRESS_ERR_WORKSPACE before enqueueing anything: 64 MiB
- * covers a full-vocabulary step of up to 256 blocks and a top-512 step of up to 64 blocks at
- * B = 16, r = 256, V = 151936, K = 15. Arguments, results and other errors as in
+ * covers a full-vocabulary or top-512 step of up to 256 blocks at B = 16, r = 256, V = 151936,
+ * K = 15. Arguments, results and other errors as in
  * xpress_jacobi_step. */
 xpress_status xpress_jacobi_step_noalloc(const xpress_weights* w, const xpress_bf16* h,
                                          const xpress_bf16* base, int64_t base_ld,

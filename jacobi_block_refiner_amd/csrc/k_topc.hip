@@ -807,7 +807,10 @@ hipError_t launch_topc_start(const uint16_t* h, const uint16_t* down_h, const ui
 }
 
 size_t topc_select_scratch_bytes(int rows, int64_t V) {
-  const int64_t nchunk8 = ((V + 7) / 8 + 7) / 8 * 8;
+  const int64_t nchunk = (V + 7) / 8;
+  const int64_t nchunk8 = (nchunk + 7) / 8 * 8;
+  // short rows keep their chunk maxima in LDS; rows past 65536 chunks take the exact path
+  if (nchunk8 <= kCmaxLds || nchunk > 65536) return 0;
   return (size_t)rows * (size_t)nchunk8 * 2;
 }
 

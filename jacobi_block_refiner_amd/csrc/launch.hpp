@@ -77,8 +77,9 @@ hipError_t launch_argmax_reduce(const uint2* part, int ntiles, int rows, int B, 
 // K3: top-C candidate selection (+ base_c) and the w2 gather. With blk non-null the selection
 // also writes the starting block: each row's best candidate into blk[n, 1 + p % (B-1)] and the
 // anchor into blk[n, 0].
-// cmax (nullable, 16-byte aligned, topc_select_scratch_bytes long): per-chunk maxima that let
-// the selection's second pass re-read only the chunks that can hold an answer.
+// cmax (nullable, 16-byte aligned, topc_select_scratch_bytes long; 0 bytes for rows of up to
+// 153,600 ids, which keep them in LDS): per-chunk maxima that let the selection's second pass
+// re-read only the chunks that can hold an answer.
 hipError_t launch_topc_select(const uint16_t* base, int64_t ld, int rows, int64_t V, int c,
                               int64_t* cand, uint16_t* base_c, const int64_t* anchor, int64_t* blk,
                               int B, uint16_t* cmax, hipStream_t s);

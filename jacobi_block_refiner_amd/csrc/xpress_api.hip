@@ -170,9 +170,8 @@ T* at(void* ws, size_t off) {
 }
 
 // Library-owned workspace of the allocation-free step: one array per GPU, in the code object's
-// device globals, held until the process ends. 64 MiB covers a full-vocabulary step of up to 256
-// blocks (43.4 MiB at B = 16, r = 256, V = 151936, K = 15) and a top-512 step of up to 64 blocks
-// (62.9 MiB). In host code the name `scratch` is only a stand-in for the symbol; its device
+// device globals, held until the process ends. 64 MiB covers a full-vocabulary or top-512 step of
+// up to 256 blocks (43.4 and 54.6 MiB at B = 16, r = 256, V = 151936, K = 15). In host code the name `scratch` is only a stand-in for the symbol; its device
 // address on each GPU comes from hipGetSymbolAddress (scratch_ptr) and is what the kernels get.
 constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
 static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];

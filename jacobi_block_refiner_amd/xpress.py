@@ -116,6 +116,34 @@ def _bf16(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
+def _at_least(t, n: int, name: str) -> None:
+    """The C ABI takes bare pointers and a block count: a tensor shorter than that count implies
+    would be read or written past its end, so it is refused here."""
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements, fewer than the {n} that N implies")
+
+
+def _base_rows(base, rows: int, V: int) -> None:
+    _bf16(base, "base")
+    if base.stride(1) != 1 or base.dim() != 2:
+        raise ValueError("base must be a [rows, V] view with unit column stride")
+    if base.shape[0] < rows or base.shape[1] != V:
+        raise ValueError(f"base is {tuple(base.shape)}; the call needs [{rows}, {V}]")
+
+
+def _step_inputs(w, h, base, anchor, am1, blk) -> int:
+    """N from blk [N, B]; h, base, anchor and am1 must cover N blocks."""
+    d = w.dims
+    N, B = blk.shape
+    if B != d["B"]:
+        raise ValueError(f"blk has {B} slots per block, the weights {d['B']}")
+    _at_least(_bf16(h, "h"), N * B * d["H"], "h")
+    _base_rows(base, N * (B - 1), d["V"])
+    _at_least(anchor, N, "anchor")
+    _at_least(am1, N, "am1")
+    return N
+
+
 @dataclass
 class Weights:
     """Device bf16 weights of one refiner head, ``nn.Linear`` layouts; ``mix_L`` is folded and
@@ -191,15 +219,17 @@ def fold_embedding(w: Weights, out: torch.Tensor | None = None) -> torch.Tensor:
 def hidden_cache(w: Weights, h: torch.Tensor, xh: torch.Tensor, ws: torch.Tensor) -> torch.Tensor:
     s = w.struct()
     N = h.shape[0]
+    _at_least(_bf16(h, "h"), N * w.dims["B"] * w.dims["H"], "h")
+    _at_least(xh, N * w.dims["B"] * w.dims["r"], "xh")
     _check(lib().xpress_hidden_cache(ctypes.byref(s), _ptr(_bf16(h, "h")), N, _ptr(xh), _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream()))
     return xh
 
 
 def initial_block(base: torch.Tensor, anchor: torch.Tensor, blk: torch.Tensor) -> torch.Tensor:
-    _bf16(base, "base")
-    assert base.stride(1) == 1
     N, B = blk.shape
+    _base_rows(base, N * (B - 1), base.shape[1])
+    _at_least(anchor, N, "anchor")
     _check(lib().xpress_initial_block(ctypes.c_void_p(base.data_ptr()), base.stride(0),
                                       _ptr(anchor), N, B, base.shape[1], _ptr(blk), _stream()))
     return blk
@@ -216,6 +246,9 @@ def lat_buffer(N: int, B: int, r: int, layout: int = LAT_ROWS, device="cuda") ->
 def latent_pass(w: Weights, blk, am1, xh, lat, ws: torch.Tensor, layout: int = LAT_ROWS) -> torch.Tensor:
     s = w.struct()
     N = blk.shape[0]
+    _at_least(am1, N, "am1")
+    _at_least(xh, N * w.dims["B"] * w.dims["r"], "xh")
+    _at_least(lat, N * (w.dims["B"] - 1) * w.dims["r"], "lat")
     _check(lib().xpress_latent_pass(ctypes.byref(s), _ptr(blk), _ptr(am1), _ptr(xh), N,
                                     _ptr(lat), layout, _ptr(ws), ws.numel() * ws.element_size(),
                                     _stream()))
@@ -224,9 +257,9 @@ def latent_pass(w: Weights, blk, am1, xh, lat, ws: torch.Tensor, layout: int = L
 
 def readout_argmax(w: Weights, lat, base, blk, ws, changed=None, layout: int = LAT_ROWS) -> torch.Tensor:
     s = w.struct()
-    _bf16(base, "base")
-    assert base.stride(1) == 1
     N = blk.shape[0]
+    _base_rows(base, N * (w.dims["B"] - 1), w.dims["V"])
+    _at_least(lat, N * (w.dims["B"] - 1) * w.dims["r"], "lat")
     _check(lib().xpress_readout_argmax(ctypes.byref(s), _ptr(lat), layout,
                                        ctypes.c_void_p(base.data_ptr()), base.stride(0), N,
                                        _ptr(blk), _ptr(changed), _ptr(ws),
@@ -243,10 +276,10 @@ def readout_tiles(V: int, rows: int) -> int:
 def readout_partials(w: Weights, lat, base, part: torch.Tensor, layout: int = LAT_ROWS) -> torch.Tensor:
     """part: int32/uint32-compatible tensor [ntiles, rows, 2] (value bits, id), range-major."""
     s = w.struct()
-    _bf16(base, "base")
-    assert base.stride(1) == 1
     rows = part.shape[1]
     N = rows // (w.dims["B"] - 1)
+    _base_rows(base, N * (w.dims["B"] - 1), w.dims["V"])
+    _at_least(lat, N * (w.dims["B"] - 1) * w.dims["r"], "lat")
     _check(lib().xpress_readout_partials(ctypes.byref(s), _ptr(lat), layout,
                                          ctypes.c_void_p(base.data_ptr()), base.stride(0), N,
                                          _ptr(part), _stream()))
@@ -264,8 +297,7 @@ def argmax_reduce(part: torch.Tensor, blk: torch.Tensor, changed=None) -> torch.
 def topc_prepare(w: Weights, base, N: int, C: int, cand, base_c, w2c=None, ws=None):
     """w2c None: candidates and base_c only (for readout_argmax_topc_ids)."""
     s = w.struct()
-    _bf16(base, "base")
-    assert base.stride(1) == 1
+    _base_rows(base, N * (w.dims["B"] - 1), w.dims["V"])
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().xpress_topc_prepare(ctypes.byref(s), ctypes.c_void_p(base.data_ptr()),
                                      base.stride(0), N, C, _ptr(cand), _ptr(base_c), _ptr(w2c),
@@ -295,9 +327,7 @@ def readout_argmax_topc_ids(w: Weights, lat, base_c, cand, blk, changed=None) ->
 def jacobi_step(w: Weights, h, base, anchor, am1, blk, *, K: int, C: int = 0,
                 flags: int = INIT_FROM_BASE, ws: torch.Tensor, passes_run=None) -> torch.Tensor:
     s = w.struct()
-    _bf16(base, "base")
-    assert base.stride(1) == 1
-    N = blk.shape[0]
+    N = _step_inputs(w, h, base, anchor, am1, blk)
     _check(lib().xpress_jacobi_step(ctypes.byref(s), _ptr(_bf16(h, "h")),
                                     ctypes.c_void_p(base.data_ptr()), base.stride(0), _ptr(anchor),
                                     _ptr(am1), N, K, C, flags, _ptr(blk), _ptr(passes_run),
@@ -310,9 +340,7 @@ def jacobi_step_noalloc(w: Weights, h, base, anchor, am1, blk, *, K: int, C: int
     """``jacobi_step`` on the library's own static per-GPU scratch: no workspace argument and no
     allocation. Calls that overlap on one GPU share that scratch and race."""
     s = w.struct()
-    _bf16(base, "base")
-    assert base.stride(1) == 1
-    N = blk.shape[0]
+    N = _step_inputs(w, h, base, anchor, am1, blk)
     _check(lib().xpress_jacobi_step_noalloc(ctypes.byref(s), _ptr(_bf16(h, "h")),
                                             ctypes.c_void_p(base.data_ptr()), base.stride(0),
                                             _ptr(anchor), _ptr(am1), N, K, C, flags, _ptr(blk),
@@ -328,11 +356,9 @@ class StepGraph:
     def __init__(self, w: Weights, h, base, anchor, am1, blk, *, K: int, C: int = 0,
                  flags: int = INIT_FROM_BASE, ws: torch.Tensor, passes_run=None):
         s = w.struct()
-        _bf16(base, "base")
-        assert base.stride(1) == 1
+        N = _step_inputs(w, h, base, anchor, am1, blk)
         self._keep = (w, h, base, anchor, am1, blk, ws, passes_run)
         self._handle = ctypes.c_void_p()
-        N = blk.shape[0]
         _check(lib().xpress_jacobi_step_graph(
             ctypes.byref(s), _ptr(_bf16(h, "h")), ctypes.c_void_p(base.data_ptr()),
             base.stride(0), _ptr(anchor), _ptr(am1), N, K, C, flags, _ptr(blk), _ptr(passes_run),

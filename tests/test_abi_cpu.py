@@ -25,10 +25,18 @@ def test_workspace_size_grows_with_blocks_and_candidates():
     b = xpress.workspace_size(256, 16, 256, 151936, 0, 15)
     c = xpress.workspace_size(32, 16, 256, 151936, 512, 15)
     assert 0 < a < b
-    # top-C adds cand (int64) + base_c (bf16) per candidate and the selection's chunk maxima; the
-    # passes read w2 through the ids, so no gathered [rows, C, r] copy (125.8 MB here)
-    assert c >= a + 480 * 512 * (8 + 2)
-    assert c < a + 480 * 512 * 256 * 2
+    # top-C adds cand (int64) + base_c (bf16) per candidate and drops the full-vocabulary readout's
+    # partials (256 per row); the passes read w2 through the ids, so no gathered [rows, C, r] copy
+    # (125.8 MB here), and rows of 151,936 ids keep the selection's chunk maxima in LDS
+    part = 480 * 256 * 8
+    assert a - part + 480 * 512 * (8 + 2) <= c < a - part + 480 * 512 * (8 + 2) + 4096
+    # rows of more than 153,600 ids keep the chunk maxima (2 bytes per 8 ids, 8-chunk groups) in
+    # the workspace
+    V = 200003
+    nchunk8 = ((V + 7) // 8 + 7) // 8 * 8
+    full = xpress.workspace_size(32, 16, 256, V, 0, 15)
+    top = xpress.workspace_size(32, 16, 256, V, 512, 15)
+    assert top >= full - part + 480 * 512 * (8 + 2) + 480 * nchunk8 * 2
 
 
 @pytest.mark.parametrize("B,r,V", [(1, 256, 1000), (17, 256, 1000), (16, 96, 1000),

@@ -82,3 +82,23 @@ def test_graph_argument_errors_and_destroy():
     with pytest.raises(RuntimeError):
         g.launch()
     assert xpress.lib().xpress_graph_destroy(None) == xpress.OK
+
+
+def test_binding_refuses_inputs_that_do_not_cover_n_blocks():
+    """The C ABI takes bare pointers and N (from blk's first dimension): the binding refuses, on
+    the host and before any call, inputs that cover fewer blocks than blk asks for."""
+    inp = synth.make_inputs(1).rounded_bf16()
+    d = Dev(inp)
+    N, B = inp.blk.shape
+    more = torch.zeros(N + 1, B, dtype=torch.int64, device="cuda")
+    for step in (lambda blk: xpress.jacobi_step(d.w, d.h, d.base, d.anchor, d.am1, blk, K=2,
+                                                ws=d.ws()),
+                 lambda blk: xpress.jacobi_step_noalloc(d.w, d.h, d.base, d.anchor, d.am1, blk,
+                                                        K=2),
+                 lambda blk: xpress.StepGraph(d.w, d.h, d.base, d.anchor, d.am1, blk, K=2,
+                                              ws=d.ws()),
+                 lambda blk: xpress.initial_block(d.base, d.anchor, blk)):
+        with pytest.raises(ValueError):
+            step(more)
+    torch.cuda.synchronize()
+    assert int(more.abs().sum().item()) == 0

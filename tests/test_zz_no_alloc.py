@@ -73,13 +73,23 @@ def test_noalloc_step_at_full_size_then_fewer_blocks():
 
 
 def test_noalloc_step_rejects_more_than_its_scratch():
-    """A step that needs more than the static scratch (256 blocks with 512 candidates needs
-    ~194 MiB) is refused on the host with XPRESS_ERR_WORKSPACE; nothing runs."""
+    """A step that needs more than the static scratch (512 blocks of the full-vocabulary shape
+    need ~87 MiB of its 64 MiB) is refused on the host with XPRESS_ERR_WORKSPACE; nothing runs.
+    The inputs cover all 512 blocks all the same, so nothing would be read out of bounds even if
+    the step ran."""
     inp = synth.make_inputs(replace(synth.WORKLOADS[1], B=16, r=256, V=151936, M=512), N=1)
     d = Dev(inp)
-    blk = torch.zeros(256, 16, dtype=torch.int64, device="cuda")
+    dims = d.w.dims
+    N, B, V = 512, dims["B"], dims["V"]
+    assert xpress.workspace_size(N, B, dims["r"], V, 0, 15) > 80 << 20
+    h = torch.zeros(N, B, dims["H"], dtype=torch.bfloat16, device="cuda")
+    base = torch.zeros(N * (B - 1), V, dtype=torch.bfloat16, device="cuda")
+    anchor = torch.zeros(N, dtype=torch.int64, device="cuda")
+    blk = torch.zeros(N, B, dtype=torch.int64, device="cuda")
     with pytest.raises(xpress.XpressError) as e:
-        xpress.jacobi_step_noalloc(d.w, d.h, d.base, d.anchor, d.am1, blk, K=15, C=512)
+        xpress.jacobi_step_noalloc(d.w, h, base, anchor, anchor, blk, K=15, C=0)
     assert e.value.status == xpress.ERR_WORKSPACE
     assert "static scratch" in str(e.value)
     assert int(blk.abs().sum().item()) == 0
+    del h, base
+    torch.cuda.empty_cache()
