@@ -32,14 +32,24 @@ __device__ __forceinline__ uint32_t order_key(uint32_t b) {
   return (b & 0x8000u) ? (~b & 0xffffu) : (b | 0x8000u);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS round trips): shifts
+// by 1, 2, 4 and 8 lanes inside each 16-lane row, then lane 15 of rows 0 and 2 added into rows
+// 1 and 3, and lane 31 into rows 2 and 3 (the GFX9 row broadcasts). Lanes whose source lies
+// outside their row add 0.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  int v = x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
 __device__ __forceinline__ int block_exclusive_scan(int x, int* s_tmp, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int inc = x;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(inc, off);
-    if (lane >= off) inc += y;
-  }
+  const int inc = wave_inclusive_scan(x);
   if (lane == 63) s_tmp[wave] = inc;
   __syncthreads();
   int pre = 0;
@@ -168,8 +178,10 @@ __device__ void select_row_exact(const uint16_t* __restrict__ row, int64_t V, in
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (sel[e]) {
-        out_id[k] = id0 + e;
-        out_b[k] = bits[e];
+        if (k < c) {  // exactly c are taken; the bound only guards the row's storage
+          out_id[k] = id0 + e;
+          out_b[k] = bits[e];
+        }
         ++k;
       }
     eq_carry += eq_total;
@@ -205,7 +217,7 @@ __device__ __forceinline__ void hist_add_aggregated(uint32_t* hist, int bin, boo
 __device__ __forceinline__ uint32_t radix_kth(const uint32_t* keys, int n, int k, uint32_t* s_hist,
                                               uint32_t* s_par, int* s_tmp, uint32_t* above_out) {
   // keys: 17-bit (key + 1, 0 = empty); returns the k-th largest non-empty key (as key + 1) and
-  // sets *above_out = number of keys strictly above it. Whole workgroup (256 threads). Two
+  // sets *above_out = number of keys strictly above it; with fewer than k non-empty keys, 0. Whole workgroup (256 threads). Two
   // histogram levels over the 16-bit key (high byte, then low byte inside the boundary bin); the
   // boundary bin is found by a parallel scan over the bins in descending order: thread t owns bin
   // 255 - t, and the bin whose [count above, count above + own count) holds k - 1 is the one.
@@ -226,6 +238,10 @@ __device__ __forceinline__ uint32_t radix_kth(const uint32_t* keys, int n, int k
       s_par[0] = (uint32_t)bin;
       s_par[1] = (uint32_t)above;
     }
+  }
+  if (total < k) {  // uniform: fewer than k non-empty keys
+    *above_out = (uint32_t)total;
+    return 0u;
   }
   __syncthreads();
   const uint32_t h1 = s_par[0], a1 = s_par[1];
@@ -385,13 +401,9 @@ __device__ __forceinline__ bool topc_select_row(int p, const uint16_t* __restric
   __threadfence_block();
   __syncthreads();
   // 2. t0: the c-th largest group maximum (every group maximum is non-empty if its group had an
-  // id below V; with fewer than c of them t0 is the smallest key, 1)
-  int ngm = 0;
-  for (int j = tid; j < kBuf; j += 256) ngm += s_key[j] != 0;
-  int ngm_total;
-  (void)block_exclusive_scan(ngm, s_tmp, ngm_total);
+  // id below V; with fewer than c of them t0 = 0, below every key)
   uint32_t above;
-  const uint32_t t0 = ngm_total >= c ? radix_kth(s_key, kBuf, c, s_hist, s_par, L.tmp_r, &above) : 1u;
+  const uint32_t t0 = radix_kth(s_key, kBuf, c, s_hist, s_par, L.tmp_r, &above);
   // the smallest fp32 value with key >= t0 - 1 (any finite value when t0 <= 1: the key's bf16
   // bits, inverse of order_key, would not be a finite value then)
   float v0 = -3.4028235e38f;
@@ -520,8 +532,10 @@ __device__ __forceinline__ bool topc_select_row(int p, const uint16_t* __restric
 #pragma unroll
   for (int e = 0; e < 8; ++e)
     if ((sm >> e) & 1u) {
-      out_id[pos] = s_id[8 * tid + e];
-      out_b[pos] = s_bits[8 * tid + e];
+      if (pos < c) {  // exactly c are taken; the bound only guards the row's storage
+        out_id[pos] = s_id[8 * tid + e];
+        out_b[pos] = s_bits[8 * tid + e];
+      }
       ++pos;
     }
   if (start_slot) {  // uniform: the best buffered element (largest key, lowest id)
