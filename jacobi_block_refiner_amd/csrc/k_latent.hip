@@ -70,13 +70,17 @@ __device__ __forceinline__ void block_tokens_finish(bool has_part, const uint2 (
 #pragma unroll
       for (int k = 0; k < 16; ++k) argmax_merge(bv, bi, __uint_as_float(q[k].x), (int)q[k].y);
     }
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) {  // the 16 slices are 16 consecutive lanes
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      argmax_merge(bv, bi, ov, oi);
-    }
-    if (j == 0 && rb < B - 1) {
+    // the 16 slices are the 16 lanes of a DPP row: shifts by 1, 2, 4 and 8 leave the row's
+    // winner in its last lane (lanes whose source lies outside the row merge -inf)
+    argmax_merge(bv, bi, __int_as_float(__builtin_amdgcn_update_dpp((int)0xff800000, __float_as_int(bv), 0x111, 0xf, 0xf, false)),
+                 __builtin_amdgcn_update_dpp(INT_MAX, bi, 0x111, 0xf, 0xf, false));
+    argmax_merge(bv, bi, __int_as_float(__builtin_amdgcn_update_dpp((int)0xff800000, __float_as_int(bv), 0x112, 0xf, 0xf, false)),
+                 __builtin_amdgcn_update_dpp(INT_MAX, bi, 0x112, 0xf, 0xf, false));
+    argmax_merge(bv, bi, __int_as_float(__builtin_amdgcn_update_dpp((int)0xff800000, __float_as_int(bv), 0x114, 0xf, 0xf, false)),
+                 __builtin_amdgcn_update_dpp(INT_MAX, bi, 0x114, 0xf, 0xf, false));
+    argmax_merge(bv, bi, __int_as_float(__builtin_amdgcn_update_dpp((int)0xff800000, __float_as_int(bv), 0x118, 0xf, 0xf, false)),
+                 __builtin_amdgcn_update_dpp(INT_MAX, bi, 0x118, 0xf, 0xf, false));
+    if (j == 15 && rb < B - 1) {
       const int64_t nv = (int64_t)bi;
       if (writer) {
         int64_t* slot = blk + (int64_t)n * B + 1 + rb;
