@@ -72,14 +72,10 @@ __device__ __forceinline__ void block_tokens_finish(bool has_part, const uint2 (
     }
     // the 16 slices are the 16 lanes of a DPP row: shifts by 1, 2, 4 and 8 leave the row's
     // winner in its last lane (lanes whose source lies outside the row merge -inf)
-    argmax_merge(bv, bi, __int_as_float(__builtin_amdgcn_update_dpp((int)0xff800000, __float_as_int(bv), 0x111, 0xf, 0xf, false)),
-                 __builtin_amdgcn_update_dpp(INT_MAX, bi, 0x111, 0xf, 0xf, false));
-    argmax_merge(bv, bi, __int_as_float(__builtin_amdgcn_update_dpp((int)0xff800000, __float_as_int(bv), 0x112, 0xf, 0xf, false)),
-                 __builtin_amdgcn_update_dpp(INT_MAX, bi, 0x112, 0xf, 0xf, false));
-    argmax_merge(bv, bi, __int_as_float(__builtin_amdgcn_update_dpp((int)0xff800000, __float_as_int(bv), 0x114, 0xf, 0xf, false)),
-                 __builtin_amdgcn_update_dpp(INT_MAX, bi, 0x114, 0xf, 0xf, false));
-    argmax_merge(bv, bi, __int_as_float(__builtin_amdgcn_update_dpp((int)0xff800000, __float_as_int(bv), 0x118, 0xf, 0xf, false)),
-                 __builtin_amdgcn_update_dpp(INT_MAX, bi, 0x118, 0xf, 0xf, false));
+    argmax_merge_dpp<0x111>(bv, bi);  // row_shr:1
+    argmax_merge_dpp<0x112>(bv, bi);  // row_shr:2
+    argmax_merge_dpp<0x114>(bv, bi);  // row_shr:4
+    argmax_merge_dpp<0x118>(bv, bi);  // row_shr:8
     if (j == 15 && rb < B - 1) {
       const int64_t nv = (int64_t)bi;
       if (writer) {

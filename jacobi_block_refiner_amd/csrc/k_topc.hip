@@ -217,10 +217,11 @@ __device__ __forceinline__ void hist_add_aggregated(uint32_t* hist, int bin, boo
 __device__ __forceinline__ uint32_t radix_kth(const uint32_t* keys, int n, int k, uint32_t* s_hist,
                                               uint32_t* s_par, int* s_tmp, uint32_t* above_out) {
   // keys: 17-bit (key + 1, 0 = empty); returns the k-th largest non-empty key (as key + 1) and
-  // sets *above_out = number of keys strictly above it; with fewer than k non-empty keys, 0. Whole workgroup (256 threads). Two
-  // histogram levels over the 16-bit key (high byte, then low byte inside the boundary bin); the
-  // boundary bin is found by a parallel scan over the bins in descending order: thread t owns bin
-  // 255 - t, and the bin whose [count above, count above + own count) holds k - 1 is the one.
+  // sets *above_out = number of keys strictly above it; with fewer than k non-empty keys it
+  // returns 0. Whole workgroup (256 threads). Two histogram levels over the 16-bit key (high
+  // byte, then low byte inside the boundary bin); the boundary bin is found by a parallel scan
+  // over the bins in descending order: thread t owns bin 255 - t, and the bin whose [count above,
+  // count above + own count) holds k - 1 is the one.
   const int tid = threadIdx.x;
   s_hist[tid] = 0;
   __syncthreads();
