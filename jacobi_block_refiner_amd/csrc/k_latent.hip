@@ -607,8 +607,9 @@ __global__ __launch_bounds__(256) void latent_share_kernel(
 }
 
 // lat[n, b-1, c] = sum_g dpart[n, g, b, c] in slice order, for slots 1..B-1. Workgroup (n, y)
-// takes 256/(r/4) consecutive slots, one thread per 4 channels of a slot.
-template <int R>
+// takes 256/(r/4) consecutive slots, one thread per 4 channels of a slot; KB shares in flight at
+// once (16 when there are more than 8 slices, so that 16 slices take one round trip).
+template <int R, int KB>
 __global__ __launch_bounds__(256) void latent_sum_kernel(const float* __restrict__ dpart, int B,
                                                          int G, uint16_t* __restrict__ lat,
                                                          const int32_t* __restrict__ flags,
@@ -621,13 +622,13 @@ __global__ __launch_bounds__(256) void latent_sum_kernel(const float* __restrict
   if (b >= B) return;
   const float4* dp4 = reinterpret_cast<const float4*>(dpart + (int64_t)n * G * 16 * R);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int g0 = 0; g0 < G; g0 += 8) {
-    // eight shares in flight at once (indexes past G clamped, their values dropped)
-    float4 v[8];
+  for (int g0 = 0; g0 < G; g0 += KB) {
+    // KB shares in flight at once (indexes past G clamped, their values dropped)
+    float4 v[KB];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = dp4[((int64_t)min(g0 + k, G - 1) * 16 + b) * QR + q];
+    for (int k = 0; k < KB; ++k) v[k] = dp4[((int64_t)min(g0 + k, G - 1) * 16 + b) * QR + q];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < KB; ++k) {
       const bool on = g0 + k < G;
       acc.x += on ? v[k].x : 0.f;
       acc.y += on ? v[k].y : 0.f;
@@ -690,8 +691,13 @@ hipError_t launch_fused_r(const uint2* part, int ntiles, int64_t* blk, const int
                        flags, pass);
   if (!with_sum) return hipGetLastError();
   constexpr int RPW = 256 / (R / 4);
-  hipLaunchKernelGGL(latent_sum_kernel<R>, dim3(N, (B - 1 + RPW - 1) / RPW), dim3(256), 0, s,
-                     dpart, B, G, lat, flags, pass, part != nullptr ? 1 : 0, lat_frag ? 1 : 0);
+  const dim3 grid(N, (B - 1 + RPW - 1) / RPW);
+  if (G > 8)
+    hipLaunchKernelGGL((latent_sum_kernel<R, 16>), grid, dim3(256), 0, s, dpart, B, G, lat, flags,
+                       pass, part != nullptr ? 1 : 0, lat_frag ? 1 : 0);
+  else
+    hipLaunchKernelGGL((latent_sum_kernel<R, 8>), grid, dim3(256), 0, s, dpart, B, G, lat, flags,
+                       pass, part != nullptr ? 1 : 0, lat_frag ? 1 : 0);
   return hipGetLastError();
 }
 
