@@ -89,8 +89,8 @@ typedef struct {
                                           in_proj's embedding block applied,
                                           w1p[v, c] = sum_k in_proj[c, 2r+k] * w1[v, k]
                                           (xpress_fold_embedding). When given and
-                                          N * M/64 <= 256 (one workgroup per block and 64-unit
-                                          slice, one round on the 256 CUs: N <= 32 at M = 512),
+                                          N * M/64 <= 448 (one workgroup per block and 64-unit
+                                          slice, two per CU in one round: N <= 56 at M = 512),
                                           the latent stage gathers its rows instead of
                                           projecting w1's rows every pass and runs as two
                                           launches instead of three (beyond that the

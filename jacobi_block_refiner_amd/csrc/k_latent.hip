@@ -20,7 +20,7 @@
 // Each workgroup reads at most 64 KB of weights; row tiles of 64 rows (4 blocks) share weight
 // reads when there are many blocks.
 // With the projected table w1p = P_e applied to every row of w1 (fold_embedding_kernel, once per
-// weight set), step 2 is a row gather, and while N * M/64 <= 256 the stage runs as
+// weight set), step 2 is a row gather, and while N * M/64 <= 448 the stage runs as
 //   latent_share_kernel (block, 64 hidden units): steps 1-4 and the slice's share of step 5;
 //   latent_sum_kernel   (block, slots): the shares summed in slice order into lat.
 //

@@ -112,13 +112,13 @@ xpress_status check_base(const xpress_bf16* base, int64_t ld, int64_t V) {
 }
 
 // Whether the latent stage runs from the projected embedding table (share + sum kernels): while
-// its N * M/64 share workgroups (one per block and 64-unit slice) fit in one round on the 256
-// CUs. Whole steps at M = 512: the table path is faster up to 32 blocks (16.4k against 15.4k
-// passes/s at 32, 18.9k against 17.4k at 24, 35.0k against 29.6k at 1); from 33 blocks on (264
-// workgroups, a second round) the three-kernel path is (14.9k against 14.4k at 33, 12.1k against
-// 11.9k at 36, 9.4k against 9.1k at 48, 6.2k against 6.0k at 96) and is taken even when the table
-// is given. The results agree within fp32 rounding either way.
-constexpr int kTableMaxWorkgroups = 256;
+// its N * M/64 share workgroups (one per block and 64-unit slice) number at most 448. Two of them
+// fit on a CU, so up to 512 run in one round. Whole steps at M = 512: the table path is faster up
+// to 56 blocks (16.8k against 15.7k passes/s at 32, 15.5k against 15.1k at 33, 12.0k against
+// 11.8k at 40, 9.86k against 9.78k at 56) and the three-kernel path from 64 (9.48k against 9.26k
+// at 64, 6.38k against 6.27k at 96, 5.10k against 4.97k at 128); it is taken there even when the
+// table is given. The results agree within fp32 rounding either way.
+constexpr int kTableMaxWorkgroups = 448;
 bool table_fits(int N, int M) { return (int64_t)N * (M / 64) <= kTableMaxWorkgroups; }
 bool use_table(const xpress_weights* w, int N) { return w->w1p != nullptr && table_fits(N, w->M); }
 
@@ -213,10 +213,10 @@ xpress_status xpress_workspace_size(int32_t n_max, int32_t B, int32_t r, int64_t
   xpress_status st = check_dims(B, r, V);
   if (st != XPRESS_OK) return st;
   // every region grows with N, except the latent scratch, whose table-path part peaks where the
-  // share workgroups N * slices reach their bound of 256, at a power of two N: the largest
-  // layout of any N <= n_max is at n_max or at one of those N
+  // slices widen from 32 to 64 units and where the path stops (some N <= kTableMaxWorkgroups,
+  // depending on M): the largest layout of any N <= n_max is at n_max or at one of those N
   size_t t = step_layout(n_max, B, r, kMaxH, V, C, k_max).total;
-  for (int n = 1; n <= kTableMaxWorkgroups && n < n_max; n *= 2) {
+  for (int n = 1; n <= kTableMaxWorkgroups && n < n_max; ++n) {
     const size_t u = step_layout(n, B, r, kMaxH, V, C, k_max).total;
     t = u > t ? u : t;
   }

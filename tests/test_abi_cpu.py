@@ -21,22 +21,24 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_workspace_size_grows_with_blocks_and_candidates():
-    a = xpress.workspace_size(32, 16, 256, 151936, 0, 15)
-    b = xpress.workspace_size(256, 16, 256, 151936, 0, 15)
-    c = xpress.workspace_size(32, 16, 256, 151936, 512, 15)
+    a = xpress.workspace_size(256, 16, 256, 151936, 0, 15)
+    b = xpress.workspace_size(512, 16, 256, 151936, 0, 15)
+    c = xpress.workspace_size(256, 16, 256, 151936, 512, 15)
     assert 0 < a < b
     # top-C adds cand (int64) + base_c (bf16) per candidate and drops the full-vocabulary readout's
     # partials (256 per row); the passes read w2 through the ids, so no gathered [rows, C, r] copy
-    # (125.8 MB here), and rows of 151,936 ids keep the selection's chunk maxima in LDS
-    part = 480 * 256 * 8
-    assert a - part + 480 * 512 * (8 + 2) <= c < a - part + 480 * 512 * (8 + 2) + 4096
+    # (1 GB here), and rows of 151,936 ids keep the selection's chunk maxima in LDS. (At 256
+    # blocks the layout of n_max itself is the largest, so the regions add up exactly.)
+    rows = 256 * 15
+    part = rows * 256 * 8
+    assert a - part + rows * 512 * (8 + 2) <= c < a - part + rows * 512 * (8 + 2) + 4096
     # rows of more than 153,600 ids keep the chunk maxima (2 bytes per 8 ids, 8-chunk groups) in
     # the workspace
     V = 200003
     nchunk8 = ((V + 7) // 8 + 7) // 8 * 8
-    full = xpress.workspace_size(32, 16, 256, V, 0, 15)
-    top = xpress.workspace_size(32, 16, 256, V, 512, 15)
-    assert top >= full - part + 480 * 512 * (8 + 2) + 480 * nchunk8 * 2
+    full = xpress.workspace_size(256, 16, 256, V, 0, 15)
+    top = xpress.workspace_size(256, 16, 256, V, 512, 15)
+    assert top >= full - part + rows * 512 * (8 + 2) + rows * nchunk8 * 2
 
 
 @pytest.mark.parametrize("B,r,V", [(1, 256, 1000), (17, 256, 1000), (16, 96, 1000),
@@ -124,11 +126,14 @@ def test_fold_embedding_and_table_arguments_are_checked():
 
 def test_workspace_for_n_max_fits_every_smaller_n():
     """A workspace sized for n_max covers every N <= n_max (the table path's latent scratch makes
-    the size non-monotone in N where that path stops: N * M/64 = 256 share workgroups, i.e.
-    after 16, 32, 64, 128 or 256 blocks depending on M)."""
-    for n_max in (15, 16, 17, 31, 32, 33, 64, 65, 96, 128, 160, 256, 257):
+    the size non-monotone in N where its slices widen from 32 to 64 units and where that path
+    stops: N * M/64 = 448 share workgroups, i.e. after 28, 56, 112, 224 or 448 blocks depending
+    on M)."""
+    for n_max in (15, 16, 17, 28, 29, 31, 32, 33, 56, 57, 64, 65, 96, 112, 113, 128, 160, 224,
+                  225, 256, 257, 448, 449):
         big = xpress.workspace_size(n_max, 16, 256, 151936, 0, 15)
-        for n in (1, 16, 17, 32, 33, 64, 65, 96, 128, 129, 256, n_max):
+        for n in (1, 8, 9, 16, 17, 28, 29, 32, 33, 56, 57, 64, 65, 96, 112, 113, 128, 129, 224,
+                  225, 256, 448, 449, n_max):
             if n <= n_max:
                 assert xpress.workspace_size(n, 16, 256, 151936, 0, 15) <= big, (n, n_max)
 

@@ -289,21 +289,25 @@ def test_fold_embedding_matches_oracle_projection(r, V):
                                          (3, 2, {"V": 2048, "M": 1024}),
                                          (1, 37, {"B": 16, "r": 256, "M": 512, "V": 3000}),
                                          (1, 5, {"B": 2, "r": 64, "M": 64, "V": 700}),
-                                         # 32 blocks at M = 512: the most the table path takes (256
-                                         # share workgroups); from 33 on the three-kernel path
-                                         # runs, table or not
+                                         # at M = 512 the table path takes up to 56 blocks (448
+                                         # share workgroups, two per CU); from 57 on the
+                                         # three-kernel path runs, table or not
                                          (1, 32, {"B": 16, "r": 256, "M": 512, "V": 3000}),
                                          (1, 33, {"B": 16, "r": 256, "M": 512, "V": 3000}),
+                                         (1, 56, {"B": 16, "r": 256, "M": 512, "V": 3000}),
+                                         (1, 57, {"B": 16, "r": 256, "M": 512, "V": 3000}),
                                          (1, 96, {"B": 16, "r": 256, "M": 512, "V": 3000}),
                                          (1, 130, {"B": 16, "r": 256, "M": 512, "V": 3000}),
                                          # the slice width follows N * M/32 <= 256 (32 units) and the
-                                         # path N * M/64 <= 256: M = 1024 at 12 blocks takes 64-unit
-                                         # slices on the table path, M = 256 at 20 and 40 blocks 32-
-                                         # and 64-unit ones, at 65 blocks the three-kernel path
+                                         # path N * M/64 <= 448: M = 1024 at 12 and 28 blocks takes
+                                         # 64-unit slices on the table path, M = 256 at 20 and 40
+                                         # blocks 32- and 64-unit ones, at 113 blocks the
+                                         # three-kernel path
                                          (3, 12, {"V": 2048, "M": 1024}),
+                                         (3, 28, {"V": 2048, "M": 1024}),
                                          (1, 20, {"B": 16, "r": 256, "M": 256, "V": 3000}),
                                          (1, 40, {"B": 16, "r": 256, "M": 256, "V": 3000}),
-                                         (1, 65, {"B": 16, "r": 256, "M": 256, "V": 3000}),
+                                         (1, 113, {"B": 16, "r": 256, "M": 256, "V": 3000}),
                                          (1, 129, {"B": 5, "r": 128, "M": 128, "V": 1000})])
 def test_latent_parity(wl_id, N, over, path):
     inp, xh = _latent_case(wl_id, N, **over)
@@ -322,7 +326,7 @@ def test_latent_parity(wl_id, N, over, path):
 def test_latent_fragment_order_is_the_same_values(path, N, over):
     """The latent written in the readout's fragment order holds exactly the values of the
     row-major latent, permuted (the order a step keeps lat in); 3 and 37 blocks leave a partial
-    last 32-row tile, 37 and 130 blocks run the three-kernel path."""
+    last 32-row tile, 130 blocks run the three-kernel path."""
     inp, xh = _latent_case(3 if N == 3 else 1, N, **({} if N == 3 else {"B": 16, "r": 256, "M": 512}), **over)
     d = _dev(inp, path)
     wl = inp.wl
