@@ -492,8 +492,12 @@ def _select_scratch(rows, V):
 
 
 @pytest.mark.parametrize("chunk_maxima", [False, True])
+# 153,600 ids: the longest row whose chunk maxima stay in LDS; 153,608 and 200,003: in the
+# workspace (or the exact path without one); 524,288: the longest row of the buffered path (16-bit
+# chunk indexes); 524,296: the exact path either way
 @pytest.mark.parametrize("C,V", [(64, 5003), (512, 8192), (700, 700), (1, 3000), (5, 7), (40, 33),
-                                 (512, 153600), (64, 153608), (512, 200003)])
+                                 (512, 153600), (64, 153608), (512, 200003), (64, 524288),
+                                 (64, 524296)])
 def test_topc_prepare_exact(C, V, chunk_maxima):
     rng = np.random.default_rng(6)
     N, B, r = 3, 16, 64
