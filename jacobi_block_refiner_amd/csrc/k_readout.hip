@@ -383,17 +383,20 @@ __global__ __launch_bounds__(64 * kNW) void readout_partial_kernel(
   }
 }
 
-// Partials of 64 consecutive rows per workgroup: thread (row lr, slice j) scans ranges j, j+4, ...
-// (each wave reads 64 consecutive rows of one range: 512 contiguous bytes), the four slice
-// winners of a row are merged in LDS, and the row's winner is written into blk in place.
+// Partials of RR consecutive rows per workgroup (64, or 16 for a few rows), S = 256/RR range
+// slices per row: thread (row lr, slice j) scans ranges j, j+S, ... with up to 16 loads in flight
+// (at 64 rows each wave reads 64 consecutive rows of one range: 512 contiguous bytes), the S
+// slice winners of a row are merged in LDS, and the row's winner is written into blk in place.
 // With passes_run (the last pass of a step, pass = K-1): workgroup 0 also writes the number of
 // passes that ran, which flags[0 .. K-2] already fix (pass p >= 1 ran iff pass p-1 changed a
 // slot), so the step needs no launch of its own for it.
+template <int RR>
 __global__ __launch_bounds__(256) void argmax_reduce_kernel(const uint2* __restrict__ part,
                                                             int ntiles, int rows, int B,
                                                             int64_t* __restrict__ blk,
                                                             int32_t* changed, int32_t* flags,
                                                             int pass, int32_t* passes_run) {
+  constexpr int S = 256 / RR;
   if (passes_run && blockIdx.x == 0 && threadIdx.x == 0) {
     int n = pass + 1;
     if (flags) {
@@ -403,26 +406,22 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const uint2* __restr
     *passes_run = n;
   }
   if (pass_skipped(flags, pass)) return;
-  __shared__ float s_v[4][64];
-  __shared__ int s_i[4][64];
-  const int lr = threadIdx.x & 63, j = threadIdx.x >> 6;
-  const int p = blockIdx.x * 64 + lr;
+  __shared__ float s_v[S][RR];
+  __shared__ int s_i[S][RR];
+  const int lr = threadIdx.x % RR, j = threadIdx.x / RR;
+  const int p = blockIdx.x * RR + lr;
   float bv = -INFINITY;
   int bi = INT_MAX;
   if (p < rows) {
     const uint2* pr = part + p;
-    int t = j;
-#pragma unroll 1
-    for (; t + 12 < ntiles; t += 16) {
-      uint2 q[4];
+    // 16 loads in flight: ranges j + S*(u + 16 i), clamped to the last range (repeats change
+    // nothing)
+    for (int t0 = j; t0 < ntiles; t0 += 16 * S) {
+      uint2 q[16];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) q[u] = pr[(int64_t)(t + 4 * u) * rows];
+      for (int u = 0; u < 16; ++u) q[u] = pr[(int64_t)min(t0 + S * u, ntiles - 1) * rows];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) argmax_merge(bv, bi, __uint_as_float(q[u].x), (int)q[u].y);
-    }
-    for (; t < ntiles; t += 4) {
-      const uint2 q = pr[(int64_t)t * rows];
-      argmax_merge(bv, bi, __uint_as_float(q.x), (int)q.y);
+      for (int u = 0; u < 16; ++u) argmax_merge(bv, bi, __uint_as_float(q[u].x), (int)q[u].y);
     }
   }
   s_v[j][lr] = bv;
@@ -430,7 +429,7 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const uint2* __restr
   __syncthreads();
   if (j == 0 && p < rows) {
 #pragma unroll
-    for (int u = 1; u < 4; ++u) argmax_merge(bv, bi, s_v[u][lr], s_i[u][lr]);
+    for (int u = 1; u < S; ++u) argmax_merge(bv, bi, s_v[u][lr], s_i[u][lr]);
     const int n = p / (B - 1), b = 1 + p % (B - 1);
     int64_t* slot = blk + (int64_t)n * B + b;
     const int64_t nv = (int64_t)bi;
@@ -500,8 +499,12 @@ hipError_t launch_readout_partial(const uint16_t* lat, const uint16_t* w2, const
 hipError_t launch_argmax_reduce(const uint2* part, int ntiles, int rows, int B, int64_t* blk,
                                 int32_t* changed, int32_t* flags, int pass, hipStream_t s,
                                 int32_t* passes_run) {
-  hipLaunchKernelGGL(argmax_reduce_kernel, dim3((rows + 63) / 64), dim3(256), 0, s, part, ntiles,
-                     rows, B, blk, changed, flags, pass, passes_run);
+  if (rows <= 16)
+    hipLaunchKernelGGL(argmax_reduce_kernel<16>, dim3(1), dim3(256), 0, s, part, ntiles, rows, B,
+                       blk, changed, flags, pass, passes_run);
+  else
+    hipLaunchKernelGGL(argmax_reduce_kernel<64>, dim3((rows + 63) / 64), dim3(256), 0, s, part,
+                       ntiles, rows, B, blk, changed, flags, pass, passes_run);
   return hipGetLastError();
 }
 
