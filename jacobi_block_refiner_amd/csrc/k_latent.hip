@@ -45,15 +45,17 @@ namespace {
 // result); the one with `writer` set writes them into blk and raises flags[pass-1] on a change.
 // Two halves, so that a kernel can issue the partials' loads (the head of its dependency chain)
 // before its other loads and reduce them after: block_tokens_load fills this thread's 16
-// partials (thread: readout row tid/16 of the block, ranges tid%16 + 16k; clamped repeats change
-// nothing), block_tokens_finish reduces them (q is ignored without part). Both are called by all
-// 256 threads; the caller synchronises before reading tok.
+// partials (lane l of wave w: readout row l%16 of the block, ranges 4*(16w + k) + l/16, so one
+// load instruction of a wave reads four ranges' contiguous rows of the block; clamped repeats
+// change nothing), block_tokens_finish reduces them (q is ignored without part). Both are called
+// by all 256 threads; the caller synchronises before reading tok.
 __device__ __forceinline__ void block_tokens_load(const uint2* __restrict__ part, int ntiles,
                                                   int rows, int n, int B, uint2 (&q)[16]) {
-  const int rb = threadIdx.x >> 4, j = threadIdx.x & 15;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rb = lane & 15, sub = lane >> 4;
   const uint2* pr = part + (int64_t)n * (B - 1) + min(rb, B - 2);
 #pragma unroll
-  for (int k = 0; k < 16; ++k) q[k] = pr[(int64_t)min(j + 16 * k, ntiles - 1) * rows];
+  for (int k = 0; k < 16; ++k) q[k] = pr[(int64_t)min((w * 16 + k) * 4 + sub, ntiles - 1) * rows];
 }
 
 __device__ __forceinline__ void block_tokens_finish(bool has_part, const uint2 (&q)[16],
@@ -63,29 +65,40 @@ __device__ __forceinline__ void block_tokens_finish(bool has_part, const uint2 (
                                                     int pass, int64_t* tok) {
   const int tid = threadIdx.x;
   if (has_part) {
-    const int rb = tid >> 4, j = tid & 15;  // readout row rb of the block, range slice j
+    __shared__ float s_bv[4][16];
+    __shared__ int s_bi[4][16];
+    const int lane = tid & 63, w = tid >> 6, rb = lane & 15;  // readout row rb of the block
     float bv = -INFINITY;
     int bi = INT_MAX;
     if (rb < B - 1) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) argmax_merge(bv, bi, __uint_as_float(q[k].x), (int)q[k].y);
     }
-    // the 16 slices are the 16 lanes of a DPP row: shifts by 1, 2, 4 and 8 leave the row's
-    // winner in its last lane (lanes whose source lies outside the row merge -inf)
-    argmax_merge_dpp<0x111>(bv, bi);  // row_shr:1
-    argmax_merge_dpp<0x112>(bv, bi);  // row_shr:2
-    argmax_merge_dpp<0x114>(bv, bi);  // row_shr:4
-    argmax_merge_dpp<0x118>(bv, bi);  // row_shr:8
-    if (j == 15 && rb < B - 1) {
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {  // the wave's four lanes of row rb
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      argmax_merge(bv, bi, ov, oi);
+    }
+    if (lane < 16) {
+      s_bv[w][lane] = bv;
+      s_bi[w][lane] = bi;
+    }
+    __syncthreads();
+    if (tid < B - 1) {  // the four waves' winners of row tid
+      bv = s_bv[0][tid];
+      bi = s_bi[0][tid];
+#pragma unroll
+      for (int k = 1; k < 4; ++k) argmax_merge(bv, bi, s_bv[k][tid], s_bi[k][tid]);
       const int64_t nv = (int64_t)bi;
       if (writer) {
-        int64_t* slot = blk + (int64_t)n * B + 1 + rb;
+        int64_t* slot = blk + (int64_t)n * B + 1 + tid;
         if (*slot != nv) {
           *slot = nv;
           if (flags) __hip_atomic_store(flags + pass - 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
-      if (rb + 2 < B) tok[rb + 2] = nv;  // slot b reads blk[b-1]
+      if (tid + 2 < B) tok[tid + 2] = nv;  // slot b reads blk[b-1]
     }
     if (tid == 0) {
       tok[0] = am1[n];

@@ -47,16 +47,6 @@ __device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi)
   i = take ? oi : i;
 }
 
-// argmax_merge with the (value, id) of the lane that DPP control CTRL (a row shift) names; a lane
-// whose source lies outside its 16-lane row merges (-inf, INT_MAX), which changes nothing.
-template <int CTRL>
-__device__ __forceinline__ void argmax_merge_dpp(float& v, int& i) {
-  const int ov = __builtin_amdgcn_update_dpp((int)0xff800000u, __float_as_int(v), CTRL, 0xf, 0xf,
-                                             false);
-  const int oi = __builtin_amdgcn_update_dpp(INT_MAX, i, CTRL, 0xf, 0xf, false);
-  argmax_merge(v, i, __int_as_float(ov), oi);
-}
-
 __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
