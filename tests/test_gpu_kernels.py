@@ -228,8 +228,11 @@ def test_readout_changed_flag_stays_clear_at_a_fixed_point():
 
 # the last two run the GEMM's deep path (a slice's chunks loaded 8 at a time): 16 chunks per
 # slice, and 20 (16 + a remainder of 4) with a ragged last row tile (528 slot rows)
+# H = 16384: the largest hidden size the library takes (256 k chunks over the split-K slices);
+# N = 256: one split, a projection workgroup of 64 channels per block
 @pytest.mark.parametrize("H,r,N,B", [(256, 64, 3, 4), (4096, 256, 3, 16), (320, 128, 2, 7),
-                                     (4096, 256, 32, 16), (5120, 256, 33, 16)])
+                                     (4096, 256, 32, 16), (5120, 256, 33, 16), (16384, 256, 3, 16),
+                                     (1024, 256, 256, 16)])
 def test_hidden_cache_parity(H, r, N, B):
     base_wl = synth.WORKLOADS[1] if r == 64 else synth.WORKLOADS[3]
     wl = replace(base_wl, N=N, B=B, H=H, r=r, V=512, M=128)
