@@ -211,6 +211,40 @@ def test_readout_zero_head_is_argmax_of_base():
     assert np.array_equal(draft_rows(blk.cpu().numpy()), np.argmax(base, axis=1))
 
 
+def test_readout_start_and_selection_at_the_largest_vocabulary():
+    """V = 2^31/r - 1 at r = 256 (8,388,607 ids, the most the library takes; ids up to 2^23 and
+    w2 offsets up to 2^31 bytes). A zero head leaves the readout the argmax of base, so the draft
+    is np.argmax (lowest id on ties, one planted at both ends of a row); the starting block is the
+    same argmax; a top-64 selection (the exact path: rows past 524,288 ids) matches the oracle."""
+    N, B, r = 1, 16, 256
+    V = (1 << 31) // r - 1
+    rows = N * (B - 1)
+    rng = np.random.default_rng(12)
+    base = synth.bf16_round(rng.standard_normal((rows, V), dtype=np.float32) * 3)
+    base[3, V - 1] = base[3, 17] = 40.0
+    z = lambda *shape: torch.zeros(*shape, dtype=torch.bfloat16, device="cuda")
+    w = xpress.Weights(w1=z(V, r), down_h=z(r, 64), down_g=z(r, 64), in_proj=z(r, 3 * r),
+                       mix_L=z(B, B, r), w_gate=z(64, r), w_up=z(64, r), w_down=z(r, 64),
+                       w2=z(V, r))
+    base_d = upload.base_logits(base)
+    log(f"readout, starting block and top-64 at V={V}")
+    blk = torch.zeros(N, B, dtype=torch.int64, device="cuda")
+    xpress.readout_argmax(w, z(rows, r), base_d, blk, xpress.alloc_workspace(N, B, r, V, 0, 1))
+    start = torch.zeros(N, B, dtype=torch.int64, device="cuda")
+    xpress.initial_block(base_d, upload.tokens(np.array([5])), start)
+    cand = torch.empty(rows, 64, dtype=torch.int64, device="cuda")
+    base_c = torch.empty(rows, 64, dtype=torch.bfloat16, device="cuda")
+    xpress.topc_prepare(w, base_d, N, 64, cand, base_c)
+    torch.cuda.synchronize()
+    want = np.argmax(base, axis=1)
+    assert want[3] == 17
+    assert np.array_equal(draft_rows(blk.cpu().numpy()), want)
+    assert np.array_equal(start.cpu().numpy()[0], np.concatenate([[5], want]))
+    assert np.array_equal(cand.cpu().numpy(), O.topc_select(base, 64))
+    del w, base_d
+    torch.cuda.empty_cache()
+
+
 def test_readout_changed_flag_stays_clear_at_a_fixed_point():
     N, B, r, V = 2, 16, 64, 3000
     lat, w2, base = _readout_case(5, N, B, r, V)
