@@ -816,3 +816,30 @@ def test_step_at_40_blocks_matches_oracle(path):
     log(f"  disallowed mismatches {bad}, near-tie row-passes {exempt}")
     assert bad == 0
     assert np.array_equal(got[:, 0], inp.anchor)
+
+
+@pytest.mark.parametrize("C,path", [(0, "table"), (0, "project"), (40, "table")])
+def test_step_is_block_permutation_equivariant(C, path):
+    """Blocks never mix: permuting the blocks of every per-block input (h, the base rows, anchor,
+    am1) permutes the step's drafts and leaves the pass count, bit for bit."""
+    inp = synth.make_inputs(replace(synth.WORKLOADS[3], V=2000), N=9, seed=6).rounded_bf16()
+    wl = inp.wl
+    perm = np.random.default_rng(1).permutation(wl.N)
+    rows = (perm[:, None] * (wl.B - 1) + np.arange(wl.B - 1)[None, :]).reshape(-1)
+    pinp = replace(inp, h=inp.h[perm], base=inp.base[rows], blk=inp.blk[perm], am1=inp.am1[perm])
+    K = 15
+    outs = []
+    for x in (inp, pinp):
+        d = _dev(x, path)
+        blk = torch.zeros(wl.N, wl.B, dtype=torch.int64, device="cuda")
+        passes = torch.zeros(1, dtype=torch.int32, device="cuda")
+        xpress.jacobi_step(d.w, d.h, d.base, d.anchor, d.am1, blk, K=K, C=C,
+                           flags=xpress.INIT_FROM_BASE | xpress.STOP_AT_FIXED_POINT,
+                           ws=xpress.alloc_workspace(wl.N, wl.B, wl.r, wl.V, C, K),
+                           passes_run=passes)
+        torch.cuda.synchronize()
+        outs.append((blk.cpu().numpy(), int(passes.item())))
+    (got, p0), (pgot, p1) = outs
+    log(f"permutation equivariance C={C} {path}: passes {p0} / {p1}")
+    assert np.array_equal(pgot, got[perm])
+    assert p0 == p1
